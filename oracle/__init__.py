@@ -1,0 +1,213 @@
+"""CPU oracle for the MoE-layer forward path (TEST INFRASTRUCTURE ONLY).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  The GPU library never calls it, and nothing here is a fallback
+for the GPU path.  It shares no code with the GPU library: the arithmetic is in
+`moe_oracle.c` (plain C, fp64 accumulation, one pass per token over its chosen
+experts); this module only builds that file with gcc and marshals numpy arrays.
+
+Activations and weights are passed as fp32 arrays or as raw bf16 bits (uint16).
+Every function cites, in `moe_oracle.c`, the page passage it follows.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_BUILD = os.path.join(_HERE, "_build")
+_SO = os.path.join(_BUILD, "libmoe_oracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile moe_oracle.c with gcc (no contraction, no fast math, OpenMP)."""
+    if not force and os.path.exists(_SO):
+        return _SO
+    os.makedirs(_BUILD, exist_ok=True)
+    tmp = _SO + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+           "-fno-fast-math", "-Wall", "-o", tmp, _SRC, "-lm"]
+    subprocess.check_call(cmd)
+    os.replace(tmp, _SO)
+    return _SO
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_SO)
+        vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        L.oracle_num_threads.restype = i32
+        L.oracle_router_logits.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp]
+        L.oracle_sigmoid_spec.argtypes = [f32]
+        L.oracle_sigmoid_spec.restype = f32
+        L.oracle_sigmoid_spec_array.argtypes = [ctypes.c_int64, vp, vp]
+        L.oracle_route.argtypes = [i32, i32, vp, i32, vp, i32, i32, f32, i32, i32, i32, vp, vp]
+        L.oracle_capacity.argtypes = [f32, ctypes.c_int64, i32]
+        L.oracle_capacity.restype = ctypes.c_int64
+        L.oracle_dispatch.argtypes = [i32, i32, i32, vp, f32, vp, vp, vp, vp, vp]
+        L.oracle_dispatch.restype = i32
+        L.oracle_grouped_ffn.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp]
+        L.oracle_combine.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+        L.oracle_layer_forward.argtypes = (
+            [i32] * 6 + [vp, vp, vp, vp] + [i32, i32, f32, i32, i32, i32, f32] + [vp, vp, vp]
+            + [i32, vp, vp, vp] + [vp, i32, vp] + [vp] * 8)
+        _lib = L
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _act(a: np.ndarray):
+    """(contiguous array, dtype code) for fp32 or raw-bf16 input."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return a, 1
+    if a.dtype != np.float32:
+        raise TypeError(f"oracle expects float32 or raw bf16 (uint16), got {a.dtype}")
+    return a, 0
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
+
+
+def router_logits(x, w_router, bias=None) -> np.ndarray:
+    x, dt = _act(x)
+    w, dt2 = _act(w_router)
+    assert dt == dt2
+    T, H = x.shape
+    E = w.shape[0]
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    out = np.empty((T, E), np.float32)
+    lib().oracle_router_logits(T, H, E, dt, _p(x), _p(w), _p(b), _p(out))
+    return out
+
+
+def sigmoid_spec(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty_like(x)
+    lib().oracle_sigmoid_spec_array(x.size, _p(x), _p(y))
+    return y
+
+
+def route(logits, k_max, k_per_token=None, score=0, renorm=1, routed_scale=1.0, num_groups=1,
+          topk_groups=1, group_topn=0):
+    l = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = l.shape
+    kpt = None if k_per_token is None else np.ascontiguousarray(k_per_token, dtype=np.int32)
+    ids = np.empty((T, k_max), np.int32)
+    gates = np.empty((T, k_max), np.float32)
+    lib().oracle_route(T, E, _p(l), k_max, _p(kpt), score, renorm, routed_scale, num_groups,
+                       topk_groups, group_topn, _p(ids), _p(gates))
+    return ids, gates
+
+
+def capacity(cf: float, A: int, E: int) -> int:
+    return int(lib().oracle_capacity(cf, A, E))
+
+
+def dispatch(ids, E, capacity_factor=0.0):
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    T, k = ids.shape
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    ros = np.empty((T, k), np.int32)
+    row_token = np.full(T * k, -1, np.int32)
+    nd = np.zeros(1, np.int32)
+    R = lib().oracle_dispatch(T, E, k, _p(ids), capacity_factor, _p(counts), _p(offsets), _p(ros),
+                              _p(row_token), _p(nd))
+    return dict(counts=counts, offsets=offsets, row_of_slot=ros, row_token=row_token,
+                num_dropped=int(nd[0]), R=int(R))
+
+
+def grouped_ffn(x_perm, offsets, w_gate, w_up, w_down, rows=None) -> np.ndarray:
+    x, dt = _act(x_perm)
+    wg, _ = _act(w_gate)
+    wu, _ = _act(w_up)
+    wd, _ = _act(w_down)
+    E, I, H = wg.shape
+    off = np.ascontiguousarray(offsets, dtype=np.int32)
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+    n = int(off[E]) if r is None else len(r)
+    y = np.empty((n, H), np.float32)
+    lib().oracle_grouped_ffn(E, H, I, dt, _p(x), _p(off), _p(wg), _p(wu), _p(wd), _p(r),
+                             0 if r is None else len(r), _p(y))
+    return y
+
+
+def combine(y_perm, row_of_slot, gates, y_shared=None) -> np.ndarray:
+    y = np.ascontiguousarray(y_perm, dtype=np.float32)
+    ros = np.ascontiguousarray(row_of_slot, dtype=np.int32)
+    g = np.ascontiguousarray(gates, dtype=np.float32)
+    ys = None if y_shared is None else np.ascontiguousarray(y_shared, dtype=np.float32)
+    T, k = ros.shape
+    H = y.shape[1]
+    out = np.empty((T, H), np.float32)
+    lib().oracle_combine(T, H, k, _p(y), _p(ros), _p(g), _p(ys), _p(out))
+    return out
+
+
+def layer_forward(x, w_router, w_gate, w_up, w_down, k_max, bias=None, k_per_token=None,
+                  score=0, renorm=1, routed_scale=1.0, num_groups=1, topk_groups=1, group_topn=0,
+                  capacity_factor=0.0, ws_gate=None, ws_up=None, ws_down=None, tokens=None):
+    """Whole layer; returns dict(out=[n,H] for `tokens` (or all), plus routing)."""
+    x, dt = _act(x)
+    wr, _ = _act(w_router)
+    wg, _ = _act(w_gate)
+    wu, _ = _act(w_up)
+    wd, _ = _act(w_down)
+    T, H = x.shape
+    E, I, _ = wg.shape
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    kpt = None if k_per_token is None else np.ascontiguousarray(k_per_token, dtype=np.int32)
+    if ws_gate is not None:
+        sg, _ = _act(ws_gate)
+        su, _ = _act(ws_up)
+        sd, _ = _act(ws_down)
+        Is = sg.shape[0]
+    else:
+        sg = su = sd = None
+        Is = 0
+    tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
+    n = T if tok is None else len(tok)
+    out = np.empty((n, H), np.float32)
+    logits = np.empty((T, E), np.float32)
+    ids = np.empty((T, k_max), np.int32)
+    gates = np.empty((T, k_max), np.float32)
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    ros = np.empty((T, k_max), np.int32)
+    row_token = np.full(T * k_max, -1, np.int32)
+    nd = np.zeros(1, np.int32)
+    lib().oracle_layer_forward(T, H, E, I, k_max, dt, _p(x), _p(wr), _p(b), _p(kpt), score, renorm,
+                               routed_scale, num_groups, topk_groups, group_topn, capacity_factor,
+                               _p(wg), _p(wu), _p(wd), Is, _p(sg), _p(su), _p(sd), _p(tok),
+                               0 if tok is None else len(tok), _p(out), _p(logits), _p(ids),
+                               _p(gates), _p(counts), _p(offsets), _p(ros), _p(row_token), _p(nd))
+    return dict(out=out, logits=logits, ids=ids, gates=gates, counts=counts, offsets=offsets,
+                row_of_slot=ros, row_token=row_token, num_dropped=int(nd[0]))
+
+
+def layer_forward_cfg(cfg, inputs_np, tokens=None):
+    """layer_forward with the routing options of a workloads.LayerConfig."""
+    i = inputs_np
+    return layer_forward(i["x"], i["w_router"], i["w_gate"], i["w_up"], i["w_down"], cfg.top_k,
+                         bias=i.get("bias"), k_per_token=i.get("k_per_token"), score=cfg.score,
+                         renorm=cfg.renormalize, routed_scale=cfg.routed_scale,
+                         num_groups=cfg.num_groups, topk_groups=cfg.topk_groups,
+                         group_topn=cfg.group_topn, capacity_factor=cfg.capacity_factor,
+                         ws_gate=i.get("ws_gate"), ws_up=i.get("ws_up"), ws_down=i.get("ws_down"),
+                         tokens=tokens)

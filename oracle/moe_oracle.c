@@ -1,0 +1,397 @@
+/*
+ * moe_oracle.c -- plain CPU oracle for one GPU's share of an expert-parallel
+ * Mixture-of-Experts layer forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or constant with the GPU library and must never serve as a
+ * fallback for it.
+ *
+ * What it computes (plain definitions, slow on purpose):
+ *   "Expert Parallelism: MoE model parallel split" (jwzheng96 sglang-learning),
+ *   §1: an MoE layer is Router -> choose top-k experts -> weighted sum; §12 Q2:
+ *   dispatch gives every token k target positions (the hidden state copied k
+ *   times) and combine merges the k outputs back into the token's position,
+ *   weighted by the router weights.
+ *   "Expert parallelism for MoE serving" (aiunderstanding.org), deep dive and
+ *   FAQ: a router picks the top-k experts per token; a per-expert capacity
+ *   (a maximum token count) drops tokens beyond it.
+ *   "LLM MoE Expert Parallel production practice" (oh-bug.com), the four
+ *   steps of an MoE layer: route top-K, send activations to the expert,
+ *   run the local expert, send outputs back and merge.
+ *
+ * Precision: every dot product and every gate is accumulated in fp64 in plain
+ * ascending order, then rounded once to fp32.  Decisions that floating point
+ * turns into integers (which experts a token picks, which groups survive) are
+ * taken on fp32 values, the precision the GPU takes them in: selection
+ * compares fp32 logits; group scores are fp32 sums of the sigmoid defined by
+ * sigmoid_spec below.
+ */
+#include <limits.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define OR_F32 0
+#define OR_BF16 1
+#define OR_SOFTMAX 0
+#define OR_SIGMOID 1
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* element i of an fp32 or raw-bf16 array, widened exactly */
+static double elem(const void* base, int dtype, size_t i) {
+  if (dtype == OR_BF16) {
+    uint32_t bits = ((uint32_t)((const uint16_t*)base)[i]) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+  }
+  return (double)((const float*)base)[i];
+}
+
+/* ---- router logits: logits[t][e] = sum_h x[t][h] * Wr[e][h] + b[e] --------- */
+void oracle_router_logits(int T, int H, int E, int dtype, const void* x, const void* w_router,
+                          const float* bias, float* logits) {
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int t = 0; t < T; ++t) {
+    for (int e = 0; e < E; ++e) {
+      double s = 0.0;
+      for (int h = 0; h < H; ++h)
+        s += elem(x, dtype, (size_t)t * H + h) * elem(w_router, dtype, (size_t)e * H + h);
+      if (bias) s += (double)bias[e];
+      logits[(size_t)t * E + e] = (float)s;
+    }
+  }
+}
+
+/* ---- sigmoid_spec: the fp32 logistic function both sides compute bit-for-bit.
+ * Definition (written out as IEEE single-precision operations, each rounded to
+ * nearest even, no contraction):
+ *   x <- min(max(x, -30), 30); z = -x
+ *   n = rint(z * log2e)                       (Cody & Waite argument reduction)
+ *   r = fma(-n, ln2_hi, z); r = fma(-n, ln2_lo, r)
+ *   p = sum_{i=0..7} r^i / i!  in Horner form with fma (Taylor series of e^r)
+ *   e = ldexp(p, n);  sigma = 1 / (1 + e)
+ * log2e = fp32(1/ln 2); ln2_hi = ln 2 truncated to 17 significant bits (so
+ * n*ln2_hi is exact for |n| < 128); ln2_lo = fp32(ln 2 - ln2_hi); the Taylor
+ * coefficients are fp32(1/i!). */
+float oracle_sigmoid_spec(float x) {
+  const float log2e = 0x1.715476p+0f;
+  const float ln2_hi = 0x1.62e400p-1f;
+  const float ln2_lo = 0x1.7f7d1cp-20f;
+  const float c7 = 0x1.a01a02p-13f, c6 = 0x1.6c16c2p-10f, c5 = 0x1.111112p-7f;
+  const float c4 = 0x1.555556p-5f, c3 = 0x1.555556p-3f, c2 = 0x1.0p-1f, c1 = 1.0f, c0 = 1.0f;
+  if (x < -30.0f) x = -30.0f;
+  if (x > 30.0f) x = 30.0f;
+  float z = -x;
+  float zl = z * log2e;
+  float n = rintf(zl);
+  float r = fmaf(-n, ln2_hi, z);
+  r = fmaf(-n, ln2_lo, r);
+  float p = c7;
+  p = fmaf(p, r, c6);
+  p = fmaf(p, r, c5);
+  p = fmaf(p, r, c4);
+  p = fmaf(p, r, c3);
+  p = fmaf(p, r, c2);
+  p = fmaf(p, r, c1);
+  p = fmaf(p, r, c0);
+  float e = ldexpf(p, (int)n);
+  float den = 1.0f + e;
+  return 1.0f / den;
+}
+
+void oracle_sigmoid_spec_array(int64_t n, const float* x, float* y) {
+  for (int64_t i = 0; i < n; ++i) y[i] = oracle_sigmoid_spec(x[i]);
+}
+
+/* (value a, index ia) ranks before (value b, index ib): larger value first,
+ * equal values by the lower index. */
+static int ranks_before(float a, int ia, float b, int ib) {
+  return a > b || (a == b && ia < ib);
+}
+
+/* ---- routing: scoring, optional group limit, top-k_t, gates ---------------
+ * Selection key is the fp32 logit (after bias); the scoring function is monotone
+ * so it picks the same set, and ranking logits avoids the ties fp32 sigmoid
+ * saturation would create.  Group-limited routing ("node-limited routing",
+ * deployment list of "Expert parallelism for MoE serving"): experts form G
+ * consecutive groups of E/G; a group's score is the fp32 sum of its `topn`
+ * largest sigmoid_spec scores added largest first (topn <= 0 means 1); the
+ * topk_groups best groups (score desc, index asc) stay eligible.
+ * Gates: softmax over all E (or sigmoid) in fp64; renormalised over the k_t
+ * selected when asked; multiplied by routed_scale.  Unused slots: id -1,
+ * gate 0.  A k_t outside [1, k_max] leaves the token with no slots.  */
+void oracle_route(int T, int E, const float* logits, int k_max, const int32_t* k_per_token,
+                  int score, int renorm, float routed_scale, int G, int topk_groups, int topn,
+                  int32_t* ids, float* gates) {
+  if (topn <= 0) topn = 1;
+#pragma omp parallel
+  {
+    unsigned char* eligible = (unsigned char*)malloc((size_t)E);
+    unsigned char* taken = (unsigned char*)malloc((size_t)E);
+    float* gscore = (float*)malloc(sizeof(float) * (size_t)(G > 0 ? G : 1));
+    unsigned char* gkeep = (unsigned char*)malloc((size_t)(G > 0 ? G : 1));
+    float* vals = (float*)malloc(sizeof(float) * (size_t)E);
+#pragma omp for schedule(static)
+    for (int t = 0; t < T; ++t) {
+      const float* l = logits + (size_t)t * E;
+      int32_t* id = ids + (size_t)t * k_max;
+      float* gt = gates + (size_t)t * k_max;
+      for (int j = 0; j < k_max; ++j) { id[j] = -1; gt[j] = 0.0f; }
+      int kt = k_per_token ? k_per_token[t] : k_max;
+      if (kt < 1 || kt > k_max) continue;
+
+      for (int e = 0; e < E; ++e) { eligible[e] = 1; taken[e] = 0; }
+      if (G > 1) {
+        int gs = E / G;
+        for (int g = 0; g < G; ++g) {
+          int n = 0;
+          for (int e = g * gs; e < (g + 1) * gs; ++e) vals[n++] = oracle_sigmoid_spec(l[e]);
+          /* partial selection sort: the topn largest, in descending order */
+          int m = topn < n ? topn : n;
+          for (int a = 0; a < m; ++a) {
+            int best = a;
+            for (int b = a + 1; b < n; ++b) if (vals[b] > vals[best]) best = b;
+            float tmp = vals[a]; vals[a] = vals[best]; vals[best] = tmp;
+          }
+          float s = vals[0];
+          for (int a = 1; a < m; ++a) s = s + vals[a];
+          gscore[g] = s;
+          gkeep[g] = 0;
+        }
+        int keep = topk_groups < G ? topk_groups : G;
+        for (int q = 0; q < keep; ++q) {
+          int best = -1;
+          for (int g = 0; g < G; ++g) {
+            if (gkeep[g]) continue;
+            if (best < 0 || ranks_before(gscore[g], g, gscore[best], best)) best = g;
+          }
+          gkeep[best] = 1;
+        }
+        for (int e = 0; e < E; ++e) eligible[e] = gkeep[e / gs];
+      }
+
+      int nsel = 0;
+      for (int j = 0; j < kt; ++j) {
+        int best = -1;
+        for (int e = 0; e < E; ++e) {
+          if (!eligible[e] || taken[e]) continue;
+          if (best < 0 || ranks_before(l[e], e, l[best], best)) best = e;
+        }
+        if (best < 0) break;          /* fewer eligible experts than k_t */
+        taken[best] = 1;
+        id[j] = best;
+        nsel++;
+      }
+
+      double p[64];
+      double* pp = nsel <= 64 ? p : (double*)malloc(sizeof(double) * (size_t)nsel);
+      if (score == OR_SOFTMAX) {
+        double mx = -INFINITY;
+        for (int e = 0; e < E; ++e) if ((double)l[e] > mx) mx = (double)l[e];
+        double den = 0.0;
+        for (int e = 0; e < E; ++e) den += exp((double)l[e] - mx);
+        for (int j = 0; j < nsel; ++j) pp[j] = exp((double)l[id[j]] - mx) / den;
+      } else {
+        for (int j = 0; j < nsel; ++j) pp[j] = 1.0 / (1.0 + exp(-(double)l[id[j]]));
+      }
+      if (renorm) {
+        double s = 0.0;
+        for (int j = 0; j < nsel; ++j) s += pp[j];
+        for (int j = 0; j < nsel; ++j) pp[j] /= s;
+      }
+      for (int j = 0; j < nsel; ++j) gt[j] = (float)(pp[j] * (double)routed_scale);
+      if (pp != p) free(pp);
+    }
+    free(eligible); free(taken); free(gscore); free(gkeep); free(vals);
+  }
+}
+
+/* ---- capacity ---------------------------------------------------------------
+ * C = ceil(cf * A / E) in fp64, A = number of routed slots; cf <= 0: no limit. */
+int64_t oracle_capacity(float cf, int64_t A, int E) {
+  if (!(cf > 0.0f)) return INT64_MAX;
+  return (int64_t)ceil((double)cf * (double)A / (double)E);
+}
+
+/* ---- dispatch: histogram, capacity, offsets, stable permutation ------------
+ * Slots are visited token-major (t ascending, then slot j).  Each expert keeps
+ * its first C slots in that order ("per-expert capacity ... drop tokens beyond
+ * it", FAQ of "Expert parallelism for MoE serving"); the kept rows of an expert
+ * are contiguous and in token order ("token sorting" of §7, "Expert
+ * Parallelism: MoE model parallel split").
+ * row_of_slot[s] = offsets[e] + rank, or -1 when unused or dropped;
+ * row_token[row] = t.  Returns the number of kept rows R. */
+int32_t oracle_dispatch(int T, int E, int k_max, const int32_t* ids, float cf, int32_t* counts,
+                        int32_t* offsets, int32_t* row_of_slot, int32_t* row_token,
+                        int32_t* num_dropped) {
+  int64_t A = 0;
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t s = 0; s < (int64_t)T * k_max; ++s) {
+    int e = ids[s];
+    if (e >= 0 && e < E) { counts[e]++; A++; }
+  }
+  int64_t C = oracle_capacity(cf, A, E);
+  offsets[0] = 0;
+  for (int e = 0; e < E; ++e) {
+    int64_t kept = counts[e] < C ? counts[e] : C;
+    offsets[e + 1] = offsets[e] + (int32_t)kept;
+  }
+  int32_t* seen = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+  for (int t = 0; t < T; ++t) {
+    for (int j = 0; j < k_max; ++j) {
+      int64_t s = (int64_t)t * k_max + j;
+      int e = ids[s];
+      if (e < 0 || e >= E) { row_of_slot[s] = -1; continue; }
+      int32_t r = seen[e]++;
+      if (r < C) {
+        int32_t row = offsets[e] + r;
+        row_of_slot[s] = row;
+        row_token[row] = t;
+      } else {
+        row_of_slot[s] = -1;
+      }
+    }
+  }
+  free(seen);
+  if (num_dropped) *num_dropped = (int32_t)(A - offsets[E]);
+  return offsets[E];
+}
+
+/* ---- one expert's SwiGLU FFN on one activation row -----------------------
+ * y = Wd . (silu(Wg . x) * (Wu . x)), silu(z) = z / (1 + e^-z); fp64 sums.
+ * wg, wu: [I][H] rows for this expert; wd: [H][I]. */
+static void ffn_row(int H, int I, int dtype, const void* x, size_t xo, const void* wg,
+                    const void* wu, size_t wo_gu, const void* wd, size_t wo_d, double* hbuf,
+                    double* y) {
+  for (int i = 0; i < I; ++i) {
+    double a = 0.0, u = 0.0;
+    for (int h = 0; h < H; ++h) {
+      double xv = elem(x, dtype, xo + h);
+      a += elem(wg, dtype, wo_gu + (size_t)i * H + h) * xv;
+      u += elem(wu, dtype, wo_gu + (size_t)i * H + h) * xv;
+    }
+    hbuf[i] = a / (1.0 + exp(-a)) * u;
+  }
+  for (int c = 0; c < H; ++c) {
+    double s = 0.0;
+    for (int i = 0; i < I; ++i) s += elem(wd, dtype, wo_d + (size_t)c * I + i) * hbuf[i];
+    y[c] = s;
+  }
+}
+
+/* ---- grouped FFN on permuted rows ----------------------------------------
+ * y_perm[r] = FFN_{e(r)}(x_perm[r]) where e(r) is the expert whose range
+ * [offsets[e], offsets[e+1]) holds r.  rows: optional subset (n_rows entries);
+ * NULL computes rows 0..offsets[E]-1 and n_rows is ignored.  y is [n][H] fp32
+ * in the order of `rows`. */
+void oracle_grouped_ffn(int E, int H, int I, int dtype, const void* x_perm,
+                        const int32_t* offsets, const void* w_gate, const void* w_up,
+                        const void* w_down, const int32_t* rows, int n_rows, float* y) {
+  int n = rows ? n_rows : offsets[E];
+#pragma omp parallel
+  {
+    double* hb = (double*)malloc(sizeof(double) * (size_t)I);
+    double* yb = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(dynamic, 1)
+    for (int q = 0; q < n; ++q) {
+      int r = rows ? rows[q] : q;
+      int e = 0;
+      while (e < E && !(r >= offsets[e] && r < offsets[e + 1])) ++e;
+      if (e == E) {
+        for (int c = 0; c < H; ++c) y[(size_t)q * H + c] = 0.0f;
+        continue;
+      }
+      ffn_row(H, I, dtype, x_perm, (size_t)r * H, w_gate, w_up, (size_t)e * I * H, w_down,
+              (size_t)e * H * I, hb, yb);
+      for (int c = 0; c < H; ++c) y[(size_t)q * H + c] = (float)yb[c];
+    }
+    free(hb);
+    free(yb);
+  }
+}
+
+/* ---- combine: out[t] = sum_j g[t][j] * y[row_of_slot[t][j]] (+ y_shared[t]) -
+ * j ascending; unused or dropped slots (row -1) contribute nothing; the shared
+ * expert's output is added last with weight 1. */
+void oracle_combine(int T, int H, int k_max, const float* y_perm, const int32_t* row_of_slot,
+                    const float* gates, const float* y_shared, float* out) {
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    for (int c = 0; c < H; ++c) {
+      double acc = 0.0;
+      for (int j = 0; j < k_max; ++j) {
+        int32_t r = row_of_slot[(size_t)t * k_max + j];
+        if (r < 0) continue;
+        acc += (double)gates[(size_t)t * k_max + j] * (double)y_perm[(size_t)r * H + c];
+      }
+      if (y_shared) acc += (double)y_shared[(size_t)t * H + c];
+      out[(size_t)t * H + c] = (float)acc;
+    }
+  }
+}
+
+/* ---- whole layer, per token over its chosen experts -----------------------
+ * out_t = sum over kept slots j (ascending) of g_{t,j} * FFN_{e_{t,j}}(x_t)
+ *         + FFN_shared(x_t)   (when a shared expert is given; weight 1).
+ * Routing and dispatch run over all T tokens (capacity depends on all of
+ * them); the FFN part runs for the tokens in `tokens` (n_tok entries, or all T
+ * when tokens is NULL).  out is [n][H] in the order of `tokens`.
+ * logits/ids/gates/counts/offsets/row_of_slot/row_token are caller buffers
+ * (sizes T*E, T*k_max, T*k_max, E, E+1, T*k_max, T*k_max). */
+void oracle_layer_forward(int T, int H, int E, int I, int k_max, int dtype, const void* x,
+                          const void* w_router, const float* bias, const int32_t* k_per_token,
+                          int score, int renorm, float routed_scale, int G, int topk_groups,
+                          int topn, float cf, const void* w_gate, const void* w_up,
+                          const void* w_down, int Is, const void* ws_gate, const void* ws_up,
+                          const void* ws_down, const int32_t* tokens, int n_tok, float* out,
+                          float* logits, int32_t* ids, float* gates, int32_t* counts,
+                          int32_t* offsets, int32_t* row_of_slot, int32_t* row_token,
+                          int32_t* num_dropped) {
+  oracle_router_logits(T, H, E, dtype, x, w_router, bias, logits);
+  oracle_route(T, E, logits, k_max, k_per_token, score, renorm, routed_scale, G, topk_groups,
+               topn, ids, gates);
+  oracle_dispatch(T, E, k_max, ids, cf, counts, offsets, row_of_slot, row_token, num_dropped);
+  int n = tokens ? n_tok : T;
+  int Imax = I > Is ? I : Is;
+#pragma omp parallel
+  {
+    double* hb = (double*)malloc(sizeof(double) * (size_t)Imax);
+    double* yb = (double*)malloc(sizeof(double) * (size_t)H);
+    double* acc = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(dynamic, 1)
+    for (int q = 0; q < n; ++q) {
+      int t = tokens ? tokens[q] : q;
+      for (int c = 0; c < H; ++c) acc[c] = 0.0;
+      for (int j = 0; j < k_max; ++j) {
+        size_t s = (size_t)t * k_max + j;
+        if (row_of_slot[s] < 0) continue;
+        int e = ids[s];
+        ffn_row(H, I, dtype, x, (size_t)t * H, w_gate, w_up, (size_t)e * I * H, w_down,
+                (size_t)e * H * I, hb, yb);
+        double g = (double)gates[s];
+        for (int c = 0; c < H; ++c) acc[c] += g * yb[c];
+      }
+      if (Is > 0 && ws_gate) {
+        ffn_row(H, Is, dtype, x, (size_t)t * H, ws_gate, ws_up, 0, ws_down, 0, hb, yb);
+        for (int c = 0; c < H; ++c) acc[c] += yb[c];
+      }
+      for (int c = 0; c < H; ++c) out[(size_t)q * H + c] = (float)acc[c];
+    }
+    free(hb);
+    free(yb);
+    free(acc);
+  }
+}
