@@ -1,0 +1,226 @@
+"""Benchmark: one GPU's share of an expert-parallel MoE layer forward on MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one moe_layer_forward call (router, top-k, dispatch, gather,
+grouped gate/up + SwiGLU, grouped down, shared expert, combine) over one batch
+of seeded synthetic input already resident in HBM.  The default workload is
+the Mixtral-8x7B-shaped prefill layer (T=4096, H=4096, E=8, top-2, I=14336,
+bf16 with fp32 accumulation).  Prints one JSON line on stdout.
+
+Timing: W untimed warm-up steps, then K steps between HIP events recorded on
+the stream the library launches on; every stage of every timed step is also
+bracketed by its own events (moe_debug stage events), which gives the
+dominant kernel's average duration for the roofline figure.  The CPU-oracle
+leg times the plain CPU oracle on a bounded token sample of the same
+workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
+PEAK_F32_FLOPS = 157.3e12     # MI355X fp32 vector
+PEAK_HBM = 8.0e12             # MI355X HBM3E bytes/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_model(cfg, counts_kept, eb):
+    """Algorithmic flops and bytes of the grouped-GEMM stages from realized counts."""
+    H, I, Is, T = cfg.hidden, cfg.inter, cfg.shared_inter, cfg.tokens
+    R = int(counts_kept.sum())
+    touched = int((counts_kept > 0).sum())
+    st = {}
+    st["gate_up"] = dict(flops=4.0 * R * H * I,
+                         bytes=R * H * eb + 2.0 * touched * I * H * eb + R * I * eb, units=R)
+    st["down"] = dict(flops=2.0 * R * H * I, bytes=R * I * eb + 1.0 * touched * H * I * eb + R * H * 4.0, units=R)
+    if Is:
+        st["shared"] = dict(flops=6.0 * T * H * Is, bytes=T * H * eb + 3.0 * Is * H * eb + T * Is * eb * 2
+                            + T * H * 4.0, units=T)
+    return st
+
+
+def cpu_baseline(cfg, inp, budget_s=15.0):
+    """The oracle as it stands, on a bounded token sample of the workload."""
+    import oracle
+    import workloads as W
+    x, wr = W.to_numpy_raw(inp["x"]), W.to_numpy_raw(inp["w_router"])
+    b, kpt = W.to_numpy_raw(inp["bias"]), W.to_numpy_raw(inp["k_per_token"])
+    # routing of every token (capacity depends on all of them), timed alone
+    t0 = time.perf_counter()
+    lo = oracle.router_logits(x, wr, b)
+    ids, _ = oracle.route(lo, cfg.top_k, kpt, cfg.score, cfg.renormalize, cfg.routed_scale, cfg.num_groups,
+                          cfg.topk_groups, cfg.group_topn)
+    t_route = time.perf_counter() - t0
+    host = {k: W.to_numpy_raw(v) for k, v in inp.items() if k not in ("w_gate", "w_up", "w_down")}
+    rng = np.random.default_rng(0)
+
+    def run(n):
+        tok = np.sort(rng.choice(cfg.tokens, size=n, replace=False)).astype(np.int32)
+        used = sorted(set(int(e) for e in ids[tok].reshape(-1) if e >= 0))
+        for key in ("w_gate", "w_up", "w_down"):
+            w = inp[key]
+            arr = np.empty(tuple(w.shape), np.uint16 if cfg.dtype == W.DT_BF16 else np.float32)
+            for e in used:
+                arr[e] = W.to_numpy_raw(w[e])
+            host[key] = arr
+        t1 = time.perf_counter()
+        oracle.layer_forward_cfg(cfg, host, tokens=tok)
+        t_all = time.perf_counter() - t1
+        return t_all
+
+    n = min(cfg.tokens, 2 * oracle.num_threads())
+    t_n = run(n)
+    # the call re-routes every token; remove that, add back the sample's share
+    per_tok = max(t_n - t_route, 1e-9) / n
+    n2 = int(min(cfg.tokens, max(n, (budget_s - t_route) / per_tok)))
+    if n2 > n:
+        t_n = run(n2)
+        n = n2
+    t_sample = max(t_n - t_route, 1e-9) + t_route * n / cfg.tokens
+    return dict(value=n / t_sample, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{n} of {cfg.tokens} tokens of the {cfg.name} workload: routing of all tokens "
+                       f"({t_route:.2f} s, charged pro rata) + per-token FFN and combine of the sample "
+                       f"({t_n - t_route:.2f} s); fp64-accumulating C oracle, OpenMP over tokens")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the layer share it measures is "
+                                   "one GPU's expert-parallel share; multi-GPU runs are not supported",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import workloads as W
+    from expert_serving_amd import abi, hiprt
+
+    cfg = W.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    inp = W.make_layer_inputs(cfg, dev)
+    shape = abi.make_shape(cfg)
+    ws = torch.empty(abi.moe_workspace_size(shape), dtype=torch.uint8, device=dev)
+    out = torch.empty(cfg.tokens, cfg.hidden, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    counts = torch.empty(cfg.experts, dtype=torch.int32, device=dev)
+    offsets = torch.empty(cfg.experts + 1, dtype=torch.int32, device=dev)
+    dropped = torch.empty(1, dtype=torch.int32, device=dev)
+
+    def step(dbg=None):
+        abi.moe_layer_forward(shape, inp["x"], inp["w_router"], inp["bias"], inp["k_per_token"], inp["w_gate"],
+                              inp["w_up"], inp["w_down"], inp["ws_gate"], inp["ws_up"], inp["ws_down"], out, dbg,
+                              ws, stream=stream)
+
+    # one call with inspection outputs for the realized counts
+    step(dict(expert_counts=counts, expert_offsets=offsets, num_dropped=dropped))
+    torch.cuda.synchronize()
+    off = offsets.cpu().numpy()
+    kept = np.diff(off)
+    cnt = counts.cpu().numpy()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    nst = len(abi.MOE_STAGES)
+    evs = [[(hiprt.event_create(), hiprt.event_create()) for _ in range(nst)] for _ in range(K)]
+    dbgs = []
+    for k in range(K):
+        d = abi.MoeDebug()
+        for i in range(nst):
+            d.stage_start[i] = evs[k][i][0]
+            d.stage_stop[i] = evs[k][i][1]
+        dbgs.append(d)
+    t_start, t_stop = hiprt.event_create(), hiprt.event_create()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    hiprt.event_record(t_start, stream)
+    for k in range(K):
+        step(dbgs[k])
+    hiprt.event_record(t_stop, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = hiprt.elapsed_ms(t_start, t_stop)
+    stage_ms = {name: float(np.mean([hiprt.elapsed_ms(*evs[k][i]) for k in range(K)]))
+                for i, name in enumerate(abi.MOE_STAGES)}
+    ms_per_step = total_ms / K
+    tokens_per_s = cfg.tokens / (ms_per_step / 1e3)
+
+    eb = cfg.elem_bytes
+    model = gemm_model(cfg, kept, eb)
+    peak_f = PEAK_BF16_FLOPS if cfg.dtype == W.DT_BF16 else PEAK_F32_FLOPS
+    # dominant kernel: the grouped-GEMM stage with the largest time
+    dom = max(model, key=lambda s: stage_ms[s])
+    m = model[dom]
+    t_s = stage_ms[dom] / 1e3
+    bound = "mfma" if m["flops"] / peak_f >= m["bytes"] / PEAK_HBM else "hbm"
+    if bound == "mfma":
+        achieved, peak, unit = m["flops"] / t_s / 1e12, peak_f / 1e12, "TFLOP/s"
+    else:
+        achieved, peak, unit = m["bytes"] / t_s / 1e9, PEAK_HBM / 1e9, "GB/s"
+    gemm_stages = [s for s in model]
+    t_gemm = sum(stage_ms[s] for s in gemm_stages) / 1e3
+    f_gemm = sum(model[s]["flops"] for s in gemm_stages)
+    b_gemm = sum(model[s]["bytes"] for s in gemm_stages)
+    t_roof_gemm = max(f_gemm / peak_f, b_gemm / PEAK_HBM)
+
+    line = {
+        "metric": "MoE-layer tokens/sec at 1 GPU; grouped-GEMM % of bf16 MFMA / HBM peak",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == W.DT_BF16 else "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
+        "config": {"workload": cfg.name, "tokens": cfg.tokens, "hidden": cfg.hidden, "experts": cfg.experts,
+                   "top_k": cfg.top_k, "intermediate": cfg.inter, "shared_intermediate": cfg.shared_inter,
+                   "capacity_factor": cfg.capacity_factor, "parallelism": "one GPU's expert-parallel share"},
+        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom,
+                     "kernel_ms": round(stage_ms[dom], 4),
+                     "per_launch_algorithmic": {"flops": m["flops"], "bytes": m["bytes"], "rows": m["units"]}},
+        "grouped_gemm": {"ms": round(t_gemm * 1e3, 4), "tflops": round(f_gemm / t_gemm / 1e12, 2),
+                         "frac_of_roofline": round(t_roof_gemm / t_gemm, 4),
+                         "frac_of_mfma_peak": round(f_gemm / t_gemm / peak_f, 4),
+                         "frac_of_hbm_peak": round(b_gemm / t_gemm / PEAK_HBM, 4)},
+        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "routing": {"rows_kept": int(kept.sum()), "dropped": int(cnt.sum() - kept.sum()),
+                    "experts_touched": int((kept > 0).sum()),
+                    "max_over_mean_load": round(float(cnt.max() / max(cnt.mean(), 1e-9)), 3)},
+        "host_wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,254 @@
+// S3-S6: dispatch indexing and the permutation gather.
+//
+// On one GPU the dispatch all-to-all of expert parallelism ("Expert
+// Parallelism: MoE model parallel split", §3 and §12 Q2) becomes a stable
+// permutation of the k_t routed copies of each token into per-expert
+// contiguous row groups, sorted by destination (the "token sorting" of §7),
+// with an optional per-expert capacity that drops slots beyond it in token
+// order ("Expert parallelism for MoE serving", technical notes and FAQ).
+//
+// Determinism: counts use LDS atomics (order does not change a count); every
+// position comes from scans and in-wave ranks, never from an atomic claim.
+//   k_tile_hist     per tile of kDispatchTileSlots slots: expert histogram
+//   k_scan_capacity column scan over tiles, capacity, offsets, drops
+//   k_rank_scatter  in-tile stable rank -> row_of_slot, row_token
+//   k_gather        x_perm[row] = x[row_token[row]]
+//   k_build_sched   row tiles of the grouped GEMM from the offsets
+#include <climits>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kRankWaves = 4;
+constexpr int kSlotsPerWave = kDispatchTileSlots / kRankWaves;
+
+__global__ __launch_bounds__(256) void k_tile_hist(const int32_t* __restrict__ ids,
+                                                   int total_slots, int E,
+                                                   int32_t* __restrict__ tile_counts,
+                                                   uint32_t* __restrict__ flags) {
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int bad;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  const int s0 = blockIdx.x * kDispatchTileSlots;
+  const int s1 = min(s0 + kDispatchTileSlots, total_slots);
+  for (int s = s0 + threadIdx.x; s < s1; s += blockDim.x) {
+    const int e = ids[s];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    else if (e != -1) bad = 1;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    tile_counts[(size_t)blockIdx.x * E + e] = cnt[e];
+  if (threadIdx.x == 0 && bad) atomicOr(flags, (uint32_t)MOE_FLAG_BAD_EXPERT);
+}
+
+// One block of 1024 threads.  Turns tile_counts into per-tile bases (in place),
+// writes counts, capacity-limited offsets, the drop count and the capacity.
+__global__ __launch_bounds__(1024) void k_scan_capacity(int32_t* __restrict__ tile_counts,
+                                                        int n_tiles, int E, float cf,
+                                                        int32_t* __restrict__ counts,
+                                                        int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ num_dropped,
+                                                        int32_t* __restrict__ cap_out) {
+  __shared__ long long s_total[1024];
+  __shared__ int s_scan[1024];
+  const int tid = threadIdx.x;
+  int run = 0;
+  if (tid < E) {
+    for (int b = 0; b < n_tiles; ++b) {
+      int32_t* p = tile_counts + (size_t)b * E + tid;
+      const int c = *p;
+      *p = run;
+      run += c;
+    }
+    counts[tid] = run;
+  }
+  s_total[tid] = tid < E ? run : 0;
+  __syncthreads();
+  for (int off = 512; off >= 1; off >>= 1) {
+    if (tid < off) s_total[tid] += s_total[tid + off];
+    __syncthreads();
+  }
+  const long long A = s_total[0];
+  long long C = LLONG_MAX;
+  if (cf > 0.0f) C = (long long)ceil((double)cf * (double)A / (double)E);
+  const int kept = tid < E ? (int)(run < C ? run : C) : 0;
+  // inclusive Hillis-Steele scan of kept over the block
+  s_scan[tid] = kept;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int add = tid >= off ? s_scan[tid - off] : 0;
+    __syncthreads();
+    s_scan[tid] += add;
+    __syncthreads();
+  }
+  if (tid < E) offsets[tid + 1] = s_scan[tid];
+  if (tid == 0) {
+    offsets[0] = 0;
+    const int R = s_scan[E - 1];
+    if (num_dropped) *num_dropped = (int32_t)(A - R);
+    *cap_out = C > INT_MAX ? INT_MAX : (int32_t)C;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_rank_scatter(const int32_t* __restrict__ ids,
+                                                      int total_slots, int k_max, int E,
+                                                      const int32_t* __restrict__ tile_base,
+                                                      const int32_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ cap_p,
+                                                      int32_t* __restrict__ row_of_slot,
+                                                      int32_t* __restrict__ row_token) {
+  __shared__ int wcnt[kRankWaves][kMaxExperts];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int tile = blockIdx.x;
+  const int wbase = tile * kDispatchTileSlots + wave * kSlotsPerWave;
+
+  for (int i = threadIdx.x; i < kRankWaves * kMaxExperts; i += blockDim.x)
+    (&wcnt[0][0])[i] = 0;
+  __syncthreads();
+  // per-wave histogram of the wave's sub-tile
+  for (int q = lane; q < kSlotsPerWave; q += 64) {
+    const int s = wbase + q;
+    if (s < total_slots) {
+      const int e = ids[s];
+      if (e >= 0 && e < E) atomicAdd(&wcnt[wave][e], 1);
+    }
+  }
+  __syncthreads();
+  // running base of each wave = tile base + counts of the earlier waves
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = tile_base[(size_t)tile * E + e];
+    for (int w = 0; w < kRankWaves; ++w) {
+      const int c = wcnt[w][e];
+      wcnt[w][e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  const int cap = *cap_p;
+  // walk the sub-tile in order, 64 slots at a time
+  for (int c0 = 0; c0 < kSlotsPerWave; c0 += 64) {
+    const int s = wbase + c0 + lane;
+    int e = -1;
+    if (s < total_slots) {
+      e = ids[s];
+      if (e < 0 || e >= E) e = -1;
+    }
+    // stable rank inside the 64-slot chunk: equal experts in earlier lanes
+    int before = 0, after = 0;
+    for (int j = 0; j < 64; ++j) {
+      const int ej = __builtin_amdgcn_readlane(e, j);
+      before += (ej == e && j < lane) ? 1 : 0;
+      after += (ej == e && j > lane) ? 1 : 0;
+    }
+    if (e >= 0) {
+      const int rank = wcnt[wave][e] + before;
+      const int row = rank < cap ? offsets[e] + rank : -1;
+      row_of_slot[s] = row;
+      if (row >= 0) row_token[row] = s / k_max;
+    } else if (s < total_slots) {
+      row_of_slot[s] = -1;
+    }
+    // the last lane of each expert advances that expert's running rank
+    if (e >= 0 && after == 0) wcnt[wave][e] += before + 1;
+  }
+}
+
+// One wavefront per permuted row; 16-byte vector copies.
+__global__ __launch_bounds__(256) void k_gather(const uint4* __restrict__ x,
+                                                const int32_t* __restrict__ row_token,
+                                                const int32_t* __restrict__ offsets, int E,
+                                                int row_vecs, uint4* __restrict__ x_perm) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= offsets[E]) return;
+  const uint4* src = x + (size_t)row_token[r] * row_vecs;
+  uint4* dst = x_perm + (size_t)r * row_vecs;
+  for (int i = lane; i < row_vecs; i += 64) dst[i] = src[i];
+}
+
+// Row tiles of `bm` rows per expert: tile list in expert order.
+__global__ __launch_bounds__(512) void k_build_sched(const int32_t* __restrict__ offsets, int E,
+                                                     int bm, MTile* __restrict__ sched,
+                                                     int32_t* __restrict__ count, int max_tiles) {
+  __shared__ int s_scan[512];
+  const int tid = threadIdx.x;
+  int nt = 0, r0 = 0, kept = 0;
+  if (tid < E) {
+    r0 = offsets[tid];
+    kept = offsets[tid + 1] - r0;
+    nt = (kept + bm - 1) / bm;
+  }
+  s_scan[tid] = nt;
+  __syncthreads();
+  for (int off = 1; off < 512; off <<= 1) {
+    const int add = tid >= off ? s_scan[tid - off] : 0;
+    __syncthreads();
+    s_scan[tid] += add;
+    __syncthreads();
+  }
+  const int base = s_scan[tid] - nt;
+  for (int i = 0; i < nt; ++i) {
+    const int slot = base + i;
+    if (slot < max_tiles) {
+      MTile m;
+      m.expert = tid;
+      m.row0 = r0 + i * bm;
+      m.rows = min(bm, kept - i * bm);
+      m.pad = 0;
+      sched[slot] = m;
+    }
+  }
+  if (tid == 511) *count = min(s_scan[511], max_tiles);
+}
+
+__global__ void k_clear_flags(uint32_t* flags) { *flags = 0u; }
+
+}  // namespace
+
+hipError_t launch_clear_flags(uint32_t* flags, hipStream_t st) {
+  hipLaunchKernelGGL(k_clear_flags, dim3(1), dim3(1), 0, st, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, int32_t* counts,
+                           int32_t* offsets, int32_t* row_of_slot, int32_t* row_token,
+                           int32_t* num_dropped, int32_t* tile_counts, int n_tiles,
+                           uint32_t* flags, hipStream_t st) {
+  const int total = s.num_tokens * s.top_k;
+  const int E = s.num_experts;
+  // the capacity is kept right after the tile table
+  int32_t* cap = tile_counts + (size_t)n_tiles * E;
+  hipLaunchKernelGGL(k_tile_hist, dim3(n_tiles), dim3(256), 0, st, ids, total, E, tile_counts,
+                     flags);
+  hipLaunchKernelGGL(k_scan_capacity, dim3(1), dim3(1024), 0, st, tile_counts, n_tiles, E,
+                     s.capacity_factor, counts, offsets, num_dropped, cap);
+  hipLaunchKernelGGL(k_rank_scatter, dim3(n_tiles), dim3(256), 0, st, ids, total, s.top_k, E,
+                     tile_counts, offsets, cap, row_of_slot, row_token);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const moe_shape& s, const void* x, const int32_t* row_token,
+                         const int32_t* offsets, void* x_perm, hipStream_t st) {
+  const int eb = s.act_dtype == MOE_BF16 ? 2 : 4;
+  const int row_vecs = s.hidden * eb / 16;
+  const int max_rows = s.num_tokens * s.top_k;
+  hipLaunchKernelGGL(k_gather, dim3((max_rows + 3) / 4), dim3(256), 0, st,
+                     static_cast<const uint4*>(x), row_token, offsets, s.num_experts, row_vecs,
+                     static_cast<uint4*>(x_perm));
+  return hipGetLastError();
+}
+
+hipError_t launch_build_schedule(const int32_t* offsets, int E, int bm, MTile* sched,
+                                 int32_t* count, int max_tiles, hipStream_t st) {
+  hipLaunchKernelGGL(k_build_sched, dim3(1), dim3(512), 0, st, offsets, E, bm, sched, count,
+                     max_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,410 @@
+// Host side of the C ABI: argument validation (pure host code, before any HIP
+// call), workspace planning, and the launch sequence of each entry point.
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+thread_local int32_t g_last_hip_error = 0;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline int elem_bytes(int dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+moe_status hip_fail(hipError_t e) {
+  g_last_hip_error = (int32_t)e;
+  return MOE_ERR_HIP;
+}
+
+// Shape rules shared by every entry point.
+moe_status check_shape(const moe_shape* s) {
+  if (!s) return MOE_ERR_INVALID_ARG;
+  if (s->num_tokens < 0 || s->hidden <= 0 || s->intermediate <= 0) return MOE_ERR_INVALID_ARG;
+  if (s->num_experts < 1) return MOE_ERR_INVALID_ARG;
+  if (s->num_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (s->top_k < 1 || s->top_k > s->num_experts) return MOE_ERR_INVALID_ARG;
+  if (s->top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  if (s->score != MOE_SCORE_SOFTMAX && s->score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (s->renormalize != 0 && s->renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(s->routed_scale) || !std::isfinite(s->capacity_factor))
+    return MOE_ERR_INVALID_ARG;
+  if (s->act_dtype != MOE_F32 && s->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (s->out_dtype != MOE_F32 && s->out_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (s->shared_intermediate < 0) return MOE_ERR_INVALID_ARG;
+  if (s->num_groups < 1) return MOE_ERR_INVALID_ARG;
+  if (s->num_groups > 1) {
+    if (s->num_experts % s->num_groups != 0) return MOE_ERR_INVALID_ARG;
+    if (s->num_groups > 64) return MOE_ERR_UNSUPPORTED;
+    if (s->topk_groups < 1 || s->topk_groups > s->num_groups) return MOE_ERR_INVALID_ARG;
+    const int gs = s->num_experts / s->num_groups;
+    if (s->group_topn < 0 || s->group_topn > gs) return MOE_ERR_INVALID_ARG;
+    if (s->group_topn > 8) return MOE_ERR_UNSUPPORTED;
+    // the kept groups must hold at least k experts
+    if ((long long)s->topk_groups * gs < s->top_k) return MOE_ERR_INVALID_ARG;
+  }
+  const int mult = s->act_dtype == MOE_BF16 ? 64 : 4;
+  if (s->hidden % mult || s->intermediate % mult || s->shared_intermediate % mult)
+    return MOE_ERR_UNSUPPORTED;
+  // slot and row indices are int32
+  if ((long long)s->num_tokens * s->top_k > (long long)INT_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  if ((long long)s->num_tokens * s->num_experts > (long long)INT_MAX) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+#define MOE_TRY(expr)                      \
+  do {                                     \
+    const moe_status st_ = (expr);         \
+    if (st_ != MOE_OK) return st_;         \
+  } while (0)
+#define MOE_HIP(expr)                      \
+  do {                                     \
+    const hipError_t e_ = (expr);          \
+    if (e_ != hipSuccess) return hip_fail(e_); \
+  } while (0)
+
+inline moe_status need(const void* p) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  return aligned16(p) ? MOE_OK : MOE_ERR_INVALID_ARG;
+}
+// 4-byte aligned index/float arrays
+inline moe_status need4(const void* p) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  return (reinterpret_cast<uintptr_t>(p) & 3u) ? MOE_ERR_INVALID_ARG : MOE_OK;
+}
+inline moe_status opt4(const void* p) { return p ? need4(p) : MOE_OK; }
+
+// Records the stage event when the caller asked for it.
+inline hipError_t stage_mark(const moe_debug* d, int stage, bool start, hipStream_t st) {
+  if (!d) return hipSuccess;
+  void* ev = start ? d->stage_start[stage] : d->stage_stop[stage];
+  return ev ? hipEventRecord(static_cast<hipEvent_t>(ev), st) : hipSuccess;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+}  // namespace
+
+GemmPlan choose_gemm_plan(const moe_shape& s) {
+  GemmPlan p;
+  const long long slots = (long long)s.num_tokens * s.top_k;
+  // rows per expert when the load is even: few rows -> weight streaming tiles
+  const long long avg = slots / (s.num_experts > 0 ? s.num_experts : 1);
+  p.bm_gu = p.bm_dn = avg >= 96 ? 128 : 32;
+  if (s.act_dtype == MOE_F32) p.bm_gu = p.bm_dn = 32;  // the fp32 kernel's tile height
+  return p;
+}
+
+WsLayout plan_workspace(const moe_shape& s) {
+  WsLayout w{};
+  const size_t T = (size_t)s.num_tokens, E = (size_t)s.num_experts, k = (size_t)s.top_k;
+  const size_t H = (size_t)s.hidden, I = (size_t)s.intermediate, Is = (size_t)s.shared_intermediate;
+  const size_t eb = (size_t)elem_bytes(s.act_dtype);
+  const size_t slots = T * k;
+  const GemmPlan gp = choose_gemm_plan(s);
+  w.n_dispatch_tiles = (int)((slots + kDispatchTileSlots - 1) / kDispatchTileSlots);
+  w.max_mtiles_gu = (int)(slots / (size_t)gp.bm_gu + E + 1);
+  w.max_mtiles_dn = (int)(slots / (size_t)gp.bm_dn + E + 1);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at_ = o;
+    o = align_up(o + bytes, 256);
+    return at_;
+  };
+  w.flags = take(256);
+  w.logits = take(T * E * 4);
+  w.ids = take(slots * 4);
+  w.gates = take(slots * 4);
+  w.counts = take(E * 4);
+  w.offsets = take((E + 1) * 4);
+  w.tile_counts = take(((size_t)w.n_dispatch_tiles * E + 4) * 4);  // + capacity word
+  w.row_of_slot = take(slots * 4);
+  w.row_token = take(slots * 4);
+  w.num_dropped = take(16);
+  w.sched_gu = take((size_t)w.max_mtiles_gu * sizeof(MTile));
+  w.sched_dn = take((size_t)w.max_mtiles_dn * sizeof(MTile));
+  w.sched_count = take(16);
+  w.x_perm = take(slots * H * eb);
+  w.h = take(slots * I * eb);
+  w.y = take(slots * H * 4);
+  w.hs = take(T * Is * eb);
+  w.ys = take(Is ? T * H * 4 : 0);
+  w.total = o;
+  return w;
+}
+
+// ---- shared launch sequences --------------------------------------------------
+namespace {
+
+moe_status run_router(const moe_shape& s, const void* x, const void* w_router, const float* bias,
+                      float* logits, hipStream_t st) {
+  const int bm = s.num_tokens >= 128 ? 128 : 32;
+  MOE_HIP(launch_gemm_plain(s.act_dtype, bm, x, s.hidden, w_router, s.num_experts, s.hidden, bias,
+                            logits, s.num_experts, nullptr, nullptr, 0, s.num_tokens, st));
+  return MOE_OK;
+}
+
+moe_status run_ffn(const moe_shape& s, const void* x_perm, const int32_t* offsets,
+                   const void* w_gate, const void* w_up, const void* w_down, float* y, void* ws,
+                   const WsLayout& L, hipStream_t st, const moe_debug* dbg = nullptr) {
+  const GemmPlan gp = choose_gemm_plan(s);
+  const int E = s.num_experts, H = s.hidden, I = s.intermediate;
+  MTile* sg = at<MTile>(ws, L.sched_gu);
+  MTile* sd = at<MTile>(ws, L.sched_dn);
+  int32_t* cnt = at<int32_t>(ws, L.sched_count);
+  const int bm_gu = gp.bm_gu;
+  const int bm_dn = gp.bm_dn;
+  MOE_HIP(launch_build_schedule(offsets, E, bm_gu, sg, cnt, L.max_mtiles_gu, st));
+  if (bm_dn != bm_gu) MOE_HIP(launch_build_schedule(offsets, E, bm_dn, sd, cnt + 1, L.max_mtiles_dn, st));
+  else { sd = sg; }
+  const int32_t* cnt_dn = bm_dn != bm_gu ? cnt + 1 : cnt;
+  void* h = at<void>(ws, L.h);
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_GATE_UP, true, st));
+  MOE_HIP(launch_gemm_gateup(s.act_dtype, bm_gu, x_perm, H, w_gate, w_up, I, H, h, I, sg, cnt,
+                             L.max_mtiles_gu, 0, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_GATE_UP, false, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_DOWN, true, st));
+  MOE_HIP(launch_gemm_plain(s.act_dtype, bm_dn, h, I, w_down, H, I, nullptr, y, H, sd, cnt_dn,
+                            L.max_mtiles_dn, 0, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_DOWN, false, st));
+  return MOE_OK;
+}
+
+moe_status run_shared(const moe_shape& s, const void* x, const void* wsg, const void* wsu,
+                      const void* wsd, void* ws, const WsLayout& L, hipStream_t st) {
+  const int T = s.num_tokens, H = s.hidden, Is = s.shared_intermediate;
+  const int bm = s.act_dtype == MOE_F32 ? 32 : (T >= 128 ? 128 : 32);
+  void* hs = at<void>(ws, L.hs);
+  float* ys = at<float>(ws, L.ys);
+  MOE_HIP(launch_gemm_gateup(s.act_dtype, bm, x, H, wsg, wsu, Is, H, hs, Is, nullptr, nullptr, 0,
+                             T, st));
+  MOE_HIP(launch_gemm_plain(s.act_dtype, bm, hs, Is, wsd, H, Is, nullptr, ys, H, nullptr, nullptr,
+                            0, T, st));
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes) {
+  MOE_TRY(check_shape(shape));
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = plan_workspace(*shape).total;
+  return MOE_OK;
+}
+
+moe_status moe_route_topk(const moe_shape* shape, const void* x, const void* w_router,
+                          const float* router_bias, const float* logits_in, float* logits_out,
+                          const int32_t* k_per_token, int32_t* topk_ids, float* topk_gates,
+                          void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_shape(shape));
+  const moe_shape& s = *shape;
+  if (logits_in) {
+    MOE_TRY(need4(logits_in));
+  } else {
+    MOE_TRY(need(x));
+    MOE_TRY(need(w_router));
+    MOE_TRY(opt4(router_bias));
+  }
+  if (logits_out) MOE_TRY(need(logits_out));
+  MOE_TRY(opt4(k_per_token));
+  MOE_TRY(need4(topk_ids));
+  MOE_TRY(need4(topk_gates));
+  MOE_TRY(need(ws));
+  const WsLayout L = plan_workspace(s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (s.num_tokens == 0) return MOE_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t* flags = at<uint32_t>(ws, L.flags);
+  MOE_HIP(launch_clear_flags(flags, st));
+  const float* logits = logits_in;
+  if (!logits) {
+    float* lo = logits_out ? logits_out : at<float>(ws, L.logits);
+    MOE_TRY(run_router(s, x, w_router, router_bias, lo, st));
+    logits = lo;
+  }
+  MOE_HIP(launch_route_topk(s, logits, k_per_token, topk_ids, topk_gates, flags, st));
+  return MOE_OK;
+}
+
+moe_status moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_ids,
+                        int32_t* expert_counts, int32_t* expert_offsets, int32_t* row_of_slot,
+                        int32_t* row_token, int32_t* num_dropped, void* x_perm, void* ws,
+                        size_t ws_bytes, void* stream) {
+  MOE_TRY(check_shape(shape));
+  const moe_shape& s = *shape;
+  MOE_TRY(need4(topk_ids));
+  MOE_TRY(need4(expert_counts));
+  MOE_TRY(need4(expert_offsets));
+  MOE_TRY(need4(row_of_slot));
+  MOE_TRY(need4(row_token));
+  MOE_TRY(opt4(num_dropped));
+  if ((x == nullptr) != (x_perm == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (x) {
+    MOE_TRY(need(x));
+    MOE_TRY(need(x_perm));
+  }
+  MOE_TRY(need(ws));
+  const WsLayout L = plan_workspace(s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (s.num_tokens == 0) return MOE_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  MOE_HIP(launch_dispatch(s, topk_ids, expert_counts, expert_offsets, row_of_slot, row_token,
+                          num_dropped, at<int32_t>(ws, L.tile_counts), L.n_dispatch_tiles,
+                          at<uint32_t>(ws, L.flags), st));
+  if (x) MOE_HIP(launch_gather(s, x, row_token, expert_offsets, x_perm, st));
+  return MOE_OK;
+}
+
+moe_status moe_grouped_ffn(const moe_shape* shape, const void* x_perm,
+                           const int32_t* expert_offsets, const void* w_gate, const void* w_up,
+                           const void* w_down, float* y_perm, void* ws, size_t ws_bytes,
+                           void* stream) {
+  MOE_TRY(check_shape(shape));
+  const moe_shape& s = *shape;
+  MOE_TRY(need(x_perm));
+  MOE_TRY(need4(expert_offsets));
+  MOE_TRY(need(w_gate));
+  MOE_TRY(need(w_up));
+  MOE_TRY(need(w_down));
+  MOE_TRY(need(y_perm));
+  MOE_TRY(need(ws));
+  const WsLayout L = plan_workspace(s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (s.num_tokens == 0) return MOE_OK;
+  return run_ffn(s, x_perm, expert_offsets, w_gate, w_up, w_down, y_perm, ws, L,
+                 static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_combine(const moe_shape* shape, const float* y_perm, const int32_t* row_of_slot,
+                       const float* topk_gates, const float* y_shared, void* out, void* stream) {
+  MOE_TRY(check_shape(shape));
+  const moe_shape& s = *shape;
+  MOE_TRY(need(y_perm));
+  MOE_TRY(need4(row_of_slot));
+  MOE_TRY(need4(topk_gates));
+  if (y_shared) MOE_TRY(need(y_shared));
+  MOE_TRY(need(out));
+  if (s.num_tokens == 0) return MOE_OK;
+  MOE_HIP(launch_combine(s, y_perm, row_of_slot, topk_gates, y_shared, out,
+                         static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* w_router,
+                             const float* router_bias, const int32_t* k_per_token,
+                             const void* w_gate, const void* w_up, const void* w_down,
+                             const void* ws_gate, const void* ws_up, const void* ws_down,
+                             void* out, const moe_debug* dbg, void* ws, size_t ws_bytes,
+                             void* stream) {
+  MOE_TRY(check_shape(shape));
+  const moe_shape& s = *shape;
+  MOE_TRY(need(x));
+  MOE_TRY(need(w_router));
+  MOE_TRY(opt4(router_bias));
+  MOE_TRY(opt4(k_per_token));
+  MOE_TRY(need(w_gate));
+  MOE_TRY(need(w_up));
+  MOE_TRY(need(w_down));
+  if (s.shared_intermediate > 0) {
+    MOE_TRY(need(ws_gate));
+    MOE_TRY(need(ws_up));
+    MOE_TRY(need(ws_down));
+  }
+  MOE_TRY(need(out));
+  MOE_TRY(need(ws));
+  if (dbg) {
+    if (dbg->logits) MOE_TRY(need(dbg->logits));
+    MOE_TRY(opt4(dbg->topk_ids));
+    MOE_TRY(opt4(dbg->topk_gates));
+    MOE_TRY(opt4(dbg->expert_counts));
+    MOE_TRY(opt4(dbg->expert_offsets));
+    MOE_TRY(opt4(dbg->row_of_slot));
+    MOE_TRY(opt4(dbg->num_dropped));
+  }
+  const WsLayout L = plan_workspace(s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (s.num_tokens == 0) return MOE_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  float* logits = (dbg && dbg->logits) ? dbg->logits : at<float>(ws, L.logits);
+  int32_t* ids = (dbg && dbg->topk_ids) ? dbg->topk_ids : at<int32_t>(ws, L.ids);
+  float* gates = (dbg && dbg->topk_gates) ? dbg->topk_gates : at<float>(ws, L.gates);
+  int32_t* counts = (dbg && dbg->expert_counts) ? dbg->expert_counts : at<int32_t>(ws, L.counts);
+  int32_t* offsets = (dbg && dbg->expert_offsets) ? dbg->expert_offsets : at<int32_t>(ws, L.offsets);
+  int32_t* ros = (dbg && dbg->row_of_slot) ? dbg->row_of_slot : at<int32_t>(ws, L.row_of_slot);
+  int32_t* nd = (dbg && dbg->num_dropped) ? dbg->num_dropped : at<int32_t>(ws, L.num_dropped);
+  uint32_t* flags = at<uint32_t>(ws, L.flags);
+  int32_t* row_token = at<int32_t>(ws, L.row_token);
+  void* x_perm = at<void>(ws, L.x_perm);
+  float* y = at<float>(ws, L.y);
+
+  MOE_HIP(launch_clear_flags(flags, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTER, true, st));
+  MOE_TRY(run_router(s, x, w_router, router_bias, logits, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTER, false, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTE, true, st));
+  MOE_HIP(launch_route_topk(s, logits, k_per_token, ids, gates, flags, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTE, false, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_DISPATCH, true, st));
+  MOE_HIP(launch_dispatch(s, ids, counts, offsets, ros, row_token, nd,
+                          at<int32_t>(ws, L.tile_counts), L.n_dispatch_tiles, flags, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_DISPATCH, false, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_GATHER, true, st));
+  MOE_HIP(launch_gather(s, x, row_token, offsets, x_perm, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_GATHER, false, st));
+  MOE_TRY(run_ffn(s, x_perm, offsets, w_gate, w_up, w_down, y, ws, L, st, dbg));
+  const float* ys = nullptr;
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_SHARED, true, st));
+  if (s.shared_intermediate > 0) {
+    MOE_TRY(run_shared(s, x, ws_gate, ws_up, ws_down, ws, L, st));
+    ys = at<float>(ws, L.ys);
+  }
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_SHARED, false, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_COMBINE, true, st));
+  MOE_HIP(launch_combine(s, y, ros, gates, ys, out, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_COMBINE, false, st));
+  return MOE_OK;
+}
+
+moe_status moe_group_score_sigmoid(const float* x, float* y, int64_t n, void* stream) {
+  if (n < 0) return MOE_ERR_INVALID_ARG;
+  if (n == 0) return MOE_OK;
+  MOE_TRY(need4(x));
+  MOE_TRY(need4(y));
+  MOE_HIP(launch_logistic(x, y, (long long)n, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+const char* moe_status_string(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or option";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+int32_t moe_last_hip_error(void) { return g_last_hip_error; }
+
+moe_status moe_read_device_flags(const void* ws, void* stream, uint32_t* flags) {
+  if (!ws || !flags) return MOE_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the flag word sits at offset 0 of every workspace layout
+  MOE_HIP(hipMemcpyAsync(flags, ws, sizeof(uint32_t), hipMemcpyDeviceToHost, st));
+  MOE_HIP(hipStreamSynchronize(st));
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// Internal declarations of the gfx950 MoE-layer library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_mi355x.h"
+
+namespace moe {
+
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopK = 16;
+constexpr int kDispatchTileSlots = 2048;  // slots per dispatch tile (one block)
+
+// One row-tile of the grouped GEMM: `rows` (1..BM) consecutive permuted rows
+// starting at row0, all belonging to `expert`.
+struct MTile {
+  int expert;
+  int row0;
+  int rows;
+  int pad;
+};
+
+// Byte offsets of every region inside the caller's workspace.
+struct WsLayout {
+  size_t flags, logits, ids, gates, counts, offsets, tile_counts, row_of_slot, row_token,
+      num_dropped, sched_gu, sched_dn, sched_count, x_perm, h, y, hs, ys, total;
+  int n_dispatch_tiles;
+  int max_mtiles_gu, max_mtiles_dn;
+};
+
+// GEMM tile configuration chosen by the host for a shape.
+struct GemmPlan {
+  int bm_gu, bm_dn;  // token rows per tile of the gate/up and down launches
+};
+
+GemmPlan choose_gemm_plan(const moe_shape& s);
+WsLayout plan_workspace(const moe_shape& s);
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---- launchers (each returns the launch status) ----------------------------
+hipError_t launch_clear_flags(uint32_t* flags, hipStream_t st);
+
+hipError_t launch_route_topk(const moe_shape& s, const float* logits, const int32_t* k_per_token,
+                             int32_t* ids, float* gates, uint32_t* flags, hipStream_t st);
+
+hipError_t launch_logistic(const float* x, float* y, long long n, hipStream_t st);
+
+hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, int32_t* counts,
+                           int32_t* offsets, int32_t* row_of_slot, int32_t* row_token,
+                           int32_t* num_dropped, int32_t* tile_counts, int n_tiles,
+                           uint32_t* flags, hipStream_t st);
+
+hipError_t launch_gather(const moe_shape& s, const void* x, const int32_t* row_token,
+                         const int32_t* offsets, void* x_perm, hipStream_t st);
+
+hipError_t launch_build_schedule(const int32_t* offsets, int E, int bm, MTile* sched,
+                                 int32_t* count, int max_tiles, hipStream_t st);
+
+// Grouped GEMMs.  `sched`/`count` give the row tiles; when sched == nullptr
+// the rows [0, static_rows) form one group (expert 0) tiled statically.
+// gate/up + SwiGLU: h[r][n] = silu(A[r].Bg[e][n]) * (A[r].Bu[e][n])
+hipError_t launch_gemm_gateup(int dtype, int bm, const void* A, int lda, const void* Bg,
+                              const void* Bu, int N, int K, void* h, int ldh, const MTile* sched,
+                              const int32_t* count, int max_tiles, int static_rows,
+                              hipStream_t st);
+// plain: Y[r][n] = A[r].B[e][n] (+ bias[n]), fp32 out
+hipError_t launch_gemm_plain(int dtype, int bm, const void* A, int lda, const void* B, int N,
+                             int K, const float* bias, float* Y, int ldy, const MTile* sched,
+                             const int32_t* count, int max_tiles, int static_rows,
+                             hipStream_t st);
+
+hipError_t launch_combine(const moe_shape& s, const float* y_perm, const int32_t* row_of_slot,
+                          const float* gates, const float* y_shared, void* out, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,218 @@
+/*
+ * moe_mi355x.h -- C ABI of the MI355X (gfx950) MoE-layer forward library.
+ *
+ * One GPU's share of an expert-parallel Mixture-of-Experts layer forward:
+ * router scoring and top-k selection, dispatch of token rows into per-expert
+ * contiguous groups, the per-expert SwiGLU FFN as a grouped GEMM, and the
+ * gate-weighted combine back to token order.  On one GPU the dispatch and
+ * combine all-to-alls of expert parallelism become an on-device permutation
+ * and its inverse.
+ *
+ * Problem statement the arguments follow:
+ *   - tokens x hidden in, a router choosing the top-k of E experts per token
+ *     ("Expert parallelism for MoE serving", overview and deep dive;
+ *     "Expert Parallelism: MoE model parallel split", §1);
+ *   - router weights weight the sum of the k expert outputs (same page, §1 and
+ *     §12 Q2);
+ *   - a per-expert capacity with tokens beyond it dropped ("Expert parallelism
+ *     for MoE serving", technical notes and FAQ);
+ *   - k as a per-request runtime control (MoE-Prism summary, §1 and §5);
+ *   - a shared expert ("LLM MoE Expert Parallel production practice", launch
+ *     checklist; "Expert Parallelism: MoE model parallel split", §4);
+ *   - node-limited (group-limited) routing ("Expert parallelism for MoE
+ *     serving", deployment examples).
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers, row-major, owned by the caller and
+ *     aligned to 16 bytes.  The library allocates no memory and keeps no state
+ *     between calls; scratch space is the caller's workspace `ws` of at least
+ *     moe_workspace_size() bytes.  Calls on different streams need distinct
+ *     workspaces.
+ *   - Weights are output-major with K contiguous: router [E][H]; gate and up
+ *     [E][I][H]; down [E][H][I]; shared gate/up [Is][H], shared down [H][Is].
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work; none synchronises with the host (except
+ *     moe_read_device_flags), so calls can be captured in a graph.
+ *   - Host-checkable errors return before anything is enqueued.  A failed
+ *     launch returns MOE_ERR_HIP (the HIP error code is kept per thread, see
+ *     moe_last_hip_error).  Errors found in data on the device (a k_t outside
+ *     [1, k_max], an expert id outside [-1, E)) mark the affected slot unused
+ *     and set bits in a flag word at the head of the workspace.
+ *   - Routing, counts, offsets and the permutation are bitwise deterministic;
+ *     all other outputs are run-to-run deterministic (no atomics in sums).
+ *   - num_tokens == 0 is valid and enqueues nothing.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, inconsistent shape       */
+  MOE_ERR_UNSUPPORTED = -2,  /* valid but outside what the kernels handle         */
+  MOE_ERR_WORKSPACE = -3,    /* ws smaller than moe_workspace_size()              */
+  MOE_ERR_HIP = -4           /* a HIP call or kernel launch failed                */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
+
+/* device flag bits (moe_read_device_flags) */
+#define MOE_FLAG_BAD_K 1u       /* some k_per_token[t] outside [1, top_k]: token routed nowhere */
+#define MOE_FLAG_BAD_EXPERT 2u  /* some topk_ids entry outside [-1, E): slot treated as unused  */
+
+typedef struct {
+  int32_t num_tokens;          /* T >= 0                                                  */
+  int32_t hidden;              /* H; bf16: multiple of 64; fp32: multiple of 4            */
+  int32_t num_experts;         /* E in [1, 512]                                            */
+  int32_t intermediate;        /* I; same rule as H                                        */
+  int32_t top_k;               /* k, or k_max when k_per_token is given; 1..min(E, 16)    */
+  int32_t score;               /* moe_score                                                */
+  int32_t renormalize;         /* 1: gates divided by their sum over the token's slots     */
+  float routed_scale;          /* multiplies routed gates after renormalising (usually 1) */
+  int32_t num_groups;          /* G >= 1 consecutive expert groups; 1 = no group limit     */
+  int32_t topk_groups;         /* groups kept per token, 1..G (ignored when G == 1)        */
+  int32_t group_topn;          /* group score = sum of the group's n best sigmoid scores;
+                                  0 means 1; at most E/G                                   */
+  float capacity_factor;       /* C = ceil(cf * A / E), A = routed slots; <= 0: no limit   */
+  int32_t shared_intermediate; /* Is; 0 = no shared expert; same rule as H                 */
+  int32_t act_dtype;           /* moe_dtype of x and of every weight                        */
+  int32_t out_dtype;           /* moe_dtype of the layer output                             */
+} moe_shape;
+
+/* Stages of moe_layer_forward, for the timing events of moe_debug. */
+typedef enum {
+  MOE_STAGE_ROUTER = 0,   /* S1 router logits                         */
+  MOE_STAGE_ROUTE = 1,    /* S2 scoring, top-k, gates                 */
+  MOE_STAGE_DISPATCH = 2, /* S3-S5 histogram, capacity, permutation   */
+  MOE_STAGE_GATHER = 3,   /* S6 x_perm gather                         */
+  MOE_STAGE_GATE_UP = 4,  /* S7 grouped gate/up GEMM + SwiGLU         */
+  MOE_STAGE_DOWN = 5,     /* S8 grouped down GEMM                     */
+  MOE_STAGE_SHARED = 6,   /* S9 shared expert (both GEMMs)            */
+  MOE_STAGE_COMBINE = 7,  /* S10 combine                              */
+  MOE_NUM_STAGES = 8
+} moe_stage;
+
+/* Optional outputs of moe_layer_forward for inspection and timing.  Each
+ * member may be NULL.  Device buffer sizes: logits T*E, topk_ids/topk_gates/
+ * row_of_slot T*top_k, expert_counts E, expert_offsets E+1, num_dropped 1.
+ * stage_start[i]/stage_stop[i] are hipEvent_t handles recorded on the call's
+ * stream immediately before the first and after the last launch of stage i
+ * (a stage that does not run records both at the same point). */
+typedef struct {
+  float* logits;
+  int32_t* topk_ids;
+  float* topk_gates;
+  int32_t* expert_counts;
+  int32_t* expert_offsets;
+  int32_t* row_of_slot;
+  int32_t* num_dropped;
+  void* stage_start[MOE_NUM_STAGES];
+  void* stage_stop[MOE_NUM_STAGES];
+} moe_debug;
+
+/* Bytes of workspace every call below needs for this shape (host only, no HIP
+ * call).  The same workspace serves all calls. */
+moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes);
+
+/* S1 + S2: router logits and top-k selection.
+ * logits[t][e] = sum_h x[t][h] * w_router[e][h] + router_bias[e], fp32 accumulate.
+ * If logits_in is non-NULL it is used instead and x/w_router/router_bias are
+ * ignored (may be NULL).  logits_out (nullable) receives the computed logits.
+ * Per token t with k_t = k_per_token ? k_per_token[t] : top_k:
+ *   eligible experts: all, or with num_groups > 1 those in the topk_groups
+ *   groups of E/G consecutive experts with the largest group score;
+ *   selection: the k_t eligible experts with the largest logits, equal logits
+ *   going to the lower expert index, written to slots 0..k_t-1 in that order;
+ *   gates: softmax over all E logits (or sigmoid of the logit), divided by
+ *   their sum over the k_t slots when renormalize, times routed_scale.
+ * Outputs topk_ids [T][top_k] int32 (-1 in unused slots) and topk_gates
+ * [T][top_k] fp32 (0 in unused slots).  Clears the workspace flag word. */
+moe_status moe_route_topk(const moe_shape* shape, const void* x, const void* w_router,
+                          const float* router_bias, const float* logits_in, float* logits_out,
+                          const int32_t* k_per_token, int32_t* topk_ids, float* topk_gates,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* S3-S6: dispatch ("Expert Parallelism: MoE model parallel split" §3 and §12
+ * Q2; token sorting §7; capacity from "Expert parallelism for MoE serving").
+ * Slots s = t*top_k + j are visited in token-major order.
+ *   expert_counts[e]  = routed slots with id e                         [E]
+ *   C                 = ceil(capacity_factor * A / E) in fp64 (A = sum of counts),
+ *                       unlimited when capacity_factor <= 0
+ *   expert_offsets    = exclusive prefix sum of min(count, C)          [E+1]
+ *   row_of_slot[s]    = expert_offsets[e] + (rank of s among slots of e), or -1
+ *                       when the slot is unused or its rank >= C       [T][top_k]
+ *   row_token[row]    = t for every kept row (rows >= R left untouched) [T*top_k]
+ *   num_dropped       = A - R, R = expert_offsets[E]                   [1]
+ *   x_perm[row]       = x[row_token[row]] (skipped when x or x_perm is NULL)
+ * Adds MOE_FLAG_BAD_EXPERT to the flag word for ids outside [-1, E). */
+moe_status moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_ids,
+                        int32_t* expert_counts, int32_t* expert_offsets, int32_t* row_of_slot,
+                        int32_t* row_token, int32_t* num_dropped, void* x_perm, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* S7-S8: grouped SwiGLU FFN over permuted rows ("LLM MoE Expert Parallel
+ * production practice", four-step layer: local expert compute).
+ * For every expert e and row r in [expert_offsets[e], expert_offsets[e+1]):
+ *   h = silu(x_perm[r] . w_gate[e]^T) * (x_perm[r] . w_up[e]^T)   (h rounded to
+ *       act_dtype), silu(z) = z / (1 + exp(-z))
+ *   y_perm[r] = h . w_down[e]^T                                    (fp32)
+ * Rows at or beyond expert_offsets[E] are not written.  x_perm [T*top_k][H],
+ * y_perm [T*top_k][H] fp32. */
+moe_status moe_grouped_ffn(const moe_shape* shape, const void* x_perm,
+                           const int32_t* expert_offsets, const void* w_gate, const void* w_up,
+                           const void* w_down, float* y_perm, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* S10: combine ("Expert Parallelism: MoE model parallel split" §1 weighted
+ * sum, §12 Q2 combine).  out[t] = sum over j ascending with
+ * row_of_slot[t][j] >= 0 of topk_gates[t][j] * y_perm[row_of_slot[t][j]],
+ * plus y_shared[t] when y_shared is non-NULL; fp32 arithmetic, out in
+ * out_dtype. */
+moe_status moe_combine(const moe_shape* shape, const float* y_perm, const int32_t* row_of_slot,
+                       const float* topk_gates, const float* y_shared, void* out, void* stream);
+
+/* The whole layer: S1-S10 in one call (may fuse steps internally).
+ * out[t] = sum over kept slots of gate * FFN_e(x[t]) + FFN_shared(x[t]).
+ * The shared expert runs when shape->shared_intermediate > 0 (then ws_gate,
+ * ws_up and ws_down are required).  dbg (nullable) receives intermediates. */
+moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* w_router,
+                             const float* router_bias, const int32_t* k_per_token,
+                             const void* w_gate, const void* w_up, const void* w_down,
+                             const void* ws_gate, const void* ws_up, const void* ws_down,
+                             void* out, const moe_debug* dbg, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* The fp32 logistic function that group-limited routing sums into group
+ * scores, evaluated elementwise: y[i] = sigma(x[i]) for i < n (device
+ * arrays).  Node-limited routing ("Expert parallelism for MoE serving",
+ * deployment examples) ranks groups by these sums, so the selected groups
+ * depend on every bit of them; this entry point lets a checker compare those
+ * bits with an independent implementation of the same operation sequence:
+ * clamp to [-30, 30]; n = rint(-x * fp32(log2 e)); r = fma(-n, ln2_hi, -x),
+ * r = fma(-n, ln2_lo, r) with ln2_hi = ln 2 to 17 significant bits and
+ * ln2_lo = fp32(ln 2 - ln2_hi); p = degree-7 Taylor polynomial of e^r with
+ * coefficients fp32(1/i!) in Horner form with fma; e = ldexp(p, n);
+ * sigma = 1 / (1 + e); IEEE fp32 operations rounded to nearest even. */
+moe_status moe_group_score_sigmoid(const float* x, float* y, int64_t n, void* stream);
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status status);
+
+/* hipError_t of the last failed HIP call on this thread (0 if none). */
+int32_t moe_last_hip_error(void);
+
+/* Copies the workspace flag word to *flags and waits for it (synchronises the
+ * stream).  For tests and diagnostics. */
+moe_status moe_read_device_flags(const void* ws, void* stream, uint32_t* flags);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

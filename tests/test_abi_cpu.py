@@ -1,0 +1,134 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, and rejects bad arguments on the host before enqueuing anything.
+
+No test here launches a kernel: every call either fails validation or has
+num_tokens == 0, and the pointers passed are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from expert_serving_amd import abi
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+FAKE = 0x10000          # aligned, never dereferenced
+FAKE_ODD = 0x10004      # 4-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:moe_status|const char\*|int32_t)\s+(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    L = abi.lib()
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(abi.EXPORTED)
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4):
+        assert abi.moe_status_string(s)
+    assert abi.moe_last_hip_error() == 0
+
+
+def base_shape(**kw):
+    return abi.make_shape(W.CONFIGS["mixtral_prefill"], **kw)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(num_tokens=-1), abi.MOE_ERR_INVALID_ARG),
+    (dict(hidden=0), abi.MOE_ERR_INVALID_ARG),
+    (dict(num_experts=0), abi.MOE_ERR_INVALID_ARG),
+    (dict(num_experts=513, top_k=2), abi.MOE_ERR_UNSUPPORTED),
+    (dict(top_k=0), abi.MOE_ERR_INVALID_ARG),
+    (dict(top_k=9), abi.MOE_ERR_INVALID_ARG),              # k > E
+    (dict(num_experts=64, top_k=17), abi.MOE_ERR_UNSUPPORTED),
+    (dict(score=2), abi.MOE_ERR_INVALID_ARG),
+    (dict(renormalize=2), abi.MOE_ERR_INVALID_ARG),
+    (dict(routed_scale=float("nan")), abi.MOE_ERR_INVALID_ARG),
+    (dict(capacity_factor=float("inf")), abi.MOE_ERR_INVALID_ARG),
+    (dict(act_dtype=7), abi.MOE_ERR_INVALID_ARG),
+    (dict(out_dtype=7), abi.MOE_ERR_INVALID_ARG),
+    (dict(hidden=4000), abi.MOE_ERR_UNSUPPORTED),           # bf16 needs multiples of 64
+    (dict(intermediate=100), abi.MOE_ERR_UNSUPPORTED),
+    (dict(shared_intermediate=-1), abi.MOE_ERR_INVALID_ARG),
+    (dict(shared_intermediate=96), abi.MOE_ERR_UNSUPPORTED),
+    (dict(num_groups=3), abi.MOE_ERR_INVALID_ARG),          # 8 % 3 != 0
+    (dict(num_groups=4, topk_groups=0), abi.MOE_ERR_INVALID_ARG),
+    (dict(num_groups=4, topk_groups=5), abi.MOE_ERR_INVALID_ARG),
+    (dict(num_groups=4, topk_groups=1, group_topn=3), abi.MOE_ERR_INVALID_ARG),  # > E/G
+    (dict(num_groups=8, topk_groups=1, top_k=2), abi.MOE_ERR_INVALID_ARG),      # 1 group of 1 < k
+    (dict(act_dtype=abi.MOE_F32, hidden=4098), abi.MOE_ERR_UNSUPPORTED),
+])
+def test_shape_validation(bad, status):
+    s = base_shape(**bad)
+    n = ctypes.c_size_t(0)
+    assert abi.lib().moe_workspace_size(ctypes.byref(s), ctypes.byref(n)) == status
+
+
+def test_workspace_size_grows_with_tokens():
+    a = abi.moe_workspace_size(base_shape(num_tokens=64))
+    b = abi.moe_workspace_size(base_shape(num_tokens=4096))
+    assert 0 < a < b
+    # x_perm, h and y of T*k rows dominate
+    s = W.CONFIGS["mixtral_prefill"]
+    assert b >= s.tokens * s.top_k * (s.hidden * 2 + s.inter * 2 + s.hidden * 4)
+
+
+def test_null_and_misaligned_pointers_rejected_before_launch():
+    L = abi.lib()
+    s = base_shape(num_tokens=16)
+    ws = abi.moe_workspace_size(s)
+    ref = ctypes.byref(s)
+    # route: missing outputs, misaligned x, no workspace
+    assert L.moe_route_topk(ref, FAKE, FAKE, None, None, None, None, None, FAKE, FAKE, ws, None) == -1
+    assert L.moe_route_topk(ref, FAKE_ODD, FAKE, None, None, None, None, FAKE, FAKE, FAKE, ws, None) == -1
+    assert L.moe_route_topk(ref, FAKE, FAKE, None, None, None, None, FAKE, FAKE, None, ws, None) == -1
+    assert L.moe_route_topk(ref, FAKE, FAKE, None, None, None, None, FAKE, FAKE, FAKE, ws - 1, None) == -3
+    # dispatch: x without x_perm
+    assert L.moe_dispatch(ref, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, ws, None) == -1
+    assert L.moe_dispatch(ref, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, ws // 2, None) == -3
+    # grouped ffn / combine / layer: missing weights or output
+    assert L.moe_grouped_ffn(ref, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, ws, None) == -1
+    assert L.moe_combine(ref, FAKE, FAKE, FAKE, None, None, None) == -1
+    assert L.moe_combine(ref, FAKE_ODD, FAKE, FAKE, None, FAKE, None) == -1
+    args = [ref, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, None, None, FAKE, None, FAKE, ws, None]
+    assert L.moe_layer_forward(*args[:4], *args[4:11], None, *args[12:]) == -1     # out missing
+    args_ws = list(args)
+    args_ws[14] = ws - 256
+    assert L.moe_layer_forward(*args_ws) == -3
+    # shared expert requested but its weights missing
+    s2 = abi.make_shape(W.CONFIGS["deepseek_v3"], num_tokens=16)
+    ws2 = abi.moe_workspace_size(s2)
+    assert L.moe_layer_forward(ctypes.byref(s2), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, None, None,
+                               FAKE, None, FAKE, ws2, None) == -1
+    assert L.moe_group_score_sigmoid(FAKE, FAKE, -1, None) == -1
+    assert L.moe_read_device_flags(None, None, None) == -1
+
+
+def test_zero_tokens_is_a_no_op():
+    L = abi.lib()
+    s = base_shape(num_tokens=0)
+    ws = abi.moe_workspace_size(s)
+    ref = ctypes.byref(s)
+    assert L.moe_route_topk(ref, FAKE, FAKE, None, None, None, None, FAKE, FAKE, FAKE, ws, None) == 0
+    assert L.moe_dispatch(ref, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, ws, None) == 0
+    assert L.moe_grouped_ffn(ref, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == 0
+    assert L.moe_combine(ref, FAKE, FAKE, FAKE, None, FAKE, None) == 0
+    assert L.moe_layer_forward(ref, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, None, None, FAKE, None,
+                               FAKE, ws, None) == 0
+    assert L.moe_group_score_sigmoid(FAKE, FAKE, 0, None) == 0
+
+
+def test_binding_raises_on_error():
+    with pytest.raises(abi.MoeError):
+        abi.moe_workspace_size(base_shape(top_k=0))
