@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
-MOE_FLAG_BAD_K, MOE_FLAG_BAD_EXPERT = 1, 2
+MOE_FLAG_BAD_K, MOE_FLAG_BAD_EXPERT, MOE_FLAG_H_RANGE = 1, 2, 4
 
 EXPORTED = ("moe_workspace_size", "moe_route_topk", "moe_dispatch", "moe_grouped_ffn", "moe_combine",
             "moe_layer_forward", "moe_group_score_sigmoid", "moe_status_string", "moe_last_hip_error",

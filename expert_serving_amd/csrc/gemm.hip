@@ -28,6 +28,7 @@ namespace moe {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -58,12 +59,48 @@ __device__ __forceinline__ bool block_tile(int mslots, int ntiles, int& m, int& 
   return m < mslots && n < ntiles;
 }
 
-template <int BM, int BN, bool DUAL, bool OUT_F32>
-__global__ __launch_bounds__(kThreads, 2) void k_gemm_bf16(
+// Kernel modes.
+//   kGateUp: A = bf16 token rows, B0/B1 = bf16 gate/up weights;
+//            out h (fp16) = silu(A.B0^T) * (A.B1^T)
+//   kDown:   A = fp16 h rows, B0 = bf16 down weights converted to fp16 while
+//            staged into LDS (exact for |w| in fp16's normal range);
+//            out y (fp32) = A.B0^T
+//   kPlain:  A = bf16 rows, B0 = bf16 weights; out fp32 = A.B0^T + bias
+enum GemmMode { kGateUp = 0, kDown = 1, kPlain = 2 };
+
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  const float lo = __uint_as_float(w << 16);
+  const float hi = __uint_as_float(w & 0xFFFF0000u);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
+  return u32x4{bf16x2_to_f16x2(v[0]), bf16x2_to_f16x2(v[1]), bf16x2_to_f16x2(v[2]),
+               bf16x2_to_f16x2(v[3])};
+}
+
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+template <int MODE>
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (MODE == kDown)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <int BM, int BN, int MODE>
+__global__ __launch_bounds__(kThreads, 2) void k_gemm_mfma(
     const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, long long strideB, int N, int K, void* __restrict__ Out,
     int ldo, const float* __restrict__ bias, const MTile* __restrict__ sched,
-    const int32_t* __restrict__ count, int mslots, int ntiles, int static_rows) {
+    const int32_t* __restrict__ count, int mslots, int ntiles, int static_rows,
+    uint32_t* __restrict__ flags) {
+  constexpr bool DUAL = MODE == kGateUp;
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int FM = WM / 16, FN = WN / 16;
   constexpr int A_LD = BM * 8 / kThreads;  // 16-byte chunks per thread
@@ -144,7 +181,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_bf16(
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
       const int r = lr + 32 * i;
-      *reinterpret_cast<u32x4*>(sB0 + r * kBK + ((lc ^ (r & 7)) << 3)) = rb0[i];
+      const u32x4 v = MODE == kDown ? bf16x8_to_f16x8(rb0[i]) : rb0[i];
+      *reinterpret_cast<u32x4*>(sB0 + r * kBK + ((lc ^ (r & 7)) << 3)) = v;
       if constexpr (DUAL) *reinterpret_cast<u32x4*>(sB1 + r * kBK + ((lc ^ (r & 7)) << 3)) = rb1[i];
     }
     __syncthreads();
@@ -152,26 +190,25 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_bf16(
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int c = kk * 4 + fk;
-      bf16x8 xa[FM], wb0[FN], wb1[DUAL ? FN : 1];
+      u32x4 xa[FM], wb0[FN], wb1[DUAL ? FN : 1];
 #pragma unroll
       for (int b = 0; b < FM; ++b) {
         const int r = wm * WM + b * 16 + fr;
-        xa[b] = *reinterpret_cast<const bf16x8*>(sA + r * kBK + ((c ^ (r & 7)) << 3));
+        xa[b] = *reinterpret_cast<const u32x4*>(sA + r * kBK + ((c ^ (r & 7)) << 3));
       }
 #pragma unroll
       for (int a = 0; a < FN; ++a) {
         const int r = wn * WN + a * 16 + fr;
-        wb0[a] = *reinterpret_cast<const bf16x8*>(sB0 + r * kBK + ((c ^ (r & 7)) << 3));
+        wb0[a] = *reinterpret_cast<const u32x4*>(sB0 + r * kBK + ((c ^ (r & 7)) << 3));
         if constexpr (DUAL)
-          wb1[a] = *reinterpret_cast<const bf16x8*>(sB1 + r * kBK + ((c ^ (r & 7)) << 3));
+          wb1[a] = *reinterpret_cast<const u32x4*>(sB1 + r * kBK + ((c ^ (r & 7)) << 3));
       }
 #pragma unroll
       for (int a = 0; a < FN; ++a)
 #pragma unroll
         for (int b = 0; b < FM; ++b) {
-          acc0[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb0[a], xa[b], acc0[a][b], 0, 0, 0);
-          if constexpr (DUAL)
-            acc1[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb1[a], xa[b], acc1[a][b], 0, 0, 0);
+          acc0[a][b] = mfma16<MODE>(wb0[a], xa[b], acc0[a][b]);
+          if constexpr (DUAL) acc1[a][b] = mfma16<MODE>(wb1[a], xa[b], acc1[a][b]);
         }
     }
     __syncthreads();
@@ -179,6 +216,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_bf16(
 #undef MOE_GLOAD
 
   // epilogue: lane holds output columns n..n+3 of token row m
+  bool overflow = false;
 #pragma unroll
   for (int a = 0; a < FN; ++a) {
     const int n = n0 + wn * WN + a * 16 + fk * 4;
@@ -190,13 +228,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_bf16(
       if constexpr (DUAL) {
         if (n + 3 < N) {
           const f32x4 g = acc0[a][b], u = acc1[a][b];
-          const uint32_t h0 = f32_to_bf16_rne(silu_mul(g[0], u[0]));
-          const uint32_t h1 = f32_to_bf16_rne(silu_mul(g[1], u[1]));
-          const uint32_t h2 = f32_to_bf16_rne(silu_mul(g[2], u[2]));
-          const uint32_t h3 = f32_to_bf16_rne(silu_mul(g[3], u[3]));
+          const float h0 = silu_mul(g[0], u[0]), h1 = silu_mul(g[1], u[1]);
+          const float h2 = silu_mul(g[2], u[2]), h3 = silu_mul(g[3], u[3]);
+          overflow |= !(fabsf(h0) <= 65504.f && fabsf(h1) <= 65504.f && fabsf(h2) <= 65504.f &&
+                        fabsf(h3) <= 65504.f);
           u32x2 pk;
-          pk[0] = h0 | (h1 << 16);
-          pk[1] = h2 | (h3 << 16);
+          pk[0] = f32_to_f16_bits(h0) | (f32_to_f16_bits(h1) << 16);
+          pk[1] = f32_to_f16_bits(h2) | (f32_to_f16_bits(h3) << 16);
           *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Out) + o) = pk;
         }
       } else {
@@ -217,6 +255,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_bf16(
         }
       }
     }
+  }
+  if constexpr (DUAL) {
+    if (overflow && flags) atomicOr(flags, (uint32_t)MOE_FLAG_H_RANGE);
   }
 }
 
@@ -303,7 +344,7 @@ inline int grid_for(int mslots, int ntiles) {
 hipError_t launch_gemm_gateup(int dtype, int bm, const void* A, int lda, const void* Bg,
                               const void* Bu, int N, int K, void* h, int ldh, const MTile* sched,
                               const int32_t* count, int max_tiles, int static_rows,
-                              hipStream_t st) {
+                              uint32_t* flags, hipStream_t st) {
   const long long strideB = (long long)N * K;
   if (dtype == MOE_F32) {
     const int mslots = sched ? max_tiles : (static_rows + 31) / 32;
@@ -321,20 +362,20 @@ hipError_t launch_gemm_gateup(int dtype, int bm, const void* A, int lda, const v
   if (mslots == 0) return hipSuccess;
   const dim3 grid(grid_for(mslots, ntiles));
 #define MOE_GU(BM)                                                                               \
-  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, true, false>), grid, dim3(kThreads), 0, st,           \
+  hipLaunchKernelGGL((k_gemm_mfma<BM, BN, kGateUp>), grid, dim3(kThreads), 0, st,               \
                      static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(Bg),     \
                      static_cast<const uint16_t*>(Bu), strideB, N, K, h, ldh, nullptr, sched,    \
-                     count, mslots, ntiles, static_rows)
+                     count, mslots, ntiles, static_rows, flags)
   if (bm == 128) MOE_GU(128);
   else MOE_GU(32);
 #undef MOE_GU
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_plain(int dtype, int bm, const void* A, int lda, const void* B, int N,
-                             int K, const float* bias, float* Y, int ldy, const MTile* sched,
-                             const int32_t* count, int max_tiles, int static_rows,
-                             hipStream_t st) {
+hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int lda,
+                             const void* B, int N, int K, const float* bias, float* Y, int ldy,
+                             const MTile* sched, const int32_t* count, int max_tiles,
+                             int static_rows, hipStream_t st) {
   const long long strideB = (long long)N * K;
   if (dtype == MOE_F32) {
     const int mslots = sched ? max_tiles : (static_rows + 31) / 32;
@@ -350,13 +391,18 @@ hipError_t launch_gemm_plain(int dtype, int bm, const void* A, int lda, const vo
   const int mslots = sched ? max_tiles : (static_rows + bm - 1) / bm;
   if (mslots == 0) return hipSuccess;
   const dim3 grid(grid_for(mslots, ntiles));
-#define MOE_PL(BM)                                                                               \
-  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, false, true>), grid, dim3(kThreads), 0, st,           \
+#define MOE_PL(BM, MODE)                                                                         \
+  hipLaunchKernelGGL((k_gemm_mfma<BM, BN, MODE>), grid, dim3(kThreads), 0, st,                  \
                      static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B),      \
                      nullptr, strideB, N, K, Y, ldy, bias, sched, count, mslots, ntiles,         \
-                     static_rows)
-  if (bm == 128) MOE_PL(128);
-  else MOE_PL(32);
+                     static_rows, nullptr)
+  if (a_is_h) {
+    if (bm == 128) MOE_PL(128, kDown);
+    else MOE_PL(32, kDown);
+  } else {
+    if (bm == 128) MOE_PL(128, kPlain);
+    else MOE_PL(32, kPlain);
+  }
 #undef MOE_PL
   return hipGetLastError();
 }

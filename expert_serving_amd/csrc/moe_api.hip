@@ -144,8 +144,8 @@ namespace {
 moe_status run_router(const moe_shape& s, const void* x, const void* w_router, const float* bias,
                       float* logits, hipStream_t st) {
   const int bm = s.num_tokens >= 128 ? 128 : 32;
-  MOE_HIP(launch_gemm_plain(s.act_dtype, bm, x, s.hidden, w_router, s.num_experts, s.hidden, bias,
-                            logits, s.num_experts, nullptr, nullptr, 0, s.num_tokens, st));
+  MOE_HIP(launch_gemm_plain(s.act_dtype, bm, false, x, s.hidden, w_router, s.num_experts, s.hidden,
+                            bias, logits, s.num_experts, nullptr, nullptr, 0, s.num_tokens, st));
   return MOE_OK;
 }
 
@@ -166,10 +166,10 @@ moe_status run_ffn(const moe_shape& s, const void* x_perm, const int32_t* offset
   void* h = at<void>(ws, L.h);
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATE_UP, true, st));
   MOE_HIP(launch_gemm_gateup(s.act_dtype, bm_gu, x_perm, H, w_gate, w_up, I, H, h, I, sg, cnt,
-                             L.max_mtiles_gu, 0, st));
+                             L.max_mtiles_gu, 0, at<uint32_t>(ws, L.flags), st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATE_UP, false, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_DOWN, true, st));
-  MOE_HIP(launch_gemm_plain(s.act_dtype, bm_dn, h, I, w_down, H, I, nullptr, y, H, sd, cnt_dn,
+  MOE_HIP(launch_gemm_plain(s.act_dtype, bm_dn, true, h, I, w_down, H, I, nullptr, y, H, sd, cnt_dn,
                             L.max_mtiles_dn, 0, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_DOWN, false, st));
   return MOE_OK;
@@ -182,9 +182,9 @@ moe_status run_shared(const moe_shape& s, const void* x, const void* wsg, const 
   void* hs = at<void>(ws, L.hs);
   float* ys = at<float>(ws, L.ys);
   MOE_HIP(launch_gemm_gateup(s.act_dtype, bm, x, H, wsg, wsu, Is, H, hs, Is, nullptr, nullptr, 0,
-                             T, st));
-  MOE_HIP(launch_gemm_plain(s.act_dtype, bm, hs, Is, wsd, H, Is, nullptr, ys, H, nullptr, nullptr,
-                            0, T, st));
+                             T, at<uint32_t>(ws, L.flags), st));
+  MOE_HIP(launch_gemm_plain(s.act_dtype, bm, true, hs, Is, wsd, H, Is, nullptr, ys, H, nullptr,
+                            nullptr, 0, T, st));
   return MOE_OK;
 }
 
@@ -258,6 +258,7 @@ moe_status moe_dispatch(const moe_shape* shape, const void* x, const int32_t* to
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (s.num_tokens == 0) return MOE_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  MOE_HIP(launch_clear_flags(at<uint32_t>(ws, L.flags), st));
   MOE_HIP(launch_dispatch(s, topk_ids, expert_counts, expert_offsets, row_of_slot, row_token,
                           num_dropped, at<int32_t>(ws, L.tile_counts), L.n_dispatch_tiles,
                           at<uint32_t>(ws, L.flags), st));
@@ -281,8 +282,9 @@ moe_status moe_grouped_ffn(const moe_shape* shape, const void* x_perm,
   const WsLayout L = plan_workspace(s);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (s.num_tokens == 0) return MOE_OK;
-  return run_ffn(s, x_perm, expert_offsets, w_gate, w_up, w_down, y_perm, ws, L,
-                 static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  MOE_HIP(launch_clear_flags(at<uint32_t>(ws, L.flags), st));
+  return run_ffn(s, x_perm, expert_offsets, w_gate, w_up, w_down, y_perm, ws, L, st);
 }
 
 moe_status moe_combine(const moe_shape* shape, const float* y_perm, const int32_t* row_of_slot,

@@ -61,16 +61,18 @@ hipError_t launch_build_schedule(const int32_t* offsets, int E, int bm, MTile* s
 
 // Grouped GEMMs.  `sched`/`count` give the row tiles; when sched == nullptr
 // the rows [0, static_rows) form one group (expert 0) tiled statically.
-// gate/up + SwiGLU: h[r][n] = silu(A[r].Bg[e][n]) * (A[r].Bu[e][n])
+// gate/up + SwiGLU: h[r][n] = silu(A[r].Bg[e][n]) * (A[r].Bu[e][n]); for bf16
+// layers h is fp16 and values outside fp16's range set MOE_FLAG_H_RANGE
 hipError_t launch_gemm_gateup(int dtype, int bm, const void* A, int lda, const void* Bg,
                               const void* Bu, int N, int K, void* h, int ldh, const MTile* sched,
                               const int32_t* count, int max_tiles, int static_rows,
-                              hipStream_t st);
-// plain: Y[r][n] = A[r].B[e][n] (+ bias[n]), fp32 out
-hipError_t launch_gemm_plain(int dtype, int bm, const void* A, int lda, const void* B, int N,
-                             int K, const float* bias, float* Y, int ldy, const MTile* sched,
-                             const int32_t* count, int max_tiles, int static_rows,
-                             hipStream_t st);
+                              uint32_t* flags, hipStream_t st);
+// plain: Y[r][n] = A[r].B[e][n] (+ bias[n]), fp32 out.  a_is_h: A is the
+// fp16 h of a bf16 layer (down projection), B is converted to fp16 on load.
+hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int lda,
+                             const void* B, int N, int K, const float* bias, float* Y, int ldy,
+                             const MTile* sched, const int32_t* count, int max_tiles,
+                             int static_rows, hipStream_t st);
 
 hipError_t launch_combine(const moe_shape& s, const float* y_perm, const int32_t* row_of_slot,
                           const float* gates, const float* y_shared, void* out, hipStream_t st);

@@ -33,7 +33,9 @@
  *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
  *     enqueues work; none synchronises with the host (except
  *     moe_read_device_flags), so calls can be captured in a graph.
- *   - Host-checkable errors return before anything is enqueued.  A failed
+ *   - Host-checkable errors return before anything is enqueued.
+ *   - Every call that takes a workspace clears its flag word at the start;
+ *     the word reports that call only.  A failed
  *     launch returns MOE_ERR_HIP (the HIP error code is kept per thread, see
  *     moe_last_hip_error).  Errors found in data on the device (a k_t outside
  *     [1, k_max], an expert id outside [-1, E)) mark the affected slot unused
@@ -66,6 +68,7 @@ typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
 /* device flag bits (moe_read_device_flags) */
 #define MOE_FLAG_BAD_K 1u       /* some k_per_token[t] outside [1, top_k]: token routed nowhere */
 #define MOE_FLAG_BAD_EXPERT 2u  /* some topk_ids entry outside [-1, E): slot treated as unused  */
+#define MOE_FLAG_H_RANGE 4u     /* some SwiGLU activation h exceeded fp16 range (bf16 layers)   */
 
 typedef struct {
   int32_t num_tokens;          /* T >= 0                                                  */
@@ -151,7 +154,8 @@ moe_status moe_route_topk(const moe_shape* shape, const void* x, const void* w_r
  *   row_token[row]    = t for every kept row (rows >= R left untouched) [T*top_k]
  *   num_dropped       = A - R, R = expert_offsets[E]                   [1]
  *   x_perm[row]       = x[row_token[row]] (skipped when x or x_perm is NULL)
- * Adds MOE_FLAG_BAD_EXPERT to the flag word for ids outside [-1, E). */
+ * Clears the workspace flag word, then sets MOE_FLAG_BAD_EXPERT in it for ids
+ * outside [-1, E).  expert_offsets[E] <= T*top_k always holds on return. */
 moe_status moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_ids,
                         int32_t* expert_counts, int32_t* expert_offsets, int32_t* row_of_slot,
                         int32_t* row_token, int32_t* num_dropped, void* x_perm, void* ws,
@@ -160,11 +164,17 @@ moe_status moe_dispatch(const moe_shape* shape, const void* x, const int32_t* to
 /* S7-S8: grouped SwiGLU FFN over permuted rows ("LLM MoE Expert Parallel
  * production practice", four-step layer: local expert compute).
  * For every expert e and row r in [expert_offsets[e], expert_offsets[e+1]):
- *   h = silu(x_perm[r] . w_gate[e]^T) * (x_perm[r] . w_up[e]^T)   (h rounded to
- *       act_dtype), silu(z) = z / (1 + exp(-z))
+ *   h = silu(x_perm[r] . w_gate[e]^T) * (x_perm[r] . w_up[e]^T),
+ *       silu(z) = z / (1 + exp(-z)); fp32 accumulation; h is kept in fp32
+ *       for fp32 layers and rounded to fp16 (11-bit significand) for bf16
+ *       layers, whose down projection then runs on fp16 inputs (w_down
+ *       converted from bf16, exact for |w| >= 2^-14); |h| > 65504 sets
+ *       MOE_FLAG_H_RANGE
  *   y_perm[r] = h . w_down[e]^T                                    (fp32)
  * Rows at or beyond expert_offsets[E] are not written.  x_perm [T*top_k][H],
- * y_perm [T*top_k][H] fp32. */
+ * y_perm [T*top_k][H] fp32.  expert_offsets must be non-decreasing with
+ * expert_offsets[0] = 0 and expert_offsets[E] <= T*top_k (as moe_dispatch
+ * writes them); the kernels trust them. */
 moe_status moe_grouped_ffn(const moe_shape* shape, const void* x_perm,
                            const int32_t* expert_offsets, const void* w_gate, const void* w_up,
                            const void* w_down, float* y_perm, void* ws, size_t ws_bytes,

@@ -1,7 +1,7 @@
 """GPU parity of the grouped SwiGLU FFN (S7-S8) and the combine (S10) through
 the C ABI against the CPU oracle.
 
-Tolerances: bf16 inputs with fp32 accumulation, h rounded to bf16:
+Tolerances: bf16 inputs with fp32 accumulation, h rounded to fp16:
 max|err| <= 2e-2 * RMS(reference); fp32 layers: 1e-4 * RMS; combine (fp32
 arithmetic on fp32 inputs): 1e-5 * RMS.
 """
