@@ -105,6 +105,9 @@ def main():
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 1 GiB device-to-device copy first (a kernel of known HBM traffic "
+                         "for scaling profiler byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU: the layer share it measures is "
@@ -119,6 +122,12 @@ def main():
 
     cfg = W.CONFIGS[args.workload]
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     inp = W.make_layer_inputs(cfg, dev)
     shape = abi.make_shape(cfg)
     ws = torch.empty(abi.moe_workspace_size(shape), dtype=torch.uint8, device=dev)

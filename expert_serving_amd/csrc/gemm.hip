@@ -30,10 +30,10 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBK = 64;
 constexpr int kGroupM = 8;
 constexpr int kThreads = 256;
 
@@ -46,17 +46,29 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;
 }
 
-// Logical tile of this block.  Returns false when the block has no tile.
-__device__ __forceinline__ bool block_tile(int mslots, int ntiles, int& m, int& n) {
+// Logical tile of this block.  Blocks are dealt round-robin to the 8 XCDs
+// (block b runs on XCD b % 8), so block b takes logical tile
+// (b % 8) * per_xcd + b / 8: each XCD gets a contiguous range of the `real`
+// tiles that exist (row tiles known on the device x column tiles), and the
+// padding blocks of the launch (grid sized for the worst case) exit.  Logical
+// tiles sweep groups of kGroupM row tiles across all column tiles, so the
+// blocks an XCD runs together share both token rows and weight rows in L2.
+__device__ __forceinline__ bool block_tile(int mtiles, int ntiles, int& m, int& n) {
   const int b = blockIdx.x;
-  const int per_xcd = gridDim.x >> 3;  // gridDim.x is a multiple of 8
-  const int L = (b & 7) * per_xcd + (b >> 3);
+  const int real = mtiles * ntiles;
+  const int per_xcd = (real + 7) >> 3;
+  const int slot = b >> 3;
+  if (slot >= per_xcd) return false;
+  const int L = (b & 7) * per_xcd + slot;
+  if (L >= real) return false;
+  const int groups_full = mtiles / kGroupM;
   const int per_group = kGroupM * ntiles;
   const int g = L / per_group;
+  const int gm = g < groups_full ? kGroupM : mtiles - groups_full * kGroupM;  // last group may be short
   const int r = L - g * per_group;
-  n = r / kGroupM;
-  m = g * kGroupM + (r - n * kGroupM);
-  return m < mslots && n < ntiles;
+  n = r / gm;
+  m = g * kGroupM + (r - n * gm);
+  return true;
 }
 
 // Kernel modes.
@@ -84,174 +96,268 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
 }
 
 template <int MODE>
-__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   if constexpr (MODE == kDown)
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                    __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   else
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                     __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-template <int BM, int BN, int MODE>
-__global__ __launch_bounds__(kThreads, 2) void k_gemm_mfma(
+constexpr int kSK = 32;  // K elements per LDS stage (one 64-byte row per tile row)
+
+// Rows of one stage, padded to whole 16-row wavefront loads per wave.
+constexpr int gemm_stage_rows(int BM, int BNB, int MODE) {
+  return (BM + BNB * (MODE == kGateUp ? 2 : 1) + 63) / 64 * 64;
+}
+// Bytes of LDS one block of k_gemm_mfma<BM, BNB, MODE, NS> uses.
+constexpr int gemm_lds_bytes(int BM, int BNB, int MODE, int NS) {
+  return NS * gemm_stage_rows(BM, BNB, MODE) * kSK * 2;
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
+
+// s_waitcnt that waits for vmcnt <= n and lgkmcnt/expcnt not at all (gfx9 encoding).
+#define MOE_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+
+// Workgroup barrier without a memory fence: the pipeline's own s_waitcnt
+// orders the LDS traffic; the empty asm keeps the compiler from moving memory
+// operations across it.
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// BM token rows x BNB weight rows (per weight matrix) per block, 4 waves
+// (2x2, or 1x4 when BM = 32), v_mfma_f32_32x32x16 (bf16, or f16 for the down
+// projection).
+//
+// Data path.  Tiles move from global memory straight into LDS with
+// global_load_lds_dwordx4 (lane L of a wavefront writes 16 bytes at LDS base
+// + 16 L), so no registers stage them.  A stage covers 32 K elements: rows
+// [A tile | B0 tile | B1 tile | pad], each 64 bytes = four 16-byte chunks,
+// chunk c of row r stored at c ^ ((r >> 2) & 3) so the 16 rows one 16-lane
+// phase of a fragment read touches fall in distinct banks; the swizzle is
+// applied on the global side by choosing the chunk each lane fetches.  NS
+// stages form a ring: NS - 2 stages stay in flight ahead of the one being
+// multiplied.
+//
+// Per step (one stage, two K=16 MFMA slices): the second slice's fragments
+// are read, the first slice's MFMAs run, the wave waits for its loads of the
+// next stage and meets the others at a barrier, the loads NS-1 stages ahead
+// are issued into the stage freed one step ago, the next step's first-slice
+// fragments are read, and the second slice's MFMAs run -- so fragment reads
+// and loads always overlap queued MFMAs.
+//
+// The weight tile is the MFMA A operand and the token tile the B operand, so
+// a lane's 16 accumulators are 4 runs of 4 consecutive output columns of one
+// token row.
+template <int BM, int BNB, int MODE, int NS>
+__global__ __launch_bounds__(kThreads) void k_gemm_mfma(
     const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, long long strideB, int N, int K, void* __restrict__ Out,
     int ldo, const float* __restrict__ bias, const MTile* __restrict__ sched,
     const int32_t* __restrict__ count, int mslots, int ntiles, int static_rows,
     uint32_t* __restrict__ flags) {
   constexpr bool DUAL = MODE == kGateUp;
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int FM = WM / 16, FN = WN / 16;
-  constexpr int A_LD = BM * 8 / kThreads;  // 16-byte chunks per thread
-  constexpr int B_LD = BN * 8 / kThreads;
-  static_assert(FM >= 1 && FN >= 1 && A_LD >= 1 && B_LD >= 1, "tile too small");
+  constexpr int WAVES_M = BM >= 64 ? 2 : 1, WAVES_N = 4 / WAVES_M;
+  constexpr int WM = BM / WAVES_M, WN = BNB / WAVES_N;
+  constexpr int FM = WM / 32, FN = WN / 32;
+  constexpr int NB = DUAL ? 2 : 1;
+  constexpr int ROWS = gemm_stage_rows(BM, BNB, MODE);   // rows of one stage (padded)
+  constexpr int STAGE = ROWS * kSK;                      // elements of one stage
+  constexpr int NL = ROWS / 64;                          // 16-row loads per wave per stage
+  static_assert(BM % 32 == 0 && BNB % 32 == 0 && FM >= 1 && FN >= 1, "tile shape");
+  static_assert(NS >= 3 && NL * (NS - 2) <= 63, "pipeline depth");
 
   int mi, ni;
-  if (!block_tile(mslots, ntiles, mi, ni)) return;
+  const int mtiles = sched ? min(*count, mslots) : (static_rows + BM - 1) / BM;
+  if (!block_tile(mtiles, ntiles, mi, ni)) return;
   int expert = 0, row0, rows;
   if (sched) {
-    if (mi >= *count) return;
     const MTile t = sched[mi];
     expert = t.expert;
     row0 = t.row0;
     rows = t.rows;
   } else {
     row0 = mi * BM;
-    if (row0 >= static_rows) return;
     rows = min(BM, static_rows - row0);
   }
-  const int n0 = ni * BN;
+  const int n0 = ni * BNB;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sA[BM * kBK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB0[BN * kBK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB1[DUAL ? BN * kBK : 8];
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
-  const int lc = tid & 7;   // 16-byte chunk of a 64-wide K row
-  const int lr = tid >> 3;  // first row this thread loads
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
 
   const uint16_t* Ab = A + (size_t)row0 * lda;
   const uint16_t* B0b = B0 + (size_t)expert * strideB;
-  const uint16_t* B1b = DUAL ? B1 + (size_t)expert * strideB : nullptr;
+  const uint16_t* B1b = DUAL ? B1 + (size_t)expert * strideB : B0b;
 
-  // per-thread global source offsets (rows clamped into range), in elements
-  int oa[A_LD], ob[B_LD];
+  // load i of this wave fills stage rows 16*(wave + 4 i) .. +16; lane -> (row, chunk)
+  int goff[NL];
 #pragma unroll
-  for (int i = 0; i < A_LD; ++i) oa[i] = min(lr + 32 * i, rows - 1) * lda + lc * 8;
-#pragma unroll
-  for (int i = 0; i < B_LD; ++i) ob[i] = min(n0 + lr + 32 * i, N - 1) * K + lc * 8;
-
-  u32x4 ra[A_LD], rb0[B_LD], rb1[DUAL ? B_LD : 1];
-#define MOE_GLOAD(k0)                                                                  \
-  do {                                                                                 \
-    _Pragma("unroll") for (int i = 0; i < A_LD; ++i)                                   \
-        ra[i] = *reinterpret_cast<const u32x4*>(Ab + oa[i] + (k0));                    \
-    _Pragma("unroll") for (int i = 0; i < B_LD; ++i)                                   \
-        rb0[i] = *reinterpret_cast<const u32x4*>(B0b + ob[i] + (k0));                  \
-    if constexpr (DUAL) {                                                              \
-      _Pragma("unroll") for (int i = 0; i < B_LD; ++i)                                 \
-          rb1[i] = *reinterpret_cast<const u32x4*>(B1b + ob[i] + (k0));                \
-    }                                                                                  \
+  for (int i = 0; i < NL; ++i) {
+    const int rho = 16 * (wave + 4 * i) + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((rho >> 2) & 3);
+    if (rho < BM) {
+      goff[i] = min(rho, rows - 1) * lda + chunk * 8;
+    } else if (rho < BM + NB * BNB) {
+      const int br = (rho - BM) % BNB;
+      goff[i] = min(n0 + br, N - 1) * K + chunk * 8;
+    } else {
+      goff[i] = chunk * 8;  // pad rows: any valid address (row 0 of the A tile)
+    }
+  }
+  const int steps = K / kSK;
+#define MOE_LOAD_STAGE(step_)                                                           \
+  do {                                                                                  \
+    const int st_ = (step_) < steps ? (step_) : steps - 1;                              \
+    uint16_t* base_ = smem + ((step_) % NS) * STAGE;                                    \
+    _Pragma("unroll") for (int i = 0; i < NL; ++i) {                                    \
+      const int r0_ = 16 * (wave + 4 * i);                                              \
+      const uint16_t* src_ = r0_ < BM ? Ab : (r0_ < BM + BNB ? B0b : (r0_ < BM + NB * BNB ? B1b : Ab)); \
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src_ + goff[i] + st_ * kSK),         \
+                                       (lds_ptr_t)(base_ + r0_ * kSK), 16, 0, 0);       \
+    }                                                                                   \
   } while (0)
 
-  f32x4 acc0[FN][FM];
-  f32x4 acc1[DUAL ? FN : 1][DUAL ? FM : 1];
+  f32x16 acc0[FN][FM];
+  f32x16 acc1[DUAL ? FN : 1][DUAL ? FM : 1];
 #pragma unroll
   for (int a = 0; a < FN; ++a)
 #pragma unroll
     for (int b = 0; b < FM; ++b) {
-      acc0[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (DUAL) acc1[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        acc0[a][b][q] = 0.f;
+        if constexpr (DUAL) acc1[a][b][q] = 0.f;
+      }
     }
 
-  const int fr = lane & 15;   // row of a 16-row fragment this lane feeds
-  const int fk = lane >> 4;   // which 8-element K chunk (of 4) this lane feeds
+  const int fr = lane & 31;   // row of a 32-row fragment this lane feeds
+  const int fk = lane >> 5;   // which 8-element K chunk (of 2) of a slice this lane feeds
 
-  MOE_GLOAD(0);
-  for (int k0 = 0; k0 < K; k0 += kBK) {
+  u32x4 xa[2][FM], wb0[2][FN], wb1[2][DUAL ? FN : 1];
+  // fragments of slice ks (0/1) of the stage holding `step_` into set `set_`
+#define MOE_READ_FRAGS(set_, step_, ks_)                                                \
+  do {                                                                                  \
+    const uint16_t* sA_ = smem + ((step_) % NS) * STAGE;                                \
+    const uint16_t* sB0_ = sA_ + BM * kSK;                                              \
+    const uint16_t* sB1_ = sB0_ + BNB * kSK;                                            \
+    const int c_ = (ks_) * 2 + fk;                                                      \
+    _Pragma("unroll") for (int b = 0; b < FM; ++b) {                                    \
+      const int r = wm * WM + b * 32 + fr;                                              \
+      xa[set_][b] = *reinterpret_cast<const u32x4*>(sA_ + r * kSK + ((c_ ^ ((r >> 2) & 3)) << 3)); \
+    }                                                                                   \
+    _Pragma("unroll") for (int a = 0; a < FN; ++a) {                                    \
+      const int r = wn * WN + a * 32 + fr;                                              \
+      wb0[set_][a] = *reinterpret_cast<const u32x4*>(sB0_ + r * kSK + ((c_ ^ ((r >> 2) & 3)) << 3)); \
+      if constexpr (DUAL)                                                               \
+        wb1[set_][a] = *reinterpret_cast<const u32x4*>(sB1_ + r * kSK + ((c_ ^ ((r >> 2) & 3)) << 3)); \
+    }                                                                                   \
+  } while (0)
+#define MOE_MFMAS(set_)                                                                 \
+  do {                                                                                  \
+    _Pragma("unroll") for (int a = 0; a < FN; ++a) {                                    \
+      const u32x4 w0_ = MODE == kDown ? bf16x8_to_f16x8(wb0[set_][a]) : wb0[set_][a];    \
+      _Pragma("unroll") for (int b = 0; b < FM; ++b) {                                  \
+        acc0[a][b] = mfma32<MODE>(w0_, xa[set_][b], acc0[a][b]);                        \
+        if constexpr (DUAL) acc1[a][b] = mfma32<MODE>(wb1[set_][a], xa[set_][b], acc1[a][b]); \
+      }                                                                                 \
+    }                                                                                   \
+  } while (0)
+
+  // prologue: stages 0 .. NS-2 in flight; wait for stage 0; first slice of step 0
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const int r = lr + 32 * i;
-      *reinterpret_cast<u32x4*>(sA + r * kBK + ((lc ^ (r & 7)) << 3)) = ra[i];
+  for (int s0 = 0; s0 < NS - 1; ++s0) MOE_LOAD_STAGE(s0);
+  MOE_WAIT_VMCNT(NL * (NS - 2));
+  raw_barrier();
+  MOE_READ_FRAGS(0, 0, 0);
+  constexpr int NRD = FM + NB * FN;   // fragment reads per slice
+  constexpr int NMF = NB * FN * FM;   // MFMAs per slice
+  for (int t = 0; t < steps; ++t) {
+    // region 1: slice-0 MFMAs with the slice-1 fragment reads between them
+    MOE_READ_FRAGS(1, t, 1);
+    MOE_MFMAS(0);
+#pragma unroll
+    for (int q = 0; q < NMF; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);            // MFMA
+      if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // DS read
     }
+    __builtin_amdgcn_sched_barrier(0);
+    MOE_WAIT_VMCNT(NL * (NS - 3));  // this wave's loads of step t+1 have landed
+    raw_barrier();                  // ... and every wave's; step t-1's stage is free
+    __builtin_amdgcn_sched_barrier(0);
+    // region 2: slice-1 MFMAs with the loads NS-1 steps ahead and the next
+    // step's slice-0 fragment reads between them (on the last step that read
+    // is of a stale stage and unused)
+    MOE_LOAD_STAGE(t + NS - 1);
+    MOE_READ_FRAGS(0, t + 1, 0);
+    MOE_MFMAS(1);
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const int r = lr + 32 * i;
-      const u32x4 v = MODE == kDown ? bf16x8_to_f16x8(rb0[i]) : rb0[i];
-      *reinterpret_cast<u32x4*>(sB0 + r * kBK + ((lc ^ (r & 7)) << 3)) = v;
-      if constexpr (DUAL) *reinterpret_cast<u32x4*>(sB1 + r * kBK + ((lc ^ (r & 7)) << 3)) = rb1[i];
+    for (int q = 0; q < NMF; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);             // MFMA
+      if (q < NL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 2);   // VMEM load
+      if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);  // DS read
     }
-    __syncthreads();
-    if (k0 + kBK < K) MOE_GLOAD(k0 + kBK);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int c = kk * 4 + fk;
-      u32x4 xa[FM], wb0[FN], wb1[DUAL ? FN : 1];
-#pragma unroll
-      for (int b = 0; b < FM; ++b) {
-        const int r = wm * WM + b * 16 + fr;
-        xa[b] = *reinterpret_cast<const u32x4*>(sA + r * kBK + ((c ^ (r & 7)) << 3));
-      }
-#pragma unroll
-      for (int a = 0; a < FN; ++a) {
-        const int r = wn * WN + a * 16 + fr;
-        wb0[a] = *reinterpret_cast<const u32x4*>(sB0 + r * kBK + ((c ^ (r & 7)) << 3));
-        if constexpr (DUAL)
-          wb1[a] = *reinterpret_cast<const u32x4*>(sB1 + r * kBK + ((c ^ (r & 7)) << 3));
-      }
-#pragma unroll
-      for (int a = 0; a < FN; ++a)
-#pragma unroll
-        for (int b = 0; b < FM; ++b) {
-          acc0[a][b] = mfma16<MODE>(wb0[a], xa[b], acc0[a][b]);
-          if constexpr (DUAL) acc1[a][b] = mfma16<MODE>(wb1[a], xa[b], acc1[a][b]);
-        }
-    }
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
   }
-#undef MOE_GLOAD
+  __builtin_amdgcn_s_waitcnt(0);  // drain the clamped tail loads before the block ends
+#undef MOE_LOAD_STAGE
+#undef MOE_READ_FRAGS
+#undef MOE_MFMAS
 
-  // epilogue: lane holds output columns n..n+3 of token row m
+  // epilogue: accumulator q of fragment (a, b) is output column
+  // n = a*32 + 8*(q/4) + 4*(lane/32) + q%4 of token row m = b*32 + lane%32
   bool overflow = false;
 #pragma unroll
-  for (int a = 0; a < FN; ++a) {
-    const int n = n0 + wn * WN + a * 16 + fk * 4;
+  for (int b = 0; b < FM; ++b) {
+    const int m = wm * WM + b * 32 + fr;
+    if (m >= rows) continue;
 #pragma unroll
-    for (int b = 0; b < FM; ++b) {
-      const int m = wm * WM + b * 16 + fr;
-      if (m >= rows) continue;
-      const size_t o = (size_t)(row0 + m) * ldo + n;
-      if constexpr (DUAL) {
-        if (n + 3 < N) {
-          const f32x4 g = acc0[a][b], u = acc1[a][b];
-          const float h0 = silu_mul(g[0], u[0]), h1 = silu_mul(g[1], u[1]);
-          const float h2 = silu_mul(g[2], u[2]), h3 = silu_mul(g[3], u[3]);
-          overflow |= !(fabsf(h0) <= 65504.f && fabsf(h1) <= 65504.f && fabsf(h2) <= 65504.f &&
-                        fabsf(h3) <= 65504.f);
-          u32x2 pk;
-          pk[0] = f32_to_f16_bits(h0) | (f32_to_f16_bits(h1) << 16);
-          pk[1] = f32_to_f16_bits(h2) | (f32_to_f16_bits(h3) << 16);
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Out) + o) = pk;
-        }
-      } else {
-        f32x4 v = acc0[a][b];
-        float* dst = static_cast<float*>(Out) + o;
-        if (n + 3 < N && (ldo & 3) == 0) {
-          if (bias) {
-            v[0] += bias[n];
-            v[1] += bias[n + 1];
-            v[2] += bias[n + 2];
-            v[3] += bias[n + 3];
+    for (int a = 0; a < FN; ++a) {
+#pragma unroll
+      for (int qi = 0; qi < 4; ++qi) {
+        const int n = n0 + wn * WN + a * 32 + 8 * qi + 4 * fk;
+        const size_t o = (size_t)(row0 + m) * ldo + n;
+        if constexpr (DUAL) {
+          if (n + 3 < N) {
+            const f32x16 g = acc0[a][b], u = acc1[a][b];
+            const float h0 = silu_mul(g[4 * qi], u[4 * qi]);
+            const float h1 = silu_mul(g[4 * qi + 1], u[4 * qi + 1]);
+            const float h2 = silu_mul(g[4 * qi + 2], u[4 * qi + 2]);
+            const float h3 = silu_mul(g[4 * qi + 3], u[4 * qi + 3]);
+            overflow |= !(fabsf(h0) <= 65504.f && fabsf(h1) <= 65504.f &&
+                          fabsf(h2) <= 65504.f && fabsf(h3) <= 65504.f);
+            u32x2 pk;
+            pk[0] = f32_to_f16_bits(h0) | (f32_to_f16_bits(h1) << 16);
+            pk[1] = f32_to_f16_bits(h2) | (f32_to_f16_bits(h3) << 16);
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Out) + o) = pk;
           }
-          *reinterpret_cast<f32x4*>(dst) = v;
         } else {
+          const f32x16 acc = acc0[a][b];
+          f32x4 v = {acc[4 * qi], acc[4 * qi + 1], acc[4 * qi + 2], acc[4 * qi + 3]};
+          float* dst = static_cast<float*>(Out) + o;
+          if (n + 3 < N && (ldo & 3) == 0) {
+            if (bias) {
+              v[0] += bias[n];
+              v[1] += bias[n + 1];
+              v[2] += bias[n + 2];
+              v[3] += bias[n + 3];
+            }
+            *reinterpret_cast<f32x4*>(dst) = v;
+          } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (n + q < N) dst[q] = v[q] + (bias ? bias[n + q] : 0.0f);
+            for (int q = 0; q < 4; ++q)
+              if (n + q < N) dst[q] = v[q] + (bias ? bias[n + q] : 0.0f);
+          }
         }
       }
     }
@@ -275,10 +381,10 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, i
                                                   int ntiles, int static_rows) {
   constexpr int TB = 32, TK = 16;
   int mi, ni;
-  if (!block_tile(mslots, ntiles, mi, ni)) return;
+  const int mtiles = sched ? min(*count, mslots) : (static_rows + TB - 1) / TB;
+  if (!block_tile(mtiles, ntiles, mi, ni)) return;
   int expert = 0, row0, rows;
   if (sched) {
-    if (mi >= *count) return;
     const MTile t = sched[mi];
     expert = t.expert;
     row0 = t.row0;
@@ -333,13 +439,44 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, i
   }
 }
 
+// Worst-case grid: every row-tile slot real; a multiple of 8 (one slot per XCD).
 inline int grid_for(int mslots, int ntiles) {
-  const int groups = (mslots + kGroupM - 1) / kGroupM;
-  const int g = groups * kGroupM * ntiles;
-  return (g + 7) / 8 * 8;
+  const long long g = (long long)mslots * ntiles;
+  return (int)((g + 7) / 8 * 8);
+}
+
+// Launches k_gemm_mfma<BM, BNB, MODE>, raising the block's LDS limit when the
+// two stages exceed the default 64 KiB.
+template <int BM, int BNB, int MODE, int NS>
+hipError_t launch_mfma(const void* A, int lda, const void* B0, const void* B1, int N, int K,
+                       void* out, int ldo, const float* bias, const MTile* sched,
+                       const int32_t* count, int mslots, int static_rows, uint32_t* flags,
+                       hipStream_t st) {
+  constexpr int lds = gemm_lds_bytes(BM, BNB, MODE, NS);
+  static_assert(lds <= 160 * 1024, "LDS");
+  static bool attr_set = false;
+  if (lds > 65536 && !attr_set) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&k_gemm_mfma<BM, BNB, MODE, NS>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int ntiles = (N + BNB - 1) / BNB;
+  const dim3 grid(grid_for(mslots, ntiles));
+  hipLaunchKernelGGL((k_gemm_mfma<BM, BNB, MODE, NS>), grid, dim3(kThreads), lds, st,
+                     static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B0),
+                     static_cast<const uint16_t*>(B1), (long long)N * K, N, K, out, ldo, bias,
+                     sched, count, mslots, ntiles, static_rows, flags);
+  return hipGetLastError();
 }
 
 }  // namespace
+
+int gemm_tile_rows(int dtype, int bm_hint) {
+  if (dtype == MOE_F32) return 32;
+  return bm_hint >= 256 ? 256 : (bm_hint >= 128 ? 128 : 32);
+}
 
 hipError_t launch_gemm_gateup(int dtype, int bm, const void* A, int lda, const void* Bg,
                               const void* Bu, int N, int K, void* h, int ldh, const MTile* sched,
@@ -356,20 +493,16 @@ hipError_t launch_gemm_gateup(int dtype, int bm, const void* A, int lda, const v
                        nullptr, sched, count, mslots, ntiles, static_rows);
     return hipGetLastError();
   }
-  constexpr int BN = 128;
-  const int ntiles = (N + BN - 1) / BN;
   const int mslots = sched ? max_tiles : (static_rows + bm - 1) / bm;
   if (mslots == 0) return hipSuccess;
-  const dim3 grid(grid_for(mslots, ntiles));
-#define MOE_GU(BM)                                                                               \
-  hipLaunchKernelGGL((k_gemm_mfma<BM, BN, kGateUp>), grid, dim3(kThreads), 0, st,               \
-                     static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(Bg),     \
-                     static_cast<const uint16_t*>(Bu), strideB, N, K, h, ldh, nullptr, sched,    \
-                     count, mslots, ntiles, static_rows, flags)
-  if (bm == 128) MOE_GU(128);
-  else MOE_GU(32);
-#undef MOE_GU
-  return hipGetLastError();
+  if (bm == 256)
+    return launch_mfma<256, 128, kGateUp, 5>(A, lda, Bg, Bu, N, K, h, ldh, nullptr, sched, count,
+                                          mslots, static_rows, flags, st);
+  if (bm == 128)
+    return launch_mfma<128, 128, kGateUp, 4>(A, lda, Bg, Bu, N, K, h, ldh, nullptr, sched, count,
+                                          mslots, static_rows, flags, st);
+  return launch_mfma<32, 128, kGateUp, 4>(A, lda, Bg, Bu, N, K, h, ldh, nullptr, sched, count,
+                                       mslots, static_rows, flags, st);
 }
 
 hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int lda,
@@ -386,25 +519,23 @@ hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int 
                        strideB, N, K, Y, ldy, bias, sched, count, mslots, ntiles, static_rows);
     return hipGetLastError();
   }
-  constexpr int BN = 128;
-  const int ntiles = (N + BN - 1) / BN;
   const int mslots = sched ? max_tiles : (static_rows + bm - 1) / bm;
   if (mslots == 0) return hipSuccess;
-  const dim3 grid(grid_for(mslots, ntiles));
-#define MOE_PL(BM, MODE)                                                                         \
-  hipLaunchKernelGGL((k_gemm_mfma<BM, BN, MODE>), grid, dim3(kThreads), 0, st,                  \
-                     static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B),      \
-                     nullptr, strideB, N, K, Y, ldy, bias, sched, count, mslots, ntiles,         \
-                     static_rows, nullptr)
   if (a_is_h) {
-    if (bm == 128) MOE_PL(128, kDown);
-    else MOE_PL(32, kDown);
-  } else {
-    if (bm == 128) MOE_PL(128, kPlain);
-    else MOE_PL(32, kPlain);
+    if (bm == 256)
+      return launch_mfma<256, 256, kDown, 5>(A, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
+                                          mslots, static_rows, nullptr, st);
+    if (bm == 128)
+      return launch_mfma<128, 128, kDown, 4>(A, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
+                                          mslots, static_rows, nullptr, st);
+    return launch_mfma<32, 128, kDown, 4>(A, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
+                                       mslots, static_rows, nullptr, st);
   }
-#undef MOE_PL
-  return hipGetLastError();
+  if (bm == 128)
+    return launch_mfma<128, 128, kPlain, 4>(A, lda, B, nullptr, N, K, Y, ldy, bias, sched, count,
+                                         mslots, static_rows, nullptr, st);
+  return launch_mfma<32, 128, kPlain, 4>(A, lda, B, nullptr, N, K, Y, ldy, bias, sched, count,
+                                      mslots, static_rows, nullptr, st);
 }
 
 }  // namespace moe

@@ -95,7 +95,7 @@ GemmPlan choose_gemm_plan(const moe_shape& s) {
   const long long slots = (long long)s.num_tokens * s.top_k;
   // rows per expert when the load is even: few rows -> weight streaming tiles
   const long long avg = slots / (s.num_experts > 0 ? s.num_experts : 1);
-  p.bm_gu = p.bm_dn = avg >= 96 ? 128 : 32;
+  p.bm_gu = p.bm_dn = avg >= 512 ? 256 : (avg >= 96 ? 128 : 32);
   if (s.act_dtype == MOE_F32) p.bm_gu = p.bm_dn = 32;  // the fp32 kernel's tile height
   return p;
 }
@@ -178,7 +178,7 @@ moe_status run_ffn(const moe_shape& s, const void* x_perm, const int32_t* offset
 moe_status run_shared(const moe_shape& s, const void* x, const void* wsg, const void* wsu,
                       const void* wsd, void* ws, const WsLayout& L, hipStream_t st) {
   const int T = s.num_tokens, H = s.hidden, Is = s.shared_intermediate;
-  const int bm = s.act_dtype == MOE_F32 ? 32 : (T >= 128 ? 128 : 32);
+  const int bm = s.act_dtype == MOE_F32 ? 32 : (T >= 2048 ? 256 : (T >= 128 ? 128 : 32));
   void* hs = at<void>(ws, L.hs);
   float* ys = at<float>(ws, L.ys);
   MOE_HIP(launch_gemm_gateup(s.act_dtype, bm, x, H, wsg, wsu, Is, H, hs, Is, nullptr, nullptr, 0,

@@ -74,6 +74,9 @@ hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int 
                              const MTile* sched, const int32_t* count, int max_tiles,
                              int static_rows, hipStream_t st);
 
+// Row-tile height the GEMM launchers use for a dtype and a requested height.
+int gemm_tile_rows(int dtype, int bm_hint);
+
 hipError_t launch_combine(const moe_shape& s, const float* y_perm, const int32_t* row_of_slot,
                           const float* gates, const float* y_shared, void* out, hipStream_t st);
 
