@@ -195,6 +195,14 @@ def main():
     b_gemm = sum(model[s]["bytes"] for s in gemm_stages)
     t_roof_gemm = max(f_gemm / peak_f, b_gemm / PEAK_HBM)
 
+    # HBM traffic of the dominant kernel from the committed counter summary,
+    # only while the kernel source is the one the counters were taken on
+    from expert_serving_amd import profiling
+    traffic = None
+    rec = profiling.read_traffic(os.path.join(ROOT, "profiles", f"{dom}_gemm_{cfg.name}_traffic.md"))
+    if rec and rec.get("source_sha256") == profiling.source_sha256():
+        traffic = float(rec["traffic_bytes"])
+
     line = {
         "metric": "MoE-layer tokens/sec at 1 GPU; grouped-GEMM % of bf16 MFMA / HBM peak",
         "value": round(tokens_per_s, 1),
@@ -212,7 +220,7 @@ def main():
                    "top_k": cfg.top_k, "intermediate": cfg.inter, "shared_intermediate": cfg.shared_inter,
                    "capacity_factor": cfg.capacity_factor, "parallelism": "one GPU's expert-parallel share"},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                     "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom,
+                     "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
                      "kernel_ms": round(stage_ms[dom], 4),
                      "per_launch_algorithmic": {"flops": m["flops"], "bytes": m["bytes"], "rows": m["units"]}},
         "grouped_gemm": {"ms": round(t_gemm * 1e3, 4), "tflops": round(f_gemm / t_gemm / 1e12, 2),

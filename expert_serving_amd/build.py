@@ -25,6 +25,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["moe_api.hip", "route.hip", "dispatch.hip", "gemm.hip", "combine.hip"]
+PEAKS_SRC = "peaks.hip"
+PEAKS_BIN = os.path.join(HERE, "moe_peaks")
 NO_CONTRACT = {"route.hip"}
 
 COMMON = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
@@ -56,8 +58,13 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    # the ceiling microbenchmark (a standalone program)
+    cmd = [HIPCC, *[c for c in COMMON if c != "-fPIC"], os.path.join(CSRC, PEAKS_SRC), "-o", PEAKS_BIN]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PEAKS_SRC}:\n{r.stdout}\n{r.stderr}")
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PEAKS_BIN}")
     return LIB
 
 
