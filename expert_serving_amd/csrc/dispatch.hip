@@ -172,39 +172,54 @@ __global__ __launch_bounds__(256) void k_gather(const uint4* __restrict__ x,
   for (int i = lane; i < row_vecs; i += 64) dst[i] = src[i];
 }
 
-// Row tiles of `bm` rows per expert: tile list in expert order.
+// Row tiles per expert, in expert order: experts with at least split_rows kept
+// rows go to the big list in tiles of bm_big rows, the others to the small
+// list in tiles of bm_small rows.
 __global__ __launch_bounds__(512) void k_build_sched(const int32_t* __restrict__ offsets, int E,
-                                                     int bm, MTile* __restrict__ sched,
-                                                     int32_t* __restrict__ count, int max_tiles) {
-  __shared__ int s_scan[512];
+                                                     int bm_big, int bm_small, int split_rows,
+                                                     MTile* __restrict__ sched_big, int max_big,
+                                                     MTile* __restrict__ sched_small, int max_small,
+                                                     int32_t* __restrict__ count) {
+  __shared__ int s_big[512], s_small[512];
   const int tid = threadIdx.x;
-  int nt = 0, r0 = 0, kept = 0;
+  int r0 = 0, kept = 0, nb = 0, ns = 0;
   if (tid < E) {
     r0 = offsets[tid];
     kept = offsets[tid + 1] - r0;
-    nt = (kept + bm - 1) / bm;
+    if (kept >= split_rows) nb = (kept + bm_big - 1) / bm_big;
+    else ns = (kept + bm_small - 1) / bm_small;
   }
-  s_scan[tid] = nt;
+  s_big[tid] = nb;
+  s_small[tid] = ns;
   __syncthreads();
   for (int off = 1; off < 512; off <<= 1) {
-    const int add = tid >= off ? s_scan[tid - off] : 0;
+    const int ab = tid >= off ? s_big[tid - off] : 0;
+    const int as = tid >= off ? s_small[tid - off] : 0;
     __syncthreads();
-    s_scan[tid] += add;
+    s_big[tid] += ab;
+    s_small[tid] += as;
     __syncthreads();
   }
-  const int base = s_scan[tid] - nt;
+  const int bm = nb ? bm_big : bm_small;
+  const int nt = nb ? nb : ns;
+  const int base = nb ? s_big[tid] - nb : s_small[tid] - ns;
+  MTile* out = nb ? sched_big : sched_small;
+  const int cap = nb ? max_big : max_small;
   for (int i = 0; i < nt; ++i) {
     const int slot = base + i;
-    if (slot < max_tiles) {
+    if (slot < cap) {
       MTile m;
       m.expert = tid;
       m.row0 = r0 + i * bm;
       m.rows = min(bm, kept - i * bm);
       m.pad = 0;
-      sched[slot] = m;
+      out[slot] = m;
     }
   }
-  if (tid == 511) *count = min(s_scan[511], max_tiles);
+  if (tid == 511) {
+    count[0] = min(s_big[511], max_big);
+    count[1] = min(s_small[511], max_small);
+  }
 }
 
 __global__ void k_clear_flags(uint32_t* flags) { *flags = 0u; }
@@ -244,10 +259,12 @@ hipError_t launch_gather(const moe_shape& s, const void* x, const int32_t* row_t
   return hipGetLastError();
 }
 
-hipError_t launch_build_schedule(const int32_t* offsets, int E, int bm, MTile* sched,
-                                 int32_t* count, int max_tiles, hipStream_t st) {
-  hipLaunchKernelGGL(k_build_sched, dim3(1), dim3(512), 0, st, offsets, E, bm, sched, count,
-                     max_tiles);
+hipError_t launch_build_schedule(const int32_t* offsets, int E, const GemmPlan& plan,
+                                 MTile* sched_big, int max_big, MTile* sched_small, int max_small,
+                                 int32_t* count, hipStream_t st) {
+  hipLaunchKernelGGL(k_build_sched, dim3(1), dim3(512), 0, st, offsets, E, plan.bm_big,
+                     plan.bm_small, plan.split_rows, sched_big, max_big, sched_small, max_small,
+                     count);
   return hipGetLastError();
 }
 

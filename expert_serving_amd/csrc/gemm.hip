@@ -34,8 +34,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kGroupM = 8;
-constexpr int kThreads = 256;
+constexpr int kGroupM = 16;
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   const uint32_t b = __float_as_uint(f);
@@ -108,12 +107,12 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
 constexpr int kSK = 32;  // K elements per LDS stage (one 64-byte row per tile row)
 
 // Rows of one stage, padded to whole 16-row wavefront loads per wave.
-constexpr int gemm_stage_rows(int BM, int BNB, int MODE) {
-  return (BM + BNB * (MODE == kGateUp ? 2 : 1) + 63) / 64 * 64;
+constexpr int gemm_stage_rows(int BM, int BNB, int MODE, int NW) {
+  return (BM + BNB * (MODE == kGateUp ? 2 : 1) + 16 * NW - 1) / (16 * NW) * (16 * NW);
 }
-// Bytes of LDS one block of k_gemm_mfma<BM, BNB, MODE, NS> uses.
-constexpr int gemm_lds_bytes(int BM, int BNB, int MODE, int NS) {
-  return NS * gemm_stage_rows(BM, BNB, MODE) * kSK * 2;
+// Bytes of LDS one block of k_gemm_mfma<BM, BNB, MODE, NS, NW> uses.
+constexpr int gemm_lds_bytes(int BM, int BNB, int MODE, int NS, int NW) {
+  return NS * gemm_stage_rows(BM, BNB, MODE, NW) * kSK * 2;
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -132,9 +131,10 @@ __device__ __forceinline__ void raw_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// BM token rows x BNB weight rows (per weight matrix) per block, 4 waves
-// (2x2, or 1x4 when BM = 32), v_mfma_f32_32x32x16 (bf16, or f16 for the down
-// projection).
+// BM token rows x BNB weight rows (per weight matrix) per block, NW waves
+// (2 x NW/2, or 1 x NW when BM = 32), v_mfma_f32_32x32x16 (bf16, or f16 for
+// the down projection).  With NW = 8 two waves share each SIMD, so one
+// wave's MFMAs keep running while the other stalls issuing loads.
 //
 // Data path.  Tiles move from global memory straight into LDS with
 // global_load_lds_dwordx4 (lane L of a wavefront writes 16 bytes at LDS base
@@ -156,21 +156,21 @@ __device__ __forceinline__ void raw_barrier() {
 // The weight tile is the MFMA A operand and the token tile the B operand, so
 // a lane's 16 accumulators are 4 runs of 4 consecutive output columns of one
 // token row.
-template <int BM, int BNB, int MODE, int NS>
-__global__ __launch_bounds__(kThreads) void k_gemm_mfma(
+template <int BM, int BNB, int MODE, int NS, int NW>
+__global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
     const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, long long strideB, int N, int K, void* __restrict__ Out,
     int ldo, const float* __restrict__ bias, const MTile* __restrict__ sched,
     const int32_t* __restrict__ count, int mslots, int ntiles, int static_rows,
     uint32_t* __restrict__ flags) {
   constexpr bool DUAL = MODE == kGateUp;
-  constexpr int WAVES_M = BM >= 64 ? 2 : 1, WAVES_N = 4 / WAVES_M;
+  constexpr int WAVES_M = BM >= 64 ? 2 : 1, WAVES_N = NW / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BNB / WAVES_N;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int NB = DUAL ? 2 : 1;
-  constexpr int ROWS = gemm_stage_rows(BM, BNB, MODE);   // rows of one stage (padded)
-  constexpr int STAGE = ROWS * kSK;                      // elements of one stage
-  constexpr int NL = ROWS / 64;                          // 16-row loads per wave per stage
+  constexpr int ROWS = gemm_stage_rows(BM, BNB, MODE, NW);  // rows of one stage (padded)
+  constexpr int STAGE = ROWS * kSK;                          // elements of one stage
+  constexpr int NL = ROWS / (16 * NW);                       // 16-row loads per wave per stage
   static_assert(BM % 32 == 0 && BNB % 32 == 0 && FM >= 1 && FN >= 1, "tile shape");
   static_assert(NS >= 3 && NL * (NS - 2) <= 63, "pipeline depth");
 
@@ -200,11 +200,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mfma(
   const uint16_t* B0b = B0 + (size_t)expert * strideB;
   const uint16_t* B1b = DUAL ? B1 + (size_t)expert * strideB : B0b;
 
-  // load i of this wave fills stage rows 16*(wave + 4 i) .. +16; lane -> (row, chunk)
+  // load i of this wave fills stage rows 16*(wave + NW i) .. +16; lane -> (row, chunk)
   int goff[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
-    const int rho = 16 * (wave + 4 * i) + (lane >> 2);
+    const int rho = 16 * (wave + NW * i) + (lane >> 2);
     const int chunk = (lane & 3) ^ ((rho >> 2) & 3);
     if (rho < BM) {
       goff[i] = min(rho, rows - 1) * lda + chunk * 8;
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mfma(
     const int st_ = (step_) < steps ? (step_) : steps - 1;                              \
     uint16_t* base_ = smem + ((step_) % NS) * STAGE;                                    \
     _Pragma("unroll") for (int i = 0; i < NL; ++i) {                                    \
-      const int r0_ = 16 * (wave + 4 * i);                                              \
+      const int r0_ = 16 * (wave + NW * i);                                             \
       const uint16_t* src_ = r0_ < BM ? Ab : (r0_ < BM + BNB ? B0b : (r0_ < BM + NB * BNB ? B1b : Ab)); \
       __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src_ + goff[i] + st_ * kSK),         \
                                        (lds_ptr_t)(base_ + r0_ * kSK), 16, 0, 0);       \
@@ -447,24 +447,24 @@ inline int grid_for(int mslots, int ntiles) {
 
 // Launches k_gemm_mfma<BM, BNB, MODE>, raising the block's LDS limit when the
 // two stages exceed the default 64 KiB.
-template <int BM, int BNB, int MODE, int NS>
+template <int BM, int BNB, int MODE, int NS, int NW>
 hipError_t launch_mfma(const void* A, int lda, const void* B0, const void* B1, int N, int K,
                        void* out, int ldo, const float* bias, const MTile* sched,
                        const int32_t* count, int mslots, int static_rows, uint32_t* flags,
                        hipStream_t st) {
-  constexpr int lds = gemm_lds_bytes(BM, BNB, MODE, NS);
+  constexpr int lds = gemm_lds_bytes(BM, BNB, MODE, NS, NW);
   static_assert(lds <= 160 * 1024, "LDS");
   static bool attr_set = false;
   if (lds > 65536 && !attr_set) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&k_gemm_mfma<BM, BNB, MODE, NS>),
+        reinterpret_cast<const void*>(&k_gemm_mfma<BM, BNB, MODE, NS, NW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int ntiles = (N + BNB - 1) / BNB;
   const dim3 grid(grid_for(mslots, ntiles));
-  hipLaunchKernelGGL((k_gemm_mfma<BM, BNB, MODE, NS>), grid, dim3(kThreads), lds, st,
+  hipLaunchKernelGGL((k_gemm_mfma<BM, BNB, MODE, NS, NW>), grid, dim3(64 * NW), lds, st,
                      static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B0),
                      static_cast<const uint16_t*>(B1), (long long)N * K, N, K, out, ldo, bias,
                      sched, count, mslots, ntiles, static_rows, flags);
@@ -496,12 +496,12 @@ hipError_t launch_gemm_gateup(int dtype, int bm, const void* A, int lda, const v
   const int mslots = sched ? max_tiles : (static_rows + bm - 1) / bm;
   if (mslots == 0) return hipSuccess;
   if (bm == 256)
-    return launch_mfma<256, 128, kGateUp, 5>(A, lda, Bg, Bu, N, K, h, ldh, nullptr, sched, count,
+    return launch_mfma<256, 128, kGateUp, 5, 8>(A, lda, Bg, Bu, N, K, h, ldh, nullptr, sched, count,
                                           mslots, static_rows, flags, st);
   if (bm == 128)
-    return launch_mfma<128, 128, kGateUp, 4>(A, lda, Bg, Bu, N, K, h, ldh, nullptr, sched, count,
+    return launch_mfma<128, 128, kGateUp, 4, 8>(A, lda, Bg, Bu, N, K, h, ldh, nullptr, sched, count,
                                           mslots, static_rows, flags, st);
-  return launch_mfma<32, 128, kGateUp, 4>(A, lda, Bg, Bu, N, K, h, ldh, nullptr, sched, count,
+  return launch_mfma<32, 128, kGateUp, 4, 4>(A, lda, Bg, Bu, N, K, h, ldh, nullptr, sched, count,
                                        mslots, static_rows, flags, st);
 }
 
@@ -523,18 +523,18 @@ hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int 
   if (mslots == 0) return hipSuccess;
   if (a_is_h) {
     if (bm == 256)
-      return launch_mfma<256, 256, kDown, 5>(A, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
+      return launch_mfma<256, 256, kDown, 5, 8>(A, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
                                           mslots, static_rows, nullptr, st);
     if (bm == 128)
-      return launch_mfma<128, 128, kDown, 4>(A, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
+      return launch_mfma<128, 128, kDown, 4, 8>(A, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
                                           mslots, static_rows, nullptr, st);
-    return launch_mfma<32, 128, kDown, 4>(A, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
+    return launch_mfma<32, 128, kDown, 4, 4>(A, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
                                        mslots, static_rows, nullptr, st);
   }
   if (bm == 128)
-    return launch_mfma<128, 128, kPlain, 4>(A, lda, B, nullptr, N, K, Y, ldy, bias, sched, count,
+    return launch_mfma<128, 128, kPlain, 4, 8>(A, lda, B, nullptr, N, K, Y, ldy, bias, sched, count,
                                          mslots, static_rows, nullptr, st);
-  return launch_mfma<32, 128, kPlain, 4>(A, lda, B, nullptr, N, K, Y, ldy, bias, sched, count,
+  return launch_mfma<32, 128, kPlain, 4, 4>(A, lda, B, nullptr, N, K, Y, ldy, bias, sched, count,
                                       mslots, static_rows, nullptr, st);
 }
 

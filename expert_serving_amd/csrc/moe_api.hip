@@ -1,5 +1,6 @@
 // Host side of the C ABI: argument validation (pure host code, before any HIP
 // call), workspace planning, and the launch sequence of each entry point.
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -93,10 +94,20 @@ T* at(void* ws, size_t off) {
 GemmPlan choose_gemm_plan(const moe_shape& s) {
   GemmPlan p;
   const long long slots = (long long)s.num_tokens * s.top_k;
-  // rows per expert when the load is even: few rows -> weight streaming tiles
+  // rows per expert if the load were even
   const long long avg = slots / (s.num_experts > 0 ? s.num_experts : 1);
-  p.bm_gu = p.bm_dn = avg >= 512 ? 256 : (avg >= 96 ? 128 : 32);
-  if (s.act_dtype == MOE_F32) p.bm_gu = p.bm_dn = 32;  // the fp32 kernel's tile height
+  p.bm_big = 256;
+  p.bm_small = 32;
+  if (s.act_dtype == MOE_F32) {
+    p.bm_big = p.bm_small = 32;  // the fp32 kernel's tile height
+    p.split_rows = 0;
+  } else if (avg >= 512) {
+    p.split_rows = 0;            // every expert large: MFMA-bound 256-row tiles
+  } else if (avg < 64) {
+    p.split_rows = 0x7fffffff;   // every expert small: weight-streaming 32-row tiles
+  } else {
+    p.split_rows = 128;          // skewed or mid-size loads: both classes
+  }
   return p;
 }
 
@@ -108,8 +119,16 @@ WsLayout plan_workspace(const moe_shape& s) {
   const size_t slots = T * k;
   const GemmPlan gp = choose_gemm_plan(s);
   w.n_dispatch_tiles = (int)((slots + kDispatchTileSlots - 1) / kDispatchTileSlots);
-  w.max_mtiles_gu = (int)(slots / (size_t)gp.bm_gu + E + 1);
-  w.max_mtiles_dn = (int)(slots / (size_t)gp.bm_dn + E + 1);
+  w.max_tiles_big = gp.has_big() ? (int)(slots / (size_t)gp.bm_big + E + 1) : 0;
+  {
+    // a small expert has fewer than split_rows rows
+    const size_t per_expert = gp.has_big() ? ((size_t)gp.split_rows + gp.bm_small - 1) / gp.bm_small
+                                           : (size_t)-1;
+    const size_t bound = slots / (size_t)gp.bm_small + E + 1;
+    w.max_tiles_small = gp.has_small() ? (int)std::min(bound, per_expert == (size_t)-1 ? bound
+                                                                                      : per_expert * E)
+                                       : 0;
+  }
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at_ = o;
@@ -126,8 +145,8 @@ WsLayout plan_workspace(const moe_shape& s) {
   w.row_of_slot = take(slots * 4);
   w.row_token = take(slots * 4);
   w.num_dropped = take(16);
-  w.sched_gu = take((size_t)w.max_mtiles_gu * sizeof(MTile));
-  w.sched_dn = take((size_t)w.max_mtiles_dn * sizeof(MTile));
+  w.sched_big = take((size_t)w.max_tiles_big * sizeof(MTile));
+  w.sched_small = take((size_t)w.max_tiles_small * sizeof(MTile));
   w.sched_count = take(16);
   w.x_perm = take(slots * H * eb);
   w.h = take(slots * I * eb);
@@ -154,23 +173,28 @@ moe_status run_ffn(const moe_shape& s, const void* x_perm, const int32_t* offset
                    const WsLayout& L, hipStream_t st, const moe_debug* dbg = nullptr) {
   const GemmPlan gp = choose_gemm_plan(s);
   const int E = s.num_experts, H = s.hidden, I = s.intermediate;
-  MTile* sg = at<MTile>(ws, L.sched_gu);
-  MTile* sd = at<MTile>(ws, L.sched_dn);
+  MTile* sb = at<MTile>(ws, L.sched_big);
+  MTile* ss = at<MTile>(ws, L.sched_small);
   int32_t* cnt = at<int32_t>(ws, L.sched_count);
-  const int bm_gu = gp.bm_gu;
-  const int bm_dn = gp.bm_dn;
-  MOE_HIP(launch_build_schedule(offsets, E, bm_gu, sg, cnt, L.max_mtiles_gu, st));
-  if (bm_dn != bm_gu) MOE_HIP(launch_build_schedule(offsets, E, bm_dn, sd, cnt + 1, L.max_mtiles_dn, st));
-  else { sd = sg; }
-  const int32_t* cnt_dn = bm_dn != bm_gu ? cnt + 1 : cnt;
+  uint32_t* flags = at<uint32_t>(ws, L.flags);
+  MOE_HIP(launch_build_schedule(offsets, E, gp, sb, L.max_tiles_big, ss, L.max_tiles_small, cnt,
+                                st));
   void* h = at<void>(ws, L.h);
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATE_UP, true, st));
-  MOE_HIP(launch_gemm_gateup(s.act_dtype, bm_gu, x_perm, H, w_gate, w_up, I, H, h, I, sg, cnt,
-                             L.max_mtiles_gu, 0, at<uint32_t>(ws, L.flags), st));
+  if (gp.has_big())
+    MOE_HIP(launch_gemm_gateup(s.act_dtype, gp.bm_big, x_perm, H, w_gate, w_up, I, H, h, I, sb,
+                               cnt, L.max_tiles_big, 0, flags, st));
+  if (gp.has_small())
+    MOE_HIP(launch_gemm_gateup(s.act_dtype, gp.bm_small, x_perm, H, w_gate, w_up, I, H, h, I, ss,
+                               cnt + 1, L.max_tiles_small, 0, flags, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATE_UP, false, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_DOWN, true, st));
-  MOE_HIP(launch_gemm_plain(s.act_dtype, bm_dn, true, h, I, w_down, H, I, nullptr, y, H, sd, cnt_dn,
-                            L.max_mtiles_dn, 0, st));
+  if (gp.has_big())
+    MOE_HIP(launch_gemm_plain(s.act_dtype, gp.bm_big, true, h, I, w_down, H, I, nullptr, y, H, sb,
+                              cnt, L.max_tiles_big, 0, st));
+  if (gp.has_small())
+    MOE_HIP(launch_gemm_plain(s.act_dtype, gp.bm_small, true, h, I, w_down, H, I, nullptr, y, H,
+                              ss, cnt + 1, L.max_tiles_small, 0, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_DOWN, false, st));
   return MOE_OK;
 }

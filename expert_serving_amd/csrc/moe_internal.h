@@ -25,14 +25,20 @@ struct MTile {
 // Byte offsets of every region inside the caller's workspace.
 struct WsLayout {
   size_t flags, logits, ids, gates, counts, offsets, tile_counts, row_of_slot, row_token,
-      num_dropped, sched_gu, sched_dn, sched_count, x_perm, h, y, hs, ys, total;
+      num_dropped, sched_big, sched_small, sched_count, x_perm, h, y, hs, ys, total;
   int n_dispatch_tiles;
-  int max_mtiles_gu, max_mtiles_dn;
+  int max_tiles_big, max_tiles_small;
 };
 
 // GEMM tile configuration chosen by the host for a shape.
+// Row tiling of the grouped GEMMs.  Experts with at least split_rows kept rows
+// are cut into tiles of bm_big rows, the others into tiles of bm_small rows;
+// each class gets its own tile list and launch (split_rows = 0: all big,
+// INT_MAX: all small).
 struct GemmPlan {
-  int bm_gu, bm_dn;  // token rows per tile of the gate/up and down launches
+  int bm_big, bm_small, split_rows;
+  bool has_big() const { return split_rows != 0x7fffffff; }
+  bool has_small() const { return split_rows != 0; }
 };
 
 GemmPlan choose_gemm_plan(const moe_shape& s);
@@ -56,8 +62,10 @@ hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, int32_t* coun
 hipError_t launch_gather(const moe_shape& s, const void* x, const int32_t* row_token,
                          const int32_t* offsets, void* x_perm, hipStream_t st);
 
-hipError_t launch_build_schedule(const int32_t* offsets, int E, int bm, MTile* sched,
-                                 int32_t* count, int max_tiles, hipStream_t st);
+// Both tile lists (see GemmPlan); count[0] = big tiles, count[1] = small tiles.
+hipError_t launch_build_schedule(const int32_t* offsets, int E, const GemmPlan& plan,
+                                 MTile* sched_big, int max_big, MTile* sched_small, int max_small,
+                                 int32_t* count, hipStream_t st);
 
 // Grouped GEMMs.  `sched`/`count` give the row tiles; when sched == nullptr
 // the rows [0, static_rows) form one group (expert 0) tiled statically.
