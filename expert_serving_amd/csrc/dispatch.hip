@@ -23,6 +23,8 @@ namespace {
 
 constexpr int kRankWaves = 4;
 constexpr int kSlotsPerWave = kDispatchTileSlots / kRankWaves;
+constexpr int kRankChunks = kSlotsPerWave / 64;  // 64-slot chunks per wave
+static_assert(kSlotsPerWave % 64 == 0, "dispatch tile");
 
 __global__ __launch_bounds__(256) void k_tile_hist(const int32_t* __restrict__ ids,
                                                    int total_slots, int E,
@@ -59,11 +61,17 @@ __global__ __launch_bounds__(1024) void k_scan_capacity(int32_t* __restrict__ ti
   const int tid = threadIdx.x;
   int run = 0;
   if (tid < E) {
-    for (int b = 0; b < n_tiles; ++b) {
-      int32_t* p = tile_counts + (size_t)b * E + tid;
-      const int c = *p;
-      *p = run;
-      run += c;
+    // eight tiles per round, so eight loads are in flight at once
+    for (int b0 = 0; b0 < n_tiles; b0 += 8) {
+      int c[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        c[i] = b0 + i < n_tiles ? tile_counts[(size_t)(b0 + i) * E + tid] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (b0 + i < n_tiles) tile_counts[(size_t)(b0 + i) * E + tid] = run;
+        run += c[i];
+      }
     }
     counts[tid] = run;
   }
@@ -103,21 +111,29 @@ __global__ __launch_bounds__(256) void k_rank_scatter(const int32_t* __restrict_
                                                       int32_t* __restrict__ row_of_slot,
                                                       int32_t* __restrict__ row_token) {
   __shared__ int wcnt[kRankWaves][kMaxExperts];
+  __shared__ int s_off[kMaxExperts];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int tile = blockIdx.x;
   const int wbase = tile * kDispatchTileSlots + wave * kSlotsPerWave;
 
+  // the wave's expert ids, all loads issued before any is used
+  int ev[kRankChunks];
+#pragma unroll
+  for (int i = 0; i < kRankChunks; ++i) {
+    const int s = wbase + 64 * i + lane;
+    ev[i] = s < total_slots ? ids[s] : -1;
+  }
   for (int i = threadIdx.x; i < kRankWaves * kMaxExperts; i += blockDim.x)
     (&wcnt[0][0])[i] = 0;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) s_off[e] = offsets[e];
+  const int cap = *cap_p;
   __syncthreads();
   // per-wave histogram of the wave's sub-tile
-  for (int q = lane; q < kSlotsPerWave; q += 64) {
-    const int s = wbase + q;
-    if (s < total_slots) {
-      const int e = ids[s];
-      if (e >= 0 && e < E) atomicAdd(&wcnt[wave][e], 1);
-    }
+#pragma unroll
+  for (int i = 0; i < kRankChunks; ++i) {
+    if (ev[i] < 0 || ev[i] >= E) ev[i] = -1;
+    if (ev[i] >= 0) atomicAdd(&wcnt[wave][ev[i]], 1);
   }
   __syncthreads();
   // running base of each wave = tile base + counts of the earlier waves
@@ -130,15 +146,12 @@ __global__ __launch_bounds__(256) void k_rank_scatter(const int32_t* __restrict_
     }
   }
   __syncthreads();
-  const int cap = *cap_p;
   // walk the sub-tile in order, 64 slots at a time
-  for (int c0 = 0; c0 < kSlotsPerWave; c0 += 64) {
-    const int s = wbase + c0 + lane;
-    int e = -1;
-    if (s < total_slots) {
-      e = ids[s];
-      if (e < 0 || e >= E) e = -1;
-    }
+#pragma unroll
+  for (int i = 0; i < kRankChunks; ++i) {
+    if (wbase + 64 * i >= total_slots) break;
+    const int s = wbase + 64 * i + lane;
+    const int e = ev[i];
     // stable rank inside the 64-slot chunk: equal experts in earlier lanes
     int before = 0, after = 0;
     for (int j = 0; j < 64; ++j) {
@@ -148,7 +161,7 @@ __global__ __launch_bounds__(256) void k_rank_scatter(const int32_t* __restrict_
     }
     if (e >= 0) {
       const int rank = wcnt[wave][e] + before;
-      const int row = rank < cap ? offsets[e] + rank : -1;
+      const int row = rank < cap ? s_off[e] + rank : -1;
       row_of_slot[s] = row;
       if (row >= 0) row_token[row] = s / k_max;
     } else if (s < total_slots) {

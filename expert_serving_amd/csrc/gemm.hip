@@ -104,15 +104,18 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                     __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-constexpr int kSK = 32;  // K elements per LDS stage (one 64-byte row per tile row)
+constexpr int kSK = 32;            // K elements per step (and per LDS row of 4-wave blocks)
+constexpr int kPingRowElems = 64;  // K elements per LDS row of 8-wave blocks (128 bytes)
 
-// Rows of one stage, padded to whole 16-row wavefront loads per wave.
+// Rows of one stage, padded to whole wavefront loads per wave: 16 rows per
+// load for 4-wave blocks, 8 rows per load for 8-wave blocks.
 constexpr int gemm_stage_rows(int BM, int BNB, int MODE, int NW) {
-  return (BM + BNB * (MODE == kGateUp ? 2 : 1) + 16 * NW - 1) / (16 * NW) * (16 * NW);
+  return (BM + BNB * (MODE == kGateUp ? 2 : 1) + (NW == 8 ? 8 : 16) * NW - 1) /
+         ((NW == 8 ? 8 : 16) * NW) * ((NW == 8 ? 8 : 16) * NW);
 }
 // Bytes of LDS one block of k_gemm_mfma<BM, BNB, MODE, NS, NW> uses.
 constexpr int gemm_lds_bytes(int BM, int BNB, int MODE, int NS, int NW) {
-  return NS * gemm_stage_rows(BM, BNB, MODE, NW) * kSK * 2;
+  return NS * gemm_stage_rows(BM, BNB, MODE, NW) * (NW == 8 ? kPingRowElems : kSK) * 2;
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -121,6 +124,9 @@ typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
 // s_waitcnt that waits for vmcnt <= n and lgkmcnt/expcnt not at all (gfx9 encoding).
 #define MOE_WAIT_VMCNT(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+
+// s_waitcnt that waits for lgkmcnt == 0 (LDS reads landed) and nothing else.
+#define MOE_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4))
 
 // Workgroup barrier without a memory fence: the pipeline's own s_waitcnt
 // orders the LDS traffic; the empty asm keeps the compiler from moving memory
@@ -133,32 +139,18 @@ __device__ __forceinline__ void raw_barrier() {
 
 // BM token rows x BNB weight rows (per weight matrix) per block, NW waves
 // (2 x NW/2, or 1 x NW when BM = 32), v_mfma_f32_32x32x16 (bf16, or f16 for
-// the down projection).  With NW = 8 two waves share each SIMD, so one
-// wave's MFMAs keep running while the other stalls issuing loads.
-//
-// Data path.  Tiles move from global memory straight into LDS with
-// global_load_lds_dwordx4 (lane L of a wavefront writes 16 bytes at LDS base
-// + 16 L), so no registers stage them.  A stage covers 32 K elements: rows
-// [A tile | B0 tile | B1 tile | pad], each 64 bytes = four 16-byte chunks,
-// chunk c of row r stored at c ^ ((r >> 2) & 3) so the 16 rows one 16-lane
-// phase of a fragment read touches fall in distinct banks; the swizzle is
-// applied on the global side by choosing the chunk each lane fetches.  NS
-// stages form a ring: NS - 2 stages stay in flight ahead of the one being
-// multiplied.
-//
-// Per step (one stage, two K=16 MFMA slices): the second slice's fragments
-// are read, the first slice's MFMAs run, the wave waits for its loads of the
-// next stage and meets the others at a barrier, the loads NS-1 stages ahead
-// are issued into the stage freed one step ago, the next step's first-slice
-// fragments are read, and the second slice's MFMAs run -- so fragment reads
-// and loads always overlap queued MFMAs.
+// the down projection).  8-wave blocks (two waves per SIMD) run a ping-pong
+// schedule over register-staged loads; 4-wave blocks (the 32-row tiles of
+// small experts) stream tiles straight into LDS.  Both schedules are
+// described where they are implemented, in the main loop below.
 //
 // The weight tile is the MFMA A operand and the token tile the B operand, so
 // a lane's 16 accumulators are 4 runs of 4 consecutive output columns of one
 // token row.
 template <int BM, int BNB, int MODE, int NS, int NW>
 __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
-    const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ B0,
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int lda,
+    const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, long long strideB, int N, int K, void* __restrict__ Out,
     int ldo, const float* __restrict__ bias, const MTile* __restrict__ sched,
     const int32_t* __restrict__ count, int mslots, int ntiles, int static_rows,
@@ -169,10 +161,12 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int NB = DUAL ? 2 : 1;
   constexpr int ROWS = gemm_stage_rows(BM, BNB, MODE, NW);  // rows of one stage (padded)
-  constexpr int STAGE = ROWS * kSK;                          // elements of one stage
-  constexpr int NL = ROWS / (16 * NW);                       // 16-row loads per wave per stage
+  // 8-wave blocks: register-staged ping-pong over two LDS stages; 4-wave
+  // blocks: direct-to-LDS loads over an NS-stage ring
+  constexpr bool PING = NW == 8;
+  constexpr bool CVT_ON_READ = MODE == kDown && !PING;  // down weights bf16 -> fp16 per read
   static_assert(BM % 32 == 0 && BNB % 32 == 0 && FM >= 1 && FN >= 1, "tile shape");
-  static_assert(NS >= 3 && NL * (NS - 2) <= 63, "pipeline depth");
+  static_assert(!PING || NS == 2, "ping-pong uses two LDS stages");
 
   int mi, ni;
   const int mtiles = sched ? min(*count, mslots) : (static_rows + BM - 1) / BM;
@@ -196,37 +190,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
   const int wave = tid >> 6;
   const int wm = wave % WAVES_M, wn = wave / WAVES_M;
 
-  const uint16_t* Ab = A + (size_t)row0 * lda;
+  // A rows are contiguous from row0, or gathered: tile row r is row a_rows[row0 + r]
+  const uint16_t* Ab = a_rows ? A : A + (size_t)row0 * lda;
   const uint16_t* B0b = B0 + (size_t)expert * strideB;
   const uint16_t* B1b = DUAL ? B1 + (size_t)expert * strideB : B0b;
-
-  // load i of this wave fills stage rows 16*(wave + NW i) .. +16; lane -> (row, chunk)
-  int goff[NL];
-#pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    const int rho = 16 * (wave + NW * i) + (lane >> 2);
-    const int chunk = (lane & 3) ^ ((rho >> 2) & 3);
-    if (rho < BM) {
-      goff[i] = min(rho, rows - 1) * lda + chunk * 8;
-    } else if (rho < BM + NB * BNB) {
-      const int br = (rho - BM) % BNB;
-      goff[i] = min(n0 + br, N - 1) * K + chunk * 8;
-    } else {
-      goff[i] = chunk * 8;  // pad rows: any valid address (row 0 of the A tile)
-    }
-  }
-  const int steps = K / kSK;
-#define MOE_LOAD_STAGE(step_)                                                           \
-  do {                                                                                  \
-    const int st_ = (step_) < steps ? (step_) : steps - 1;                              \
-    uint16_t* base_ = smem + ((step_) % NS) * STAGE;                                    \
-    _Pragma("unroll") for (int i = 0; i < NL; ++i) {                                    \
-      const int r0_ = 16 * (wave + NW * i);                                             \
-      const uint16_t* src_ = r0_ < BM ? Ab : (r0_ < BM + BNB ? B0b : (r0_ < BM + NB * BNB ? B1b : Ab)); \
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src_ + goff[i] + st_ * kSK),         \
-                                       (lds_ptr_t)(base_ + r0_ * kSK), 16, 0, 0);       \
-    }                                                                                   \
-  } while (0)
 
   f32x16 acc0[FN][FM];
   f32x16 acc1[DUAL ? FN : 1][DUAL ? FM : 1];
@@ -245,7 +212,182 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
   const int fk = lane >> 5;   // which 8-element K chunk (of 2) of a slice this lane feeds
 
   u32x4 xa[2][FM], wb0[2][FN], wb1[2][DUAL ? FN : 1];
-  // fragments of slice ks (0/1) of the stage holding `step_` into set `set_`
+#define MOE_MFMAS(set_)                                                                 \
+  do {                                                                                  \
+    _Pragma("unroll") for (int a = 0; a < FN; ++a) {                                    \
+      const u32x4 w0_ = CVT_ON_READ ? bf16x8_to_f16x8(wb0[set_][a]) : wb0[set_][a];      \
+      _Pragma("unroll") for (int b = 0; b < FM; ++b) {                                  \
+        acc0[a][b] = mfma32<MODE>(w0_, xa[set_][b], acc0[a][b]);                        \
+        if constexpr (DUAL) acc1[a][b] = mfma32<MODE>(wb1[set_][a], xa[set_][b], acc1[a][b]); \
+      }                                                                                 \
+    }                                                                                   \
+  } while (0)
+  // global element offset of tile row rho, 16-byte chunk ch (K offset added per load)
+  auto row_goff = [&](int rho, int ch) -> int {
+    if (rho < BM) {
+      const int r = min(rho, rows - 1);
+      return (a_rows ? a_rows[row0 + r] : r) * lda + ch * 8;
+    }
+    if (rho < BM + NB * BNB) return min(n0 + (rho - BM) % BNB, N - 1) * K + ch * 8;
+    return ch * 8;  // pad rows: any valid address (row 0 of the A tile)
+  };
+
+  constexpr int NRD = FM + NB * FN;   // fragment reads per slice
+  constexpr int NMF = NB * FN * FM;   // MFMAs per slice
+  if constexpr (PING) {
+    // Two groups of four waves, one wave of each per SIMD, offset by half a
+    // step: while one group runs its MFMAs the other reads its fragments from
+    // LDS and writes the next stage into LDS; then they swap at a barrier.
+    // Every wave runs the same loop -- a memory phase M(t), a barrier, a
+    // compute phase C(t), a barrier -- and the second group starts one
+    // barrier late, so its M(t) runs beside the first group's C(t).
+    //
+    // A step t covers K = 32 (two MFMA slices); an LDS stage holds K = 64
+    // (128-byte rows, so every global load fetches whole 128-byte lines: 8
+    // rows of 8 lanes per wavefront load, which the vector-memory path moves
+    // at nearly twice the rate of 16 rows of 64 bytes).  Chunk c of row r
+    // sits at c ^ ((r >> 1) & 7), so the 16 lanes an LDS cycle serves (16
+    // consecutive rows of one chunk, or 2 rows of 8 chunks) hit distinct
+    // banks.  Two LDS buffers, stage s in buffer s % 2.
+    //
+    // Tiles go global -> registers -> LDS.  M(t), t = 2s + h: read the
+    // fragments of step t (half h of stage s) and write half h of stage s+1
+    // (loaded two steps earlier into register set h).  C(t): the global
+    // loads of half h of stage s+2 (into set h, just written out), then the
+    // MFMAs of step t, so the vector-memory unit works through one group's
+    // loads while the LDS serves the other group.  Stage
+    // s+1's buffer last held stage s-1, read by both groups before the
+    // barrier that precedes the first write; all four writes of stage s+1
+    // land before the leading group's first read of it, two phases later.
+    constexpr int RW = kPingRowElems;
+    constexpr int PSTAGE = ROWS * RW;   // elements of one stage
+    constexpr int NI = ROWS / (8 * NW); // 8-row loads per wave per stage
+    constexpr int NH = NI / 2;          // ... per half stage
+    static_assert(NI % 2 == 0, "half stages");
+    const bool lag = wave >= NW / 2;
+    const int stages = K / RW;
+    int goff[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) goff[j] = row_goff(8 * (wave + NW * j) + (lane >> 3), lane & 7);
+    u32x4 ldr[2][NH];
+#define MOE_ISSUE(set_, stage_, half_)                                                  \
+  do {                                                                                  \
+    const int st_ = (stage_) < stages ? (stage_) : stages - 1;                          \
+    _Pragma("unroll") for (int jj = 0; jj < NH; ++jj) {                                 \
+      const int j_ = (half_) * NH + jj;                                                 \
+      const int r0_ = 8 * (wave + NW * j_);                                             \
+      const uint16_t* src_ = r0_ < BM ? Ab : (r0_ < BM + BNB ? B0b : (r0_ < BM + NB * BNB ? B1b : Ab)); \
+      ldr[set_][jj] = *reinterpret_cast<const u32x4*>(src_ + goff[j_] + st_ * RW);      \
+    }                                                                                   \
+  } while (0)
+#define MOE_STORE(set_, stage_, half_)                                                  \
+  do {                                                                                  \
+    uint16_t* base_ = smem + ((stage_) & 1) * PSTAGE;                                   \
+    _Pragma("unroll") for (int jj = 0; jj < NH; ++jj) {                                 \
+      const int j_ = (half_) * NH + jj;                                                 \
+      const int r0_ = 8 * (wave + NW * j_);                                             \
+      const int row_ = r0_ + (lane >> 3);                                               \
+      u32x4 v_ = ldr[set_][jj];                                                         \
+      if (MODE == kDown && r0_ >= BM && r0_ < BM + BNB) v_ = bf16x8_to_f16x8(v_);       \
+      *reinterpret_cast<u32x4*>(base_ + row_ * RW + (((lane & 7) ^ ((row_ >> 1) & 7)) << 3)) = v_; \
+    }                                                                                   \
+  } while (0)
+#define MOE_READ_FRAGS_P(set_, step_, ks_)                                              \
+  do {                                                                                  \
+    const uint16_t* sA_ = smem + (((step_) >> 1) & 1) * PSTAGE;                         \
+    const uint16_t* sB0_ = sA_ + BM * RW;                                               \
+    const uint16_t* sB1_ = sB0_ + BNB * RW;                                             \
+    const int c_ = ((step_) & 1) * 4 + (ks_) * 2 + fk;                                  \
+    _Pragma("unroll") for (int b = 0; b < FM; ++b) {                                    \
+      const int r = wm * WM + b * 32 + fr;                                              \
+      xa[set_][b] = *reinterpret_cast<const u32x4*>(sA_ + r * RW + ((c_ ^ ((r >> 1) & 7)) << 3)); \
+    }                                                                                   \
+    _Pragma("unroll") for (int a = 0; a < FN; ++a) {                                    \
+      const int r = wn * WN + a * 32 + fr;                                              \
+      wb0[set_][a] = *reinterpret_cast<const u32x4*>(sB0_ + r * RW + ((c_ ^ ((r >> 1) & 7)) << 3)); \
+      if constexpr (DUAL)                                                               \
+        wb1[set_][a] = *reinterpret_cast<const u32x4*>(sB1_ + r * RW + ((c_ ^ ((r >> 1) & 7)) << 3)); \
+    }                                                                                   \
+  } while (0)
+#define MOE_PP_STEP(tt_, h_)                                                            \
+  do {                                                                                  \
+    MOE_READ_FRAGS_P(0, (tt_), 0);                                                      \
+    MOE_READ_FRAGS_P(1, (tt_), 1);                                                      \
+    MOE_STORE(h_, ((tt_) >> 1) + 1, h_);                                                \
+    __builtin_amdgcn_sched_barrier(0);                                                  \
+    MOE_WAIT_LGKM0();                                                                   \
+    raw_barrier();                                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                  \
+    __builtin_amdgcn_s_setprio(1);                                                      \
+    MOE_ISSUE(h_, ((tt_) >> 1) + 2, h_);                                                \
+    MOE_MFMAS(0);                                                                       \
+    MOE_MFMAS(1);                                                                       \
+    __builtin_amdgcn_sched_group_barrier(0x020, NH, 3);                                 \
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NMF, 3);                            \
+    __builtin_amdgcn_s_setprio(0);                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                  \
+    raw_barrier();                                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                  \
+  } while (0)
+    MOE_ISSUE(0, 0, 0);
+    MOE_ISSUE(1, 0, 1);
+    MOE_STORE(0, 0, 0);
+    MOE_STORE(1, 0, 1);
+    MOE_ISSUE(0, 1, 0);
+    MOE_ISSUE(1, 1, 1);
+    MOE_WAIT_LGKM0();
+    raw_barrier();
+    if (lag) raw_barrier();
+    // two steps per stage (K is a multiple of 64), so register sets alternate statically
+    for (int t = 0; t < 2 * stages; t += 2) {
+      MOE_PP_STEP(t, 0);
+      MOE_PP_STEP(t + 1, 1);
+    }
+    if (!lag) raw_barrier();
+#undef MOE_PP_STEP
+#undef MOE_READ_FRAGS_P
+#undef MOE_STORE
+#undef MOE_ISSUE
+  } else {
+    // 4-wave blocks.  Tiles move from global memory straight into LDS with
+    // global_load_lds_dwordx4 (lane L of a wavefront writes 16 bytes at LDS
+    // base + 16 L), so no registers stage them.  A stage covers 32 K
+    // elements: rows [A tile | B0 tile | B1 tile | pad], each 64 bytes = four
+    // 16-byte chunks, chunk c of row r stored at c ^ ((r >> 2) & 3) so the 16
+    // rows one 16-lane phase of a fragment read touches fall in distinct
+    // banks; the swizzle is applied on the global side by choosing the chunk
+    // each lane fetches.  NS stages form a ring: NS - 2 stages stay in flight
+    // ahead of the one being multiplied.
+    //
+    // Per step (one stage, two K=16 MFMA slices): the second slice's
+    // fragments are read, the first slice's MFMAs run, the wave waits for
+    // its loads of the next stage and meets the others at a barrier, the
+    // loads NS-1 stages ahead are issued into the stage freed one step ago,
+    // the next step's first-slice fragments are read, and the second slice's
+    // MFMAs run -- so fragment reads and loads always overlap queued MFMAs.
+    constexpr int STAGE = ROWS * kSK;      // elements of one stage
+    constexpr int NL = ROWS / (16 * NW);   // 16-row loads per wave per stage
+    static_assert(NS >= 3 && NL * (NS - 2) <= 63, "pipeline depth");
+    // load i of this wave fills stage rows 16*(wave + NW i) .. +16; lane -> (row, chunk)
+    int goff[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int rho = 16 * (wave + NW * i) + (lane >> 2);
+      goff[i] = row_goff(rho, (lane & 3) ^ ((rho >> 2) & 3));
+    }
+    const int steps = K / kSK;
+#define MOE_LOAD_STAGE(step_)                                                           \
+  do {                                                                                  \
+    const int st_ = (step_) < steps ? (step_) : steps - 1;                              \
+    uint16_t* base_ = smem + ((step_) % NS) * STAGE;                                    \
+    _Pragma("unroll") for (int i = 0; i < NL; ++i) {                                    \
+      const int r0_ = 16 * (wave + NW * i);                                             \
+      const uint16_t* src_ = r0_ < BM ? Ab : (r0_ < BM + BNB ? B0b : (r0_ < BM + NB * BNB ? B1b : Ab)); \
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src_ + goff[i] + st_ * kSK),         \
+                                       (lds_ptr_t)(base_ + r0_ * kSK), 16, 0, 0);       \
+    }                                                                                   \
+  } while (0)
+    // fragments of slice ks (0/1) of the stage holding `step_` into set `set_`
 #define MOE_READ_FRAGS(set_, step_, ks_)                                                \
   do {                                                                                  \
     const uint16_t* sA_ = smem + ((step_) % NS) * STAGE;                                \
@@ -263,56 +405,44 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
         wb1[set_][a] = *reinterpret_cast<const u32x4*>(sB1_ + r * kSK + ((c_ ^ ((r >> 2) & 3)) << 3)); \
     }                                                                                   \
   } while (0)
-#define MOE_MFMAS(set_)                                                                 \
-  do {                                                                                  \
-    _Pragma("unroll") for (int a = 0; a < FN; ++a) {                                    \
-      const u32x4 w0_ = MODE == kDown ? bf16x8_to_f16x8(wb0[set_][a]) : wb0[set_][a];    \
-      _Pragma("unroll") for (int b = 0; b < FM; ++b) {                                  \
-        acc0[a][b] = mfma32<MODE>(w0_, xa[set_][b], acc0[a][b]);                        \
-        if constexpr (DUAL) acc1[a][b] = mfma32<MODE>(wb1[set_][a], xa[set_][b], acc1[a][b]); \
-      }                                                                                 \
-    }                                                                                   \
-  } while (0)
-
-  // prologue: stages 0 .. NS-2 in flight; wait for stage 0; first slice of step 0
+    // prologue: stages 0 .. NS-2 in flight; wait for stage 0; first slice of step 0
 #pragma unroll
-  for (int s0 = 0; s0 < NS - 1; ++s0) MOE_LOAD_STAGE(s0);
-  MOE_WAIT_VMCNT(NL * (NS - 2));
-  raw_barrier();
-  MOE_READ_FRAGS(0, 0, 0);
-  constexpr int NRD = FM + NB * FN;   // fragment reads per slice
-  constexpr int NMF = NB * FN * FM;   // MFMAs per slice
-  for (int t = 0; t < steps; ++t) {
-    // region 1: slice-0 MFMAs with the slice-1 fragment reads between them
-    MOE_READ_FRAGS(1, t, 1);
-    MOE_MFMAS(0);
+    for (int s0 = 0; s0 < NS - 1; ++s0) MOE_LOAD_STAGE(s0);
+    MOE_WAIT_VMCNT(NL * (NS - 2));
+    raw_barrier();
+    MOE_READ_FRAGS(0, 0, 0);
+    for (int t = 0; t < steps; ++t) {
+      // region 1: slice-0 MFMAs with the slice-1 fragment reads between them
+      MOE_READ_FRAGS(1, t, 1);
+      MOE_MFMAS(0);
 #pragma unroll
-    for (int q = 0; q < NMF; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);            // MFMA
-      if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // DS read
+      for (int q = 0; q < NMF; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);            // MFMA
+        if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // DS read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      MOE_WAIT_VMCNT(NL * (NS - 3));  // this wave's loads of step t+1 have landed
+      raw_barrier();                  // ... and every wave's; step t-1's stage is free
+      __builtin_amdgcn_sched_barrier(0);
+      // region 2: slice-1 MFMAs with the loads NS-1 steps ahead and the next
+      // step's slice-0 fragment reads between them (on the last step that read
+      // is of a stale stage and unused)
+      MOE_LOAD_STAGE(t + NS - 1);
+      MOE_READ_FRAGS(0, t + 1, 0);
+      MOE_MFMAS(1);
+#pragma unroll
+      for (int q = 0; q < NMF; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);             // MFMA
+        if (q < NL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 2);   // VMEM load
+        if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);  // DS read
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    MOE_WAIT_VMCNT(NL * (NS - 3));  // this wave's loads of step t+1 have landed
-    raw_barrier();                  // ... and every wave's; step t-1's stage is free
-    __builtin_amdgcn_sched_barrier(0);
-    // region 2: slice-1 MFMAs with the loads NS-1 steps ahead and the next
-    // step's slice-0 fragment reads between them (on the last step that read
-    // is of a stale stage and unused)
-    MOE_LOAD_STAGE(t + NS - 1);
-    MOE_READ_FRAGS(0, t + 1, 0);
-    MOE_MFMAS(1);
-#pragma unroll
-    for (int q = 0; q < NMF; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);             // MFMA
-      if (q < NL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 2);   // VMEM load
-      if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);  // DS read
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // drain the clamped tail loads before the block ends
-#undef MOE_LOAD_STAGE
 #undef MOE_READ_FRAGS
+#undef MOE_LOAD_STAGE
+  }
 #undef MOE_MFMAS
+  __builtin_amdgcn_s_waitcnt(0);  // drain the clamped tail loads before the block ends
 
   // epilogue: accumulator q of fragment (a, b) is output column
   // n = a*32 + 8*(q/4) + 4*(lane/32) + q%4 of token row m = b*32 + lane%32
@@ -370,7 +500,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
 // fp32 grouped GEMM: 32x32 output tile (per B matrix), 2x2 outputs per thread,
 // K step 16.  Used by fp32 layers, whose sizes make it latency-bound.
 template <bool DUAL>
-__global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, int lda,
+__global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A,
+                                                  const int32_t* __restrict__ a_rows, int lda,
                                                   const float* __restrict__ B0,
                                                   const float* __restrict__ B1,
                                                   long long strideB, int N, int K,
@@ -407,7 +538,8 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, i
       const int kk = k0 + k;
       const int ar = min(r, rows - 1);
       const int bn = min(n0 + r, N - 1);
-      sA[r][k] = kk < K ? A[(size_t)(row0 + ar) * lda + kk] : 0.f;
+      const size_t arow = a_rows ? (size_t)a_rows[row0 + ar] : (size_t)(row0 + ar);
+      sA[r][k] = kk < K ? A[arow * lda + kk] : 0.f;
       sB0[r][k] = kk < K ? B0b[(size_t)bn * K + kk] : 0.f;
       if constexpr (DUAL) sB1[r][k] = kk < K ? B1b[(size_t)bn * K + kk] : 0.f;
     }
@@ -448,7 +580,8 @@ inline int grid_for(int mslots, int ntiles) {
 // Launches k_gemm_mfma<BM, BNB, MODE>, raising the block's LDS limit when the
 // two stages exceed the default 64 KiB.
 template <int BM, int BNB, int MODE, int NS, int NW>
-hipError_t launch_mfma(const void* A, int lda, const void* B0, const void* B1, int N, int K,
+hipError_t launch_mfma(const void* A, const int32_t* a_rows, int lda, const void* B0,
+                       const void* B1, int N, int K,
                        void* out, int ldo, const float* bias, const MTile* sched,
                        const int32_t* count, int mslots, int static_rows, uint32_t* flags,
                        hipStream_t st) {
@@ -465,8 +598,9 @@ hipError_t launch_mfma(const void* A, int lda, const void* B0, const void* B1, i
   const int ntiles = (N + BNB - 1) / BNB;
   const dim3 grid(grid_for(mslots, ntiles));
   hipLaunchKernelGGL((k_gemm_mfma<BM, BNB, MODE, NS, NW>), grid, dim3(64 * NW), lds, st,
-                     static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B0),
-                     static_cast<const uint16_t*>(B1), (long long)N * K, N, K, out, ldo, bias,
+                     static_cast<const uint16_t*>(A), a_rows, lda,
+                     static_cast<const uint16_t*>(B0), static_cast<const uint16_t*>(B1),
+                     (long long)N * K, N, K, out, ldo, bias,
                      sched, count, mslots, ntiles, static_rows, flags);
   return hipGetLastError();
 }
@@ -478,8 +612,9 @@ int gemm_tile_rows(int dtype, int bm_hint) {
   return bm_hint >= 256 ? 256 : (bm_hint >= 128 ? 128 : 32);
 }
 
-hipError_t launch_gemm_gateup(int dtype, int bm, const void* A, int lda, const void* Bg,
-                              const void* Bu, int N, int K, void* h, int ldh, const MTile* sched,
+hipError_t launch_gemm_gateup(int dtype, int bm, const void* A, const int32_t* a_rows, int lda,
+                              const void* Bg, const void* Bu, int N, int K, void* h, int ldh,
+                              const MTile* sched,
                               const int32_t* count, int max_tiles, int static_rows,
                               uint32_t* flags, hipStream_t st) {
   const long long strideB = (long long)N * K;
@@ -488,7 +623,7 @@ hipError_t launch_gemm_gateup(int dtype, int bm, const void* A, int lda, const v
     const int ntiles = (N + 31) / 32;
     if (mslots == 0) return hipSuccess;
     hipLaunchKernelGGL(k_gemm_f32<true>, dim3(grid_for(mslots, ntiles)), dim3(256), 0, st,
-                       static_cast<const float*>(A), lda, static_cast<const float*>(Bg),
+                       static_cast<const float*>(A), a_rows, lda, static_cast<const float*>(Bg),
                        static_cast<const float*>(Bu), strideB, N, K, static_cast<float*>(h), ldh,
                        nullptr, sched, count, mslots, ntiles, static_rows);
     return hipGetLastError();
@@ -496,12 +631,12 @@ hipError_t launch_gemm_gateup(int dtype, int bm, const void* A, int lda, const v
   const int mslots = sched ? max_tiles : (static_rows + bm - 1) / bm;
   if (mslots == 0) return hipSuccess;
   if (bm == 256)
-    return launch_mfma<256, 128, kGateUp, 5, 8>(A, lda, Bg, Bu, N, K, h, ldh, nullptr, sched, count,
+    return launch_mfma<256, 128, kGateUp, 2, 8>(A, a_rows, lda, Bg, Bu, N, K, h, ldh, nullptr, sched, count,
                                           mslots, static_rows, flags, st);
   if (bm == 128)
-    return launch_mfma<128, 128, kGateUp, 4, 8>(A, lda, Bg, Bu, N, K, h, ldh, nullptr, sched, count,
+    return launch_mfma<128, 128, kGateUp, 2, 8>(A, a_rows, lda, Bg, Bu, N, K, h, ldh, nullptr, sched, count,
                                           mslots, static_rows, flags, st);
-  return launch_mfma<32, 128, kGateUp, 4, 4>(A, lda, Bg, Bu, N, K, h, ldh, nullptr, sched, count,
+  return launch_mfma<32, 128, kGateUp, 4, 4>(A, a_rows, lda, Bg, Bu, N, K, h, ldh, nullptr, sched, count,
                                        mslots, static_rows, flags, st);
 }
 
@@ -515,7 +650,7 @@ hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int 
     const int ntiles = (N + 31) / 32;
     if (mslots == 0) return hipSuccess;
     hipLaunchKernelGGL(k_gemm_f32<false>, dim3(grid_for(mslots, ntiles)), dim3(256), 0, st,
-                       static_cast<const float*>(A), lda, static_cast<const float*>(B), nullptr,
+                       static_cast<const float*>(A), nullptr, lda, static_cast<const float*>(B), nullptr,
                        strideB, N, K, Y, ldy, bias, sched, count, mslots, ntiles, static_rows);
     return hipGetLastError();
   }
@@ -523,18 +658,18 @@ hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int 
   if (mslots == 0) return hipSuccess;
   if (a_is_h) {
     if (bm == 256)
-      return launch_mfma<256, 256, kDown, 5, 8>(A, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
+      return launch_mfma<256, 256, kDown, 2, 8>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
                                           mslots, static_rows, nullptr, st);
     if (bm == 128)
-      return launch_mfma<128, 128, kDown, 4, 8>(A, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
+      return launch_mfma<128, 128, kDown, 2, 8>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
                                           mslots, static_rows, nullptr, st);
-    return launch_mfma<32, 128, kDown, 4, 4>(A, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
+    return launch_mfma<32, 128, kDown, 4, 4>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
                                        mslots, static_rows, nullptr, st);
   }
   if (bm == 128)
-    return launch_mfma<128, 128, kPlain, 4, 8>(A, lda, B, nullptr, N, K, Y, ldy, bias, sched, count,
+    return launch_mfma<128, 128, kPlain, 2, 8>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, bias, sched, count,
                                          mslots, static_rows, nullptr, st);
-  return launch_mfma<32, 128, kPlain, 4, 4>(A, lda, B, nullptr, N, K, Y, ldy, bias, sched, count,
+  return launch_mfma<32, 128, kPlain, 4, 4>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, bias, sched, count,
                                       mslots, static_rows, nullptr, st);
 }
 

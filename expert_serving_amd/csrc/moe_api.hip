@@ -49,8 +49,15 @@ moe_status check_shape(const moe_shape* s) {
   const int mult = s->act_dtype == MOE_BF16 ? 64 : 4;
   if (s->hidden % mult || s->intermediate % mult || s->shared_intermediate % mult)
     return MOE_ERR_UNSUPPORTED;
-  // slot and row indices are int32
+  // slot and row indices are int32, and so are the GEMM's element offsets
+  // inside x (gathered rows) and inside one expert's weight matrix
   if ((long long)s->num_tokens * s->top_k > (long long)INT_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  const long long H = s->hidden;
+  if ((long long)s->num_tokens * H > (long long)INT_MAX) return MOE_ERR_UNSUPPORTED;
+  if ((long long)s->intermediate * H > (long long)INT_MAX ||
+      (long long)s->shared_intermediate * H > (long long)INT_MAX ||
+      (long long)s->num_experts * H > (long long)INT_MAX)
+    return MOE_ERR_UNSUPPORTED;
   if ((long long)s->num_tokens * s->num_experts > (long long)INT_MAX) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -148,7 +155,6 @@ WsLayout plan_workspace(const moe_shape& s) {
   w.sched_big = take((size_t)w.max_tiles_big * sizeof(MTile));
   w.sched_small = take((size_t)w.max_tiles_small * sizeof(MTile));
   w.sched_count = take(16);
-  w.x_perm = take(slots * H * eb);
   w.h = take(slots * I * eb);
   w.y = take(slots * H * 4);
   w.hs = take(T * Is * eb);
@@ -162,14 +168,22 @@ namespace {
 
 moe_status run_router(const moe_shape& s, const void* x, const void* w_router, const float* bias,
                       float* logits, hipStream_t st) {
-  const int bm = s.num_tokens >= 128 ? 128 : 32;
+  if (router_skinny_supported(s)) {
+    MOE_HIP(launch_router_skinny(s, x, w_router, bias, logits, st));
+    return MOE_OK;
+  }
+  // 128-row tiles only when they alone give every compute unit a block
+  const int tiles128 = (s.num_tokens + 127) / 128 * ((s.num_experts + 127) / 128);
+  const int bm = tiles128 >= 256 ? 128 : 32;
   MOE_HIP(launch_gemm_plain(s.act_dtype, bm, false, x, s.hidden, w_router, s.num_experts, s.hidden,
                             bias, logits, s.num_experts, nullptr, nullptr, 0, s.num_tokens, st));
   return MOE_OK;
 }
 
-moe_status run_ffn(const moe_shape& s, const void* x_perm, const int32_t* offsets,
-                   const void* w_gate, const void* w_up, const void* w_down, float* y, void* ws,
+// a_rows (nullable): rows of x_perm are x[a_rows[r]] (gather fused into the GEMM)
+moe_status run_ffn(const moe_shape& s, const void* x_perm, const int32_t* a_rows,
+                   const int32_t* offsets, const void* w_gate, const void* w_up,
+                   const void* w_down, float* y, void* ws,
                    const WsLayout& L, hipStream_t st, const moe_debug* dbg = nullptr) {
   const GemmPlan gp = choose_gemm_plan(s);
   const int E = s.num_experts, H = s.hidden, I = s.intermediate;
@@ -182,11 +196,11 @@ moe_status run_ffn(const moe_shape& s, const void* x_perm, const int32_t* offset
   void* h = at<void>(ws, L.h);
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATE_UP, true, st));
   if (gp.has_big())
-    MOE_HIP(launch_gemm_gateup(s.act_dtype, gp.bm_big, x_perm, H, w_gate, w_up, I, H, h, I, sb,
-                               cnt, L.max_tiles_big, 0, flags, st));
+    MOE_HIP(launch_gemm_gateup(s.act_dtype, gp.bm_big, x_perm, a_rows, H, w_gate, w_up, I, H, h,
+                               I, sb, cnt, L.max_tiles_big, 0, flags, st));
   if (gp.has_small())
-    MOE_HIP(launch_gemm_gateup(s.act_dtype, gp.bm_small, x_perm, H, w_gate, w_up, I, H, h, I, ss,
-                               cnt + 1, L.max_tiles_small, 0, flags, st));
+    MOE_HIP(launch_gemm_gateup(s.act_dtype, gp.bm_small, x_perm, a_rows, H, w_gate, w_up, I, H,
+                               h, I, ss, cnt + 1, L.max_tiles_small, 0, flags, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATE_UP, false, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_DOWN, true, st));
   if (gp.has_big())
@@ -205,8 +219,8 @@ moe_status run_shared(const moe_shape& s, const void* x, const void* wsg, const 
   const int bm = s.act_dtype == MOE_F32 ? 32 : (T >= 2048 ? 256 : (T >= 128 ? 128 : 32));
   void* hs = at<void>(ws, L.hs);
   float* ys = at<float>(ws, L.ys);
-  MOE_HIP(launch_gemm_gateup(s.act_dtype, bm, x, H, wsg, wsu, Is, H, hs, Is, nullptr, nullptr, 0,
-                             T, at<uint32_t>(ws, L.flags), st));
+  MOE_HIP(launch_gemm_gateup(s.act_dtype, bm, x, nullptr, H, wsg, wsu, Is, H, hs, Is, nullptr,
+                             nullptr, 0, T, at<uint32_t>(ws, L.flags), st));
   MOE_HIP(launch_gemm_plain(s.act_dtype, bm, true, hs, Is, wsd, H, Is, nullptr, ys, H, nullptr,
                             nullptr, 0, T, st));
   return MOE_OK;
@@ -308,7 +322,7 @@ moe_status moe_grouped_ffn(const moe_shape* shape, const void* x_perm,
   if (s.num_tokens == 0) return MOE_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   MOE_HIP(launch_clear_flags(at<uint32_t>(ws, L.flags), st));
-  return run_ffn(s, x_perm, expert_offsets, w_gate, w_up, w_down, y_perm, ws, L, st);
+  return run_ffn(s, x_perm, nullptr, expert_offsets, w_gate, w_up, w_down, y_perm, ws, L, st);
 }
 
 moe_status moe_combine(const moe_shape* shape, const float* y_perm, const int32_t* row_of_slot,
@@ -371,7 +385,6 @@ moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* 
   int32_t* nd = (dbg && dbg->num_dropped) ? dbg->num_dropped : at<int32_t>(ws, L.num_dropped);
   uint32_t* flags = at<uint32_t>(ws, L.flags);
   int32_t* row_token = at<int32_t>(ws, L.row_token);
-  void* x_perm = at<void>(ws, L.x_perm);
   float* y = at<float>(ws, L.y);
 
   MOE_HIP(launch_clear_flags(flags, st));
@@ -385,10 +398,10 @@ moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* 
   MOE_HIP(launch_dispatch(s, ids, counts, offsets, ros, row_token, nd,
                           at<int32_t>(ws, L.tile_counts), L.n_dispatch_tiles, flags, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_DISPATCH, false, st));
+  // S6 gather: fused into the gate/up GEMM's tile loads (rows x[row_token[r]])
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATHER, true, st));
-  MOE_HIP(launch_gather(s, x, row_token, offsets, x_perm, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATHER, false, st));
-  MOE_TRY(run_ffn(s, x_perm, offsets, w_gate, w_up, w_down, y, ws, L, st, dbg));
+  MOE_TRY(run_ffn(s, x, row_token, offsets, w_gate, w_up, w_down, y, ws, L, st, dbg));
   const float* ys = nullptr;
   MOE_HIP(stage_mark(dbg, MOE_STAGE_SHARED, true, st));
   if (s.shared_intermediate > 0) {

@@ -11,7 +11,7 @@ namespace moe {
 
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 16;
-constexpr int kDispatchTileSlots = 2048;  // slots per dispatch tile (one block)
+constexpr int kDispatchTileSlots = 1024;  // slots per dispatch tile (one block)
 
 // One row-tile of the grouped GEMM: `rows` (1..BM) consecutive permuted rows
 // starting at row0, all belonging to `expert`.
@@ -25,7 +25,7 @@ struct MTile {
 // Byte offsets of every region inside the caller's workspace.
 struct WsLayout {
   size_t flags, logits, ids, gates, counts, offsets, tile_counts, row_of_slot, row_token,
-      num_dropped, sched_big, sched_small, sched_count, x_perm, h, y, hs, ys, total;
+      num_dropped, sched_big, sched_small, sched_count, h, y, hs, ys, total;
   int n_dispatch_tiles;
   int max_tiles_big, max_tiles_small;
 };
@@ -54,6 +54,12 @@ hipError_t launch_route_topk(const moe_shape& s, const float* logits, const int3
 
 hipError_t launch_logistic(const float* x, float* y, long long n, hipStream_t st);
 
+// S1 without MFMA for bf16 layers with at most kRouterSkinnyMaxExperts experts
+constexpr int kRouterSkinnyMaxExperts = 32;
+bool router_skinny_supported(const moe_shape& s);
+hipError_t launch_router_skinny(const moe_shape& s, const void* x, const void* w_router,
+                                const float* bias, float* logits, hipStream_t st);
+
 hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, int32_t* counts,
                            int32_t* offsets, int32_t* row_of_slot, int32_t* row_token,
                            int32_t* num_dropped, int32_t* tile_counts, int n_tiles,
@@ -71,10 +77,12 @@ hipError_t launch_build_schedule(const int32_t* offsets, int E, const GemmPlan& 
 // the rows [0, static_rows) form one group (expert 0) tiled statically.
 // gate/up + SwiGLU: h[r][n] = silu(A[r].Bg[e][n]) * (A[r].Bu[e][n]); for bf16
 // layers h is fp16 and values outside fp16's range set MOE_FLAG_H_RANGE
-hipError_t launch_gemm_gateup(int dtype, int bm, const void* A, int lda, const void* Bg,
-                              const void* Bu, int N, int K, void* h, int ldh, const MTile* sched,
-                              const int32_t* count, int max_tiles, int static_rows,
-                              uint32_t* flags, hipStream_t st);
+// a_rows (nullable): A row r is A[a_rows[r]] (the dispatch gather fused into
+// the tile loads); else A is contiguous.
+hipError_t launch_gemm_gateup(int dtype, int bm, const void* A, const int32_t* a_rows, int lda,
+                              const void* Bg, const void* Bu, int N, int K, void* h, int ldh,
+                              const MTile* sched, const int32_t* count, int max_tiles,
+                              int static_rows, uint32_t* flags, hipStream_t st);
 // plain: Y[r][n] = A[r].B[e][n] (+ bias[n]), fp32 out.  a_is_h: A is the
 // fp16 h of a bf16 layer (down projection), B is converted to fp16 on load.
 hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int lda,

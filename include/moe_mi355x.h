@@ -88,13 +88,15 @@ typedef struct {
   int32_t act_dtype;           /* moe_dtype of x and of every weight                        */
   int32_t out_dtype;           /* moe_dtype of the layer output                             */
 } moe_shape;
+/* Element offsets are int32 inside the kernels: T*top_k <= 2^30 and each of
+ * T*H, E*H, I*H and Is*H <= 2^31-1, else MOE_ERR_UNSUPPORTED. */
 
 /* Stages of moe_layer_forward, for the timing events of moe_debug. */
 typedef enum {
   MOE_STAGE_ROUTER = 0,   /* S1 router logits                         */
   MOE_STAGE_ROUTE = 1,    /* S2 scoring, top-k, gates                 */
   MOE_STAGE_DISPATCH = 2, /* S3-S5 histogram, capacity, permutation   */
-  MOE_STAGE_GATHER = 3,   /* S6 x_perm gather                         */
+  MOE_STAGE_GATHER = 3,   /* S6 x_perm gather (fused into S7: empty)  */
   MOE_STAGE_GATE_UP = 4,  /* S7 grouped gate/up GEMM + SwiGLU         */
   MOE_STAGE_DOWN = 5,     /* S8 grouped down GEMM                     */
   MOE_STAGE_SHARED = 6,   /* S9 shared expert (both GEMMs)            */

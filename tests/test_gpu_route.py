@@ -88,19 +88,40 @@ def test_route_parity_given_logits(name, T, E, k, o):
     assert flags == (abi.MOE_FLAG_BAD_K if o.get("bad_k") else 0)
 
 
-def test_router_logits_parity_bf16_and_fp32():
-    for dt, (T, H, E) in ((W.DT_BF16, (1000, 4096, 8)), (W.DT_BF16, (777, 7168, 256)), (W.DT_F32, (300, 512, 8)),
-                          (W.DT_BF16, (130, 2048, 5))):
-        say(f"router logits dtype={dt} T={T} H={H} E={E}")
-        x = W.normal((T, H), 1.0, dt, dev(), 11)
-        wr = W.normal((E, H), H ** -0.5, dt, dev(), 12)
-        b = torch.from_numpy(W.log_zipf_bias(E, 1.1)).to(dev())
-        shape = abi.make_shape(num_tokens=T, hidden=H, num_experts=E, intermediate=64, top_k=min(2, E),
-                               act_dtype=dt)
-        ws = workspace(shape)
-        lo = torch.empty(T, E, dtype=torch.float32, device=dev())
-        ids = i32(T * shape.top_k)
-        gates = f32(T * shape.top_k)
-        abi.moe_route_topk(shape, x, wr, b, None, lo, None, ids, gates, ws)
-        ref = oracle.router_logits(host(x), host(wr), b.cpu().numpy())
-        assert_close_rms(lo.cpu().numpy(), ref, 1e-5, "logits")
+# (dtype, T, H, E, bias): bf16 layers with E <= 32 take the vector-ALU router
+# (one token per block below 1024 tokens, several above), the rest the MFMA
+# GEMM; ragged token counts, one-chunk rows (H = 64) and E below the
+# kernel's expert bound are all covered
+ROUTER_CASES = [
+    (W.DT_BF16, 1000, 4096, 8, True),
+    (W.DT_BF16, 1024, 4096, 8, True),
+    (W.DT_BF16, 4099, 4096, 8, False),
+    (W.DT_BF16, 1, 4096, 8, True),
+    (W.DT_BF16, 130, 2048, 5, True),
+    (W.DT_BF16, 1027, 2048, 16, True),
+    (W.DT_BF16, 70, 1024, 13, False),
+    (W.DT_BF16, 2050, 1024, 32, True),
+    (W.DT_BF16, 3, 64, 24, True),
+    (W.DT_BF16, 257, 2048, 33, True),
+    (W.DT_BF16, 777, 7168, 256, True),
+    (W.DT_BF16, 4096, 2048, 128, True),
+    (W.DT_F32, 300, 512, 8, True),
+]
+
+
+@pytest.mark.parametrize("dt,T,H,E,with_bias", ROUTER_CASES,
+                         ids=[f"{'bf16' if c[0] == W.DT_BF16 else 'f32'}-T{c[1]}-H{c[2]}-E{c[3]}" for c in ROUTER_CASES])
+def test_router_logits_parity(dt, T, H, E, with_bias):
+    say(f"router logits dtype={dt} T={T} H={H} E={E} bias={with_bias}")
+    x = W.normal((T, H), 1.0, dt, dev(), 11)
+    wr = W.normal((E, H), H ** -0.5, dt, dev(), 12)
+    b = torch.from_numpy(W.log_zipf_bias(E, 1.1)).to(dev()) if with_bias else None
+    shape = abi.make_shape(num_tokens=T, hidden=H, num_experts=E, intermediate=64, top_k=min(2, E),
+                           act_dtype=dt)
+    ws = workspace(shape)
+    lo = torch.empty(T, E, dtype=torch.float32, device=dev())
+    ids = i32(T * shape.top_k)
+    gates = f32(T * shape.top_k)
+    abi.moe_route_topk(shape, x, wr, b, None, lo, None, ids, gates, ws)
+    ref = oracle.router_logits(host(x), host(wr), None if b is None else b.cpu().numpy())
+    assert_close_rms(lo.cpu().numpy(), ref, 1e-5, "logits")
