@@ -164,7 +164,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
   // 8-wave blocks: register-staged ping-pong over two LDS stages; 4-wave
   // blocks: direct-to-LDS loads over an NS-stage ring
   constexpr bool PING = NW == 8;
-  constexpr bool CVT_ON_READ = MODE == kDown && !PING;  // down weights bf16 -> fp16 per read
+  // down weights are converted to fp16 once when staged through registers
+  // (8-wave blocks), else on every fragment read
+  constexpr bool CVT_ON_READ = MODE == kDown && !PING;
   static_assert(BM % 32 == 0 && BNB % 32 == 0 && FM >= 1 && FN >= 1, "tile shape");
   static_assert(!PING || NS == 2, "ping-pong uses two LDS stages");
 
@@ -264,16 +266,33 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
     constexpr int NI = ROWS / (8 * NW); // 8-row loads per wave per stage
     constexpr int NH = NI / 2;          // ... per half stage
     static_assert(NI % 2 == 0, "half stages");
+#define MOE_READ_FRAGS_P(set_, step_, ks_)                                              \
+  do {                                                                                  \
+    const uint16_t* sA_ = smem + (((step_) >> 1) & 1) * PSTAGE;                         \
+    const uint16_t* sB0_ = sA_ + BM * RW;                                               \
+    const uint16_t* sB1_ = sB0_ + BNB * RW;                                             \
+    const int c_ = ((step_) & 1) * 4 + (ks_) * 2 + fk;                                  \
+    _Pragma("unroll") for (int b = 0; b < FM; ++b) {                                    \
+      const int r = wm * WM + b * 32 + fr;                                              \
+      xa[set_][b] = *reinterpret_cast<const u32x4*>(sA_ + r * RW + ((c_ ^ ((r >> 1) & 7)) << 3)); \
+    }                                                                                   \
+    _Pragma("unroll") for (int a = 0; a < FN; ++a) {                                    \
+      const int r = wn * WN + a * 32 + fr;                                              \
+      wb0[set_][a] = *reinterpret_cast<const u32x4*>(sB0_ + r * RW + ((c_ ^ ((r >> 1) & 7)) << 3)); \
+      if constexpr (DUAL)                                                               \
+        wb1[set_][a] = *reinterpret_cast<const u32x4*>(sB1_ + r * RW + ((c_ ^ ((r >> 1) & 7)) << 3)); \
+    }                                                                                   \
+  } while (0)
     const bool lag = wave >= NW / 2;
     const int stages = K / RW;
     int goff[NI];
 #pragma unroll
     for (int j = 0; j < NI; ++j) goff[j] = row_goff(8 * (wave + NW * j) + (lane >> 3), lane & 7);
     u32x4 ldr[2][NH];
-#define MOE_ISSUE(set_, stage_, half_)                                                  \
+#define MOE_ISSUE(set_, stage_, half_, jj0_, jj1_)                                      \
   do {                                                                                  \
     const int st_ = (stage_) < stages ? (stage_) : stages - 1;                          \
-    _Pragma("unroll") for (int jj = 0; jj < NH; ++jj) {                                 \
+    _Pragma("unroll") for (int jj = (jj0_); jj < (jj1_); ++jj) {                        \
       const int j_ = (half_) * NH + jj;                                                 \
       const int r0_ = 8 * (wave + NW * j_);                                             \
       const uint16_t* src_ = r0_ < BM ? Ab : (r0_ < BM + BNB ? B0b : (r0_ < BM + NB * BNB ? B1b : Ab)); \
@@ -292,23 +311,6 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
       *reinterpret_cast<u32x4*>(base_ + row_ * RW + (((lane & 7) ^ ((row_ >> 1) & 7)) << 3)) = v_; \
     }                                                                                   \
   } while (0)
-#define MOE_READ_FRAGS_P(set_, step_, ks_)                                              \
-  do {                                                                                  \
-    const uint16_t* sA_ = smem + (((step_) >> 1) & 1) * PSTAGE;                         \
-    const uint16_t* sB0_ = sA_ + BM * RW;                                               \
-    const uint16_t* sB1_ = sB0_ + BNB * RW;                                             \
-    const int c_ = ((step_) & 1) * 4 + (ks_) * 2 + fk;                                  \
-    _Pragma("unroll") for (int b = 0; b < FM; ++b) {                                    \
-      const int r = wm * WM + b * 32 + fr;                                              \
-      xa[set_][b] = *reinterpret_cast<const u32x4*>(sA_ + r * RW + ((c_ ^ ((r >> 1) & 7)) << 3)); \
-    }                                                                                   \
-    _Pragma("unroll") for (int a = 0; a < FN; ++a) {                                    \
-      const int r = wn * WN + a * 32 + fr;                                              \
-      wb0[set_][a] = *reinterpret_cast<const u32x4*>(sB0_ + r * RW + ((c_ ^ ((r >> 1) & 7)) << 3)); \
-      if constexpr (DUAL)                                                               \
-        wb1[set_][a] = *reinterpret_cast<const u32x4*>(sB1_ + r * RW + ((c_ ^ ((r >> 1) & 7)) << 3)); \
-    }                                                                                   \
-  } while (0)
 #define MOE_PP_STEP(tt_, h_)                                                            \
   do {                                                                                  \
     MOE_READ_FRAGS_P(0, (tt_), 0);                                                      \
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
     raw_barrier();                                                                      \
     __builtin_amdgcn_sched_barrier(0);                                                  \
     __builtin_amdgcn_s_setprio(1);                                                      \
-    MOE_ISSUE(h_, ((tt_) >> 1) + 2, h_);                                                \
+    MOE_ISSUE(h_, ((tt_) >> 1) + 2, h_, 0, NH);                                         \
     MOE_MFMAS(0);                                                                       \
     MOE_MFMAS(1);                                                                       \
     __builtin_amdgcn_sched_group_barrier(0x020, NH, 3);                                 \
@@ -329,12 +331,12 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
     raw_barrier();                                                                      \
     __builtin_amdgcn_sched_barrier(0);                                                  \
   } while (0)
-    MOE_ISSUE(0, 0, 0);
-    MOE_ISSUE(1, 0, 1);
+    MOE_ISSUE(0, 0, 0, 0, NH);
+    MOE_ISSUE(1, 0, 1, 0, NH);
     MOE_STORE(0, 0, 0);
     MOE_STORE(1, 0, 1);
-    MOE_ISSUE(0, 1, 0);
-    MOE_ISSUE(1, 1, 1);
+    MOE_ISSUE(0, 1, 0, 0, NH);
+    MOE_ISSUE(1, 1, 1, 0, NH);
     MOE_WAIT_LGKM0();
     raw_barrier();
     if (lag) raw_barrier();
@@ -345,9 +347,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
     }
     if (!lag) raw_barrier();
 #undef MOE_PP_STEP
-#undef MOE_READ_FRAGS_P
 #undef MOE_STORE
 #undef MOE_ISSUE
+#undef MOE_READ_FRAGS_P
   } else {
     // 4-wave blocks.  Tiles move from global memory straight into LDS with
     // global_load_lds_dwordx4 (lane L of a wavefront writes 16 bytes at LDS
@@ -663,6 +665,11 @@ hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int 
     if (bm == 128)
       return launch_mfma<128, 128, kDown, 2, 8>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
                                           mslots, static_rows, nullptr, st);
+    // few blocks (decode-sized layers): a deeper ring keeps more weight bytes
+    // in flight per compute unit
+    if ((long long)mslots * ((N + 127) / 128) <= 1024)
+      return launch_mfma<32, 128, kDown, 6, 4>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sched,
+                                               count, mslots, static_rows, nullptr, st);
     return launch_mfma<32, 128, kDown, 4, 4>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
                                        mslots, static_rows, nullptr, st);
   }
