@@ -1,6 +1,8 @@
 // Measured ceilings of the GPU the library runs on: sustained bf16 MFMA rate
-// (16x16x32 and 32x32x16 forms, 1-2 waves per SIMD), LDS read bandwidth, and
-// HBM read and copy bandwidth.  Standalone program: moe_peaks.
+// (16x16x32 and 32x32x16 forms, 1-2 waves per SIMD), LDS bandwidth (reads,
+// the grouped GEMM's read and write shapes, and their mix), vector-memory
+// load rate for the GEMM's two tile-row shapes, and HBM read and copy
+// bandwidth.  Standalone program: moe_peaks.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -59,6 +61,40 @@ __global__ __launch_bounds__(256) void k_mfma32(float* out, int iters) {
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// 32x32x16 with random operands, a different pair per chain, so consecutive
+// MFMAs switch their inputs as a real GEMM's do (the power drawn, and so the
+// clock the chip holds, depends on the operand bits)
+__device__ __forceinline__ unsigned hash32(unsigned x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+__global__ __launch_bounds__(256) void k_mfma32_rand(float* out, int iters) {
+  constexpr int CH = 4;
+  bf16x8 a[CH], b[CH];
+  for (int j = 0; j < CH; ++j)
+    for (int i = 0; i < 8; ++i) {
+      // bf16 values in about [-2, 2] with random mantissas
+      const unsigned ha = hash32((blockIdx.x * 256 + threadIdx.x) * 64 + j * 8 + i);
+      const unsigned hb = hash32(ha ^ 0x9e3779b9u);
+      a[j][i] = (__bf16)(((int)(ha & 0xFFFF) - 32768) / 16384.0f);
+      b[j][i] = (__bf16)(((int)(hb & 0xFFFF) - 32768) / 16384.0f);
+    }
+  f32x16 c[CH];
+  for (int j = 0; j < CH; ++j)
+    for (int q = 0; q < 16; ++q) c[j][q] = 0;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[j], c[j], 0, 0, 0);
+  }
+  float s = 0;
+  for (int j = 0; j < CH; ++j) s += c[j][0] + c[j][5] + c[j][10] + c[j][15];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 // 16-byte LDS reads from a 32 KiB buffer; the address changes every iteration
 __global__ __launch_bounds__(256) void k_lds(unsigned* out, int iters) {
   __shared__ __attribute__((aligned(16))) unsigned lds[8192];
@@ -72,6 +108,65 @@ __global__ __launch_bounds__(256) void k_lds(unsigned* out, int iters) {
       const int idx = ((w * 8 + j) * 64 + lane + it * 64) & 2047;
       acc ^= *reinterpret_cast<const u32x4*>(lds + idx * 4);
     }
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+// LDS traffic in the grouped GEMM's shapes, timed in shader clocks
+// (s_memtime): 16-byte reads of 16 rows x 1 chunk per 16 lanes, 16-byte writes
+// of 2 rows x 8 chunks, on 128-byte rows with chunk c of row r at
+// c ^ ((r >> 1) & 7).  MODE 0: reads, 1: writes, 2: three reads per write.
+template <int MODE>
+__global__ __launch_bounds__(512) void k_lds_shapes(unsigned long long* cyc, unsigned* out, int iters) {
+  extern __shared__ __attribute__((aligned(16))) unsigned short sm[];  // 512 rows x 64 elements
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < 512 * 64 / 8; i += blockDim.x)
+    reinterpret_cast<u32x4*>(sm)[i] = u32x4{1u, 2u, 3u, (unsigned)i};
+  __syncthreads();
+  u32x4 acc = {0, 0, 0, 0};
+  const int fr = lane & 31, fk = lane >> 5;
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (MODE == 0 || (MODE == 2 && (j & 3) != 3)) {
+        const int r = ((wave * 8 + j) * 32 + fr + it * 64) & 511;
+        const int c = (j * 2 + fk) & 7;
+        acc ^= *reinterpret_cast<const u32x4*>(sm + r * 64 + ((c ^ ((r >> 1) & 7)) << 3));
+      } else {
+        const int r = ((wave * 8 + j) * 8 + (lane >> 3) + it * 64) & 511;
+        const int c = lane & 7;
+        *reinterpret_cast<u32x4*>(sm + r * 64 + ((c ^ ((r >> 1) & 7)) << 3)) =
+            u32x4{(unsigned)it, 0u, 0u, (unsigned)j};
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  if (threadIdx.x == 0) cyc[blockIdx.x] = t1 - t0;
+  out[blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+// Vector-memory load rate for 1 KiB-per-wavefront loads shaped as the GEMM's
+// tile rows: LPR lanes per row, i.e. 16 rows x 64 bytes (LPR 4) or 8 rows x
+// 128 bytes (LPR 8); rows 8 KiB apart in a 16 MiB (L2/MALL-resident) buffer.
+template <int LPR>
+__global__ __launch_bounds__(512) void k_rows(const u32x4* __restrict__ buf, unsigned* out, int iters) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane / LPR, chunk = lane % LPR;
+  constexpr int kRowsPerLoad = 64 / LPR;
+  u32x4 acc = {0, 0, 0, 0};
+  int r0 = (blockIdx.x * 8 + wave) * 7;
+  for (int it = 0; it < iters; ++it) {
+    u32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = (r0 + j * kRowsPerLoad + row) & 2047;
+      v[j] = buf[(size_t)r * 512 + ((it * LPR + chunk) & 511)];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc ^= v[j];
+    r0 += 8 * kRowsPerLoad;
   }
   out[blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
@@ -131,6 +226,9 @@ int main() {
     ms = time_ms([&] { hipLaunchKernelGGL(k_mfma32<4>, dim3(grid), dim3(256), 0, 0, o, iters); });
     printf("mfma bf16 32x32x16, %d wave(s)/SIMD,  4 chains: %.1f TFLOP/s\n", bpc,
            (double)grid * 4 * iters * 4 * 32768.0 / ms / 1e9);
+    ms = time_ms([&] { hipLaunchKernelGGL(k_mfma32_rand, dim3(grid), dim3(256), 0, 0, o, iters); });
+    printf("mfma bf16 32x32x16, %d wave(s)/SIMD,  4 chains, random operands: %.1f TFLOP/s\n", bpc,
+           (double)grid * 4 * iters * 4 * 32768.0 / ms / 1e9);
   }
   for (int bpc : {1, 4}) {
     const int grid = CUs * bpc;
@@ -141,6 +239,45 @@ int main() {
     printf("lds 16-byte reads, %d block(s)/CU: %.0f bytes/clk/CU at the peak clock\n", bpc,
            bytes / (ms * 1e-3) / CUs / (p.clockRate * 1e3));
     CK(hipFree(ou));
+  }
+  {
+    unsigned long long* cyc;
+    unsigned* ou;
+    CK(hipMalloc(&cyc, (size_t)CUs * sizeof(unsigned long long)));
+    CK(hipMalloc(&ou, (size_t)CUs * 512 * 4));
+    const int it_lds = 4000;
+    for (int mode = 0; mode < 3; ++mode) {
+      auto kern = mode == 0 ? k_lds_shapes<0> : (mode == 1 ? k_lds_shapes<1> : k_lds_shapes<2>);
+      CK(hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, 65536));
+      hipLaunchKernelGGL(kern, dim3(CUs), dim3(512), 65536, 0, cyc, ou, it_lds);
+      CK(hipDeviceSynchronize());
+      unsigned long long* h = (unsigned long long*)malloc((size_t)CUs * sizeof(unsigned long long));
+      CK(hipMemcpy(h, cyc, (size_t)CUs * sizeof(unsigned long long), hipMemcpyDeviceToHost));
+      double avg = 0;
+      for (int i = 0; i < CUs; ++i) avg += (double)h[i];
+      avg /= CUs;
+      free(h);
+      printf("lds %s, 8 waves/CU: %.0f bytes/clk/CU (shader clocks)\n",
+             mode == 0 ? "GEMM fragment reads  " : (mode == 1 ? "GEMM row writes      " : "3 reads : 1 write mix"),
+             512.0 * it_lds * 8 * 16 / avg);
+    }
+    u32x4* buf;
+    CK(hipMalloc(&buf, 16 << 20));
+    CK(hipMemset(buf, 1, 16 << 20));
+    const int it_rows = 2000;
+    for (int lpr : {4, 8}) {
+      const float ms = time_ms([&] {
+        if (lpr == 4) hipLaunchKernelGGL(k_rows<4>, dim3(CUs), dim3(512), 0, 0, buf, ou, it_rows);
+        else hipLaunchKernelGGL(k_rows<8>, dim3(CUs), dim3(512), 0, 0, buf, ou, it_rows);
+      });
+      const double bytes = (double)CUs * 512 * it_rows * 8 * 16.0;
+      printf("vector-memory loads, %2d rows x %3d bytes per wavefront load: %.0f bytes/clk/CU at the peak clock\n",
+             64 / lpr, lpr * 16, bytes / (ms * 1e-3) / CUs / (p.clockRate * 1e3));
+    }
+    CK(hipFree(buf));
+    CK(hipFree(ou));
+    CK(hipFree(cyc));
   }
   const long n = (4L << 30) / 16;
   u32x4 *a, *b;
