@@ -24,6 +24,10 @@ FFN_CASES = [
     ("bf16_small_tiles", W.DT_BF16, 8, 1024, 640, [16, 3, 0, 40, 17, 1, 64, 9], 150),
     ("bf16_one_expert_ragged", W.DT_BF16, 1, 256, 192, [203], 203),
     ("bf16_many_experts_skew", W.DT_BF16, 64, 256, 128, None, 4096),
+    # odd numbers of 64-wide K stages in both projections (5 and 3), all 256-row tiles
+    ("bf16_odd_k_stages", W.DT_BF16, 2, 320, 192, [600, 300], 1024),
+    # the smallest K (one 64-wide stage), a big and an empty expert
+    ("bf16_min_k", W.DT_BF16, 2, 64, 64, [300, 0], 600),
     ("f32_tiny", W.DT_F32, 3, 128, 96, [40, 0, 33], 73),
     ("f32_ragged", W.DT_F32, 5, 64, 36, [1, 31, 32, 33, 70], 167),
 ]

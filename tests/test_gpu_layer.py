@@ -126,7 +126,7 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("name,T", SMALL, ids=[s[0] for s in SMALL])
+@pytest.mark.parametrize("name,T", SMALL, ids=[f"{s[0]}-T{s[1]}" for s in SMALL])
 def test_layer_parity_all_tokens(name, T):
     cfg = W.CONFIGS[name]
     if T is not None:
@@ -146,6 +146,13 @@ def test_layer_parity_full_size_sampled(name):
     cfg = W.CONFIGS[name]
     inp = W.make_layer_inputs(cfg, dev())
     compare_layer(cfg, inp, sample=sample_tokens(cfg.tokens))
+
+
+def test_layer_parity_shared_expert_mid_tiles():
+    # 512 tokens put the shared expert on 128-row tiles (the 8-wave 128x128 kernel)
+    cfg = W.CONFIGS["deepseek_v3"].with_tokens(512)
+    inp = W.make_layer_inputs(cfg, dev(), salt=3)
+    compare_layer(cfg, inp, sample=sample_tokens(cfg.tokens, n=40, seed=1))
 
 
 def test_layer_deterministic_and_bf16_output():
