@@ -8,12 +8,13 @@ of seeded synthetic input already resident in HBM.  The default workload is
 the Mixtral-8x7B-shaped prefill layer (T=4096, H=4096, E=8, top-2, I=14336,
 bf16 with fp32 accumulation).  Prints one JSON line on stdout.
 
-Timing: W untimed warm-up steps, then K steps between HIP events recorded on
-the stream the library launches on; every stage of every timed step is also
-bracketed by its own events (moe_debug stage events), which gives the
-dominant kernel's average duration for the roofline figure.  The CPU-oracle
-leg times the plain CPU oracle on a bounded token sample of the same
-workload.
+Timing: W untimed warm-up steps; then up to five untimed steps with events
+around every stage (moe_debug stage events) for the per-stage breakdown,
+which picks the dominant grouped-GEMM stage; then the timed region: K steps
+between HIP events recorded on the stream the library launches on, with
+events around the dominant stage only (two per step), which give its average
+duration for the roofline figure.  The CPU-oracle leg times the plain CPU
+oracle on a bounded token sample of the same workload.
 """
 
 from __future__ import annotations
@@ -154,36 +155,49 @@ def main():
 
     K = args.steps
     nst = len(abi.MOE_STAGES)
-    evs = [[(hiprt.event_create(), hiprt.event_create()) for _ in range(nst)] for _ in range(K)]
-    dbgs = []
-    for k in range(K):
+    eb = cfg.elem_bytes
+    model = gemm_model(cfg, kept, eb)
+
+    def stage_dbg(stages):
+        """MoeDebug whose timing events bracket the given stages only."""
         d = abi.MoeDebug()
-        for i in range(nst):
-            d.stage_start[i] = evs[k][i][0]
-            d.stage_stop[i] = evs[k][i][1]
-        dbgs.append(d)
+        ev = {}
+        for i in stages:
+            ev[i] = (hiprt.event_create(), hiprt.event_create())
+            d.stage_start[i], d.stage_stop[i] = ev[i]
+        return d, ev
+
+    # per-stage breakdown: a few untimed steps with events around every stage
+    nb = min(K, 5)
+    brk = [stage_dbg(range(nst)) for _ in range(nb)]
+    for d, _ in brk:
+        step(d)
+    torch.cuda.synchronize()
+    stage_ms = {name: float(np.mean([hiprt.elapsed_ms(*ev[i]) for _, ev in brk]))
+                for i, name in enumerate(abi.MOE_STAGES)}
+    # dominant kernel: the grouped-GEMM stage with the largest time
+    dom = max(model, key=lambda s: stage_ms[s])
+    i_dom = abi.MOE_STAGES.index(dom)
+
+    # timed region: K steps; events only around the dominant stage (two per step)
+    timed = [stage_dbg([i_dom]) for _ in range(K)]
     t_start, t_stop = hiprt.event_create(), hiprt.event_create()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     hiprt.event_record(t_start, stream)
-    for k in range(K):
-        step(dbgs[k])
+    for d, _ in timed:
+        step(d)
     hiprt.event_record(t_stop, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = hiprt.elapsed_ms(t_start, t_stop)
-    stage_ms = {name: float(np.mean([hiprt.elapsed_ms(*evs[k][i]) for k in range(K)]))
-                for i, name in enumerate(abi.MOE_STAGES)}
+    dom_ms = float(np.mean([hiprt.elapsed_ms(*ev[i_dom]) for _, ev in timed]))
     ms_per_step = total_ms / K
     tokens_per_s = cfg.tokens / (ms_per_step / 1e3)
 
-    eb = cfg.elem_bytes
-    model = gemm_model(cfg, kept, eb)
     peak_f = PEAK_BF16_FLOPS if cfg.dtype == W.DT_BF16 else PEAK_F32_FLOPS
-    # dominant kernel: the grouped-GEMM stage with the largest time
-    dom = max(model, key=lambda s: stage_ms[s])
     m = model[dom]
-    t_s = stage_ms[dom] / 1e3
+    t_s = dom_ms / 1e3
     bound = "mfma" if m["flops"] / peak_f >= m["bytes"] / PEAK_HBM else "hbm"
     if bound == "mfma":
         achieved, peak, unit = m["flops"] / t_s / 1e12, peak_f / 1e12, "TFLOP/s"
@@ -221,12 +235,13 @@ def main():
                    "capacity_factor": cfg.capacity_factor, "parallelism": "one GPU's expert-parallel share"},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
-                     "kernel_ms": round(stage_ms[dom], 4),
+                     "kernel_ms": round(dom_ms, 4),
                      "per_launch_algorithmic": {"flops": m["flops"], "bytes": m["bytes"], "rows": m["units"]}},
         "grouped_gemm": {"ms": round(t_gemm * 1e3, 4), "tflops": round(f_gemm / t_gemm / 1e12, 2),
                          "frac_of_roofline": round(t_roof_gemm / t_gemm, 4),
                          "frac_of_mfma_peak": round(f_gemm / t_gemm / peak_f, 4),
                          "frac_of_hbm_peak": round(b_gemm / t_gemm / PEAK_HBM, 4)},
+        # from the separate breakdown steps (events around every stage)
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "routing": {"rows_kept": int(kept.sum()), "dropped": int(cnt.sum() - kept.sum()),
                     "experts_touched": int((kept > 0).sum()),
