@@ -12,6 +12,7 @@
 //   k_tile_hist     per tile of kDispatchTileSlots slots: expert histogram
 //   k_scan_capacity column scan over tiles, capacity, offsets, drops
 //   k_rank_scatter  in-tile stable rank -> row_of_slot, row_token
+//   k_dispatch_single  all three in one block when the slots fit one tile
 //   k_gather        x_perm[row] = x[row_token[row]]
 //   k_build_sched   row tiles of the grouped GEMM from the offsets
 #include <climits>
@@ -103,6 +104,56 @@ __global__ __launch_bounds__(1024) void k_scan_capacity(int32_t* __restrict__ ti
   }
 }
 
+// This wave's expert ids of tile slots [wbase, wbase + kSlotsPerWave), all
+// loads issued before any is used; ids outside [0, E) become -1.
+__device__ __forceinline__ void load_wave_ids(const int32_t* __restrict__ ids, int wbase,
+                                              int total_slots, int E, int lane,
+                                              int (&ev)[kRankChunks], bool& bad) {
+#pragma unroll
+  for (int i = 0; i < kRankChunks; ++i) {
+    const int s = wbase + 64 * i + lane;
+    ev[i] = s < total_slots ? ids[s] : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < kRankChunks; ++i) {
+    if (ev[i] < -1 || ev[i] >= E) bad = true;
+    if (ev[i] < 0 || ev[i] >= E) ev[i] = -1;
+  }
+}
+
+// Walks the wave's slots in order, 64 at a time: a slot's rank in its expert
+// is the wave's running base (wcnt_wave[e], advanced by the last lane holding
+// e) plus the equal experts in earlier lanes of the chunk; ranks at or beyond
+// the capacity drop the slot.
+__device__ __forceinline__ void scatter_wave(const int (&ev)[kRankChunks], int wbase,
+                                             int total_slots, int k_max, int lane,
+                                             int* __restrict__ wcnt_wave,
+                                             const int* __restrict__ s_off, int cap,
+                                             int32_t* __restrict__ row_of_slot,
+                                             int32_t* __restrict__ row_token) {
+#pragma unroll
+  for (int i = 0; i < kRankChunks; ++i) {
+    if (wbase + 64 * i >= total_slots) break;
+    const int s = wbase + 64 * i + lane;
+    const int e = ev[i];
+    int before = 0, after = 0;
+    for (int j = 0; j < 64; ++j) {
+      const int ej = __builtin_amdgcn_readlane(e, j);
+      before += (ej == e && j < lane) ? 1 : 0;
+      after += (ej == e && j > lane) ? 1 : 0;
+    }
+    if (e >= 0) {
+      const int rank = wcnt_wave[e] + before;
+      const int row = rank < cap ? s_off[e] + rank : -1;
+      row_of_slot[s] = row;
+      if (row >= 0) row_token[row] = s / k_max;
+    } else if (s < total_slots) {
+      row_of_slot[s] = -1;
+    }
+    if (e >= 0 && after == 0) wcnt_wave[e] += before + 1;
+  }
+}
+
 __global__ __launch_bounds__(256) void k_rank_scatter(const int32_t* __restrict__ ids,
                                                       int total_slots, int k_max, int E,
                                                       const int32_t* __restrict__ tile_base,
@@ -117,13 +168,9 @@ __global__ __launch_bounds__(256) void k_rank_scatter(const int32_t* __restrict_
   const int tile = blockIdx.x;
   const int wbase = tile * kDispatchTileSlots + wave * kSlotsPerWave;
 
-  // the wave's expert ids, all loads issued before any is used
   int ev[kRankChunks];
-#pragma unroll
-  for (int i = 0; i < kRankChunks; ++i) {
-    const int s = wbase + 64 * i + lane;
-    ev[i] = s < total_slots ? ids[s] : -1;
-  }
+  bool bad = false;  // reported by k_tile_hist
+  load_wave_ids(ids, wbase, total_slots, E, lane, ev, bad);
   for (int i = threadIdx.x; i < kRankWaves * kMaxExperts; i += blockDim.x)
     (&wcnt[0][0])[i] = 0;
   for (int e = threadIdx.x; e < E; e += blockDim.x) s_off[e] = offsets[e];
@@ -131,10 +178,8 @@ __global__ __launch_bounds__(256) void k_rank_scatter(const int32_t* __restrict_
   __syncthreads();
   // per-wave histogram of the wave's sub-tile
 #pragma unroll
-  for (int i = 0; i < kRankChunks; ++i) {
-    if (ev[i] < 0 || ev[i] >= E) ev[i] = -1;
+  for (int i = 0; i < kRankChunks; ++i)
     if (ev[i] >= 0) atomicAdd(&wcnt[wave][ev[i]], 1);
-  }
   __syncthreads();
   // running base of each wave = tile base + counts of the earlier waves
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
@@ -146,30 +191,94 @@ __global__ __launch_bounds__(256) void k_rank_scatter(const int32_t* __restrict_
     }
   }
   __syncthreads();
-  // walk the sub-tile in order, 64 slots at a time
+  scatter_wave(ev, wbase, total_slots, k_max, lane, wcnt[wave], s_off, cap, row_of_slot,
+               row_token);
+}
+
+// The whole of S3-S5 in one block when all slots fit one tile (decode-sized
+// batches): histogram, capacity, offsets and drops, then the ranks -- the
+// three launches of the tiled path in one.
+__global__ __launch_bounds__(256) void k_dispatch_single(const int32_t* __restrict__ ids,
+                                                         int total_slots, int k_max, int E,
+                                                         float cf, int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ num_dropped,
+                                                         int32_t* __restrict__ row_of_slot,
+                                                         int32_t* __restrict__ row_token,
+                                                         uint32_t* __restrict__ flags) {
+  __shared__ int wcnt[kRankWaves][kMaxExperts];
+  __shared__ int s_off[kMaxExperts];
+  __shared__ int s_scan[256];
+  __shared__ long long s_sum[256];
+  __shared__ int s_bad;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wbase = wave * kSlotsPerWave;
+
+  int ev[kRankChunks];
+  bool bad = false;
+  load_wave_ids(ids, wbase, total_slots, E, lane, ev, bad);
+  for (int i = tid; i < kRankWaves * kMaxExperts; i += blockDim.x) (&wcnt[0][0])[i] = 0;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  if (bad) s_bad = 1;
 #pragma unroll
-  for (int i = 0; i < kRankChunks; ++i) {
-    if (wbase + 64 * i >= total_slots) break;
-    const int s = wbase + 64 * i + lane;
-    const int e = ev[i];
-    // stable rank inside the 64-slot chunk: equal experts in earlier lanes
-    int before = 0, after = 0;
-    for (int j = 0; j < 64; ++j) {
-      const int ej = __builtin_amdgcn_readlane(e, j);
-      before += (ej == e && j < lane) ? 1 : 0;
-      after += (ej == e && j > lane) ? 1 : 0;
+  for (int i = 0; i < kRankChunks; ++i)
+    if (ev[i] >= 0) atomicAdd(&wcnt[wave][ev[i]], 1);
+  __syncthreads();
+  // thread t owns experts 2t and 2t+1: counts, then wave bases (tile base 0)
+  int cnt2[2] = {0, 0};
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = 2 * tid + q;
+    if (e < E) {
+      int run = 0;
+      for (int w = 0; w < kRankWaves; ++w) {
+        const int c = wcnt[w][e];
+        wcnt[w][e] = run;
+        run += c;
+      }
+      cnt2[q] = run;
+      counts[e] = run;
     }
-    if (e >= 0) {
-      const int rank = wcnt[wave][e] + before;
-      const int row = rank < cap ? s_off[e] + rank : -1;
-      row_of_slot[s] = row;
-      if (row >= 0) row_token[row] = s / k_max;
-    } else if (s < total_slots) {
-      row_of_slot[s] = -1;
-    }
-    // the last lane of each expert advances that expert's running rank
-    if (e >= 0 && after == 0) wcnt[wave][e] += before + 1;
   }
+  // A = total routed slots; capacity C = ceil(cf * A / E), as in k_scan_capacity
+  s_sum[tid] = (long long)cnt2[0] + cnt2[1];
+  __syncthreads();
+  for (int off = 128; off >= 1; off >>= 1) {
+    if (tid < off) s_sum[tid] += s_sum[tid + off];
+    __syncthreads();
+  }
+  const long long A = s_sum[0];
+  long long C = LLONG_MAX;
+  if (cf > 0.0f) C = (long long)ceil((double)cf * (double)A / (double)E);
+  const int k0 = (int)(cnt2[0] < C ? cnt2[0] : C), k1 = (int)(cnt2[1] < C ? cnt2[1] : C);
+  // inclusive scan of the per-thread kept sums
+  s_scan[tid] = k0 + k1;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int add = tid >= off ? s_scan[tid - off] : 0;
+    __syncthreads();
+    s_scan[tid] += add;
+    __syncthreads();
+  }
+  const int excl = s_scan[tid] - k0 - k1;
+  if (2 * tid < E) {
+    s_off[2 * tid] = excl;
+    offsets[2 * tid + 1] = excl + k0;
+  }
+  if (2 * tid + 1 < E) {
+    s_off[2 * tid + 1] = excl + k0;
+    offsets[2 * tid + 2] = excl + k0 + k1;
+  }
+  if (tid == 0) {
+    offsets[0] = 0;
+    if (num_dropped) *num_dropped = (int32_t)(A - s_scan[255]);
+  }
+  __syncthreads();
+  if (tid == 0 && s_bad) atomicOr(flags, (uint32_t)MOE_FLAG_BAD_EXPERT);
+  const int cap = C > INT_MAX ? INT_MAX : (int)C;
+  scatter_wave(ev, wbase, total_slots, k_max, lane, wcnt[wave], s_off, cap, row_of_slot,
+               row_token);
 }
 
 // One wavefront per permuted row; 16-byte vector copies.
@@ -250,6 +359,12 @@ hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, int32_t* coun
                            uint32_t* flags, hipStream_t st) {
   const int total = s.num_tokens * s.top_k;
   const int E = s.num_experts;
+  if (n_tiles == 1) {
+    hipLaunchKernelGGL(k_dispatch_single, dim3(1), dim3(256), 0, st, ids, total, s.top_k, E,
+                       s.capacity_factor, counts, offsets, num_dropped, row_of_slot, row_token,
+                       flags);
+    return hipGetLastError();
+  }
   // the capacity is kept right after the tile table
   int32_t* cap = tile_counts + (size_t)n_tiles * E;
   hipLaunchKernelGGL(k_tile_hist, dim3(n_tiles), dim3(256), 0, st, ids, total, E, tile_counts,

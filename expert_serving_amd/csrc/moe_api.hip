@@ -172,9 +172,10 @@ moe_status run_router(const moe_shape& s, const void* x, const void* w_router, c
     MOE_HIP(launch_router_skinny(s, x, w_router, bias, logits, st));
     return MOE_OK;
   }
-  // 128-row tiles only when they alone give every compute unit a block
+  // 128-row tiles (8-wave blocks) once there are enough of them to spread
+  // over the chip; 32-row tiles for few tokens
   const int tiles128 = (s.num_tokens + 127) / 128 * ((s.num_experts + 127) / 128);
-  const int bm = tiles128 >= 256 ? 128 : 32;
+  const int bm = tiles128 >= 64 ? 128 : 32;
   MOE_HIP(launch_gemm_plain(s.act_dtype, bm, false, x, s.hidden, w_router, s.num_experts, s.hidden,
                             bias, logits, s.num_experts, nullptr, nullptr, 0, s.num_tokens, st));
   return MOE_OK;

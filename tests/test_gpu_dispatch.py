@@ -24,6 +24,12 @@ DISPATCH_CASES = [
     ("one_token", 1, 8, 2, 0.0, None, 0.0),
     ("ragged_tiles", 2049, 5, 3, 0.0, (1, 2, 3), 0.5),
     ("e512", 900, 512, 16, 0.0, None, 1.0),
+    # all slots in one tile (the fused single-block path): drops with per-token k,
+    # exactly one full tile, 512 experts, one expert
+    ("single_tile_capacity", 300, 16, 3, 0.5, (1, 2, 3), 0.8),
+    ("single_tile_full", 512, 8, 2, 0.0, None, 0.0),
+    ("single_tile_e512", 60, 512, 16, 1.0, None, 1.0),
+    ("single_tile_one_expert", 700, 1, 1, 0.0, None, 0.0),
 ]
 
 
@@ -64,13 +70,14 @@ def test_dispatch_parity(name, T, E, k, cf, kch, zipf):
     say(f"  R={R} dropped={ref['num_dropped']} max/mean={ref['counts'].max() / max(ref['counts'].mean(), 1e-9):.2f}")
 
 
-def test_dispatch_invalid_ids_flagged_and_unused():
-    T, E, k = 500, 12, 3
+@pytest.mark.parametrize("T", [500, 300], ids=["tiled", "single_tile"])
+def test_dispatch_invalid_ids_flagged_and_unused(T):
+    E, k = 12, 3
     ids, _ = oracle.route(W.make_logits(T, E, seed=99).numpy(), k)
     ids = ids.copy()
     ids[5, 1] = E + 3
     ids[77, 0] = -5
-    ids[400, 2] = -1
+    ids[T - 100, 2] = -1
     ref = oracle.dispatch(ids, E, 0.0)        # the oracle also skips ids outside [0, E)
     got = run_dispatch(T, E, k, 0.0, ids)
     assert got["flags"] == abi.MOE_FLAG_BAD_EXPERT

@@ -105,7 +105,8 @@ ROUTER_CASES = [
     (W.DT_BF16, 257, 2048, 33, True),
     (W.DT_BF16, 777, 7168, 256, True),
     (W.DT_BF16, 4096, 2048, 128, True),
-    (W.DT_BF16, 16384, 1024, 256, True),      # enough 128-row tiles for the 8-wave MFMA kernel
+    (W.DT_BF16, 16384, 1024, 256, True),      # 128-row tiles (8-wave MFMA kernel)
+    (W.DT_BF16, 8192, 1024, 64, True),        # the smallest token count on 128-row tiles
     (W.DT_F32, 300, 512, 8, True),
 ]
 
