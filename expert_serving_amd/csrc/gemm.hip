@@ -22,6 +22,8 @@
 //     b is remapped to give each XCD a contiguous range of logical tiles, and
 //     logical tiles sweep groups of kGroupM row tiles across all column tiles
 //     so the XCD's L2 serves both the token rows and the weight rows.
+#include <atomic>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -589,13 +591,20 @@ hipError_t launch_mfma(const void* A, const int32_t* a_rows, int lda, const void
                        hipStream_t st) {
   constexpr int lds = gemm_lds_bytes(BM, BNB, MODE, NS, NW);
   static_assert(lds <= 160 * 1024, "LDS");
-  static bool attr_set = false;
-  if (lds > 65536 && !attr_set) {
-    const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&k_gemm_mfma<BM, BNB, MODE, NS, NW>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if constexpr (lds > 65536) {
+    // raise the kernel's LDS limit once per device (setting it again is harmless,
+    // so concurrent first calls may both set it)
+    static std::atomic<uint64_t> set_on{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    const uint64_t bit = 1ull << (dev & 63);
+    if (!(set_on.load(std::memory_order_acquire) & bit)) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_mfma<BM, BNB, MODE, NS, NW>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      if (e != hipSuccess) return e;
+      set_on.fetch_or(bit, std::memory_order_release);
+    }
   }
   const int ntiles = (N + BNB - 1) / BNB;
   const dim3 grid(grid_for(mslots, ntiles));
