@@ -147,6 +147,41 @@ __global__ __launch_bounds__(512) void k_lds_shapes(unsigned long long* cyc, uns
   out[blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+
+// LDS fragment reads (as k_lds_shapes) alongside direct-to-LDS loads
+// (global_load_lds_dwordx4, 8 rows x 128 bytes per wavefront load, from a
+// 1 MiB L2-resident buffer) into a second 64 KiB region: 3 reads per load.
+__global__ __launch_bounds__(512) void k_lds_with_dma(const u32x4* __restrict__ src,
+                                                      unsigned long long* cyc, unsigned* out,
+                                                      int iters) {
+  extern __shared__ __attribute__((aligned(16))) unsigned short sm[];  // 2 x 512 rows x 64 elements
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < 512 * 64 / 8; i += blockDim.x)
+    reinterpret_cast<u32x4*>(sm)[i] = u32x4{1u, 2u, 3u, (unsigned)i};
+  __syncthreads();
+  u32x4 acc = {0, 0, 0, 0};
+  const int fr = lane & 31, fk = lane >> 5;
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int r = ((wave * 8 + j) * 32 + fr + it * 64) & 511;
+      const int c = (j * 2 + fk) & 7;
+      acc ^= *reinterpret_cast<const u32x4*>(sm + r * 64 + ((c ^ ((r >> 1) & 7)) << 3));
+    }
+    const int row = (wave * 8 + (lane >> 3) + it * 64) & 8191;
+    unsigned short* dst = sm + 32768 + ((wave + 8 * it) & 63) * 512;
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src + (size_t)row * 8 + (lane & 7)), (lds_ptr_t)dst,
+                                     16, 0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  if (threadIdx.x == 0) cyc[blockIdx.x] = t1 - t0;
+  out[blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
 // Vector-memory load rate for 1 KiB-per-wavefront loads shaped as the GEMM's
 // tile rows: LPR lanes per row, i.e. 16 rows x 64 bytes (LPR 4) or 8 rows x
 // 128 bytes (LPR 8); rows 8 KiB apart in a 16 MiB (L2/MALL-resident) buffer.
@@ -261,6 +296,24 @@ int main() {
       printf("lds %s, 8 waves/CU: %.0f bytes/clk/CU (shader clocks)\n",
              mode == 0 ? "GEMM fragment reads  " : (mode == 1 ? "GEMM row writes      " : "3 reads : 1 write mix"),
              512.0 * it_lds * 8 * 16 / avg);
+    }
+    {
+      u32x4* src;
+      CK(hipMalloc(&src, 1 << 20));
+      CK(hipMemset(src, 1, 1 << 20));
+      CK(hipFuncSetAttribute(reinterpret_cast<const void*>(k_lds_with_dma),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, 131072));
+      hipLaunchKernelGGL(k_lds_with_dma, dim3(CUs), dim3(512), 131072, 0, src, cyc, ou, it_lds);
+      CK(hipDeviceSynchronize());
+      unsigned long long* h = (unsigned long long*)malloc((size_t)CUs * sizeof(unsigned long long));
+      CK(hipMemcpy(h, cyc, (size_t)CUs * sizeof(unsigned long long), hipMemcpyDeviceToHost));
+      double avg = 0;
+      for (int i = 0; i < CUs; ++i) avg += (double)h[i];
+      avg /= CUs;
+      free(h);
+      printf("lds 3 reads : 1 direct-to-LDS load, 8 waves/CU: %.0f bytes/clk/CU (shader clocks)\n",
+             512.0 * it_lds * 4 * 16 / avg);
+      CK(hipFree(src));
     }
     u32x4* buf;
     CK(hipMalloc(&buf, 16 << 20));
