@@ -57,6 +57,8 @@ def lib():
         L.oracle_capacity.restype = ctypes.c_int64
         L.oracle_dispatch.argtypes = [i32, i32, i32, vp, f32, vp, vp, vp, vp, vp]
         L.oracle_dispatch.restype = i32
+        L.oracle_map_replicas.argtypes = [i32, i32, i32, vp, vp, vp, i32, vp]
+        L.oracle_map_replicas.restype = i32
         L.oracle_grouped_ffn.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp]
         L.oracle_combine.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
         L.oracle_layer_forward.argtypes = (
@@ -131,6 +133,21 @@ def dispatch(ids, E, capacity_factor=0.0):
                               _p(row_token), _p(nd))
     return dict(counts=counts, offsets=offsets, row_of_slot=ros, row_token=row_token,
                 num_dropped=int(nd[0]), R=int(R))
+
+
+def map_replicas(ids, replica_offsets, replica_experts, num_physical):
+    """Physical expert of every slot (least-loaded replica, token-major order)
+    and the number of slots whose replica-table entry was invalid."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    T, k = ids.shape
+    E = len(replica_offsets) - 1
+    ro = np.ascontiguousarray(replica_offsets, dtype=np.int32)
+    rex = np.ascontiguousarray(replica_experts, dtype=np.int32)
+    if rex.size == 0:
+        rex = np.zeros(1, np.int32)
+    phys = np.empty((T, k), np.int32)
+    bad = lib().oracle_map_replicas(T, E, k, _p(ids), _p(ro), _p(rex), int(num_physical), _p(phys))
+    return phys, int(bad)
 
 
 def grouped_ffn(x_perm, offsets, w_gate, w_up, w_down, rows=None) -> np.ndarray:

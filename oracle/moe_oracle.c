@@ -270,6 +270,47 @@ int32_t oracle_dispatch(int T, int E, int k_max, const int32_t* ids, float cf, i
   return offsets[E];
 }
 
+/* ---- redundant experts: replica choice per slot ----------------------------
+ * A hot expert may have several identical copies ("replicas"); the router
+ * sends each of its tokens to the copy with the lower load ("LLM MoE Expert
+ * Parallel production practice", step 3: selective replicas of hot experts;
+ * "Expert Parallelism: MoE model parallel split" §6.2: static replicas, the
+ * router splits by load).  Plain definition on one batch: slots are visited
+ * token-major; a slot of logical expert e goes to the replica of e with the
+ * fewest slots assigned so far in this batch, ties to the lower replica
+ * index; that replica's count then grows by one.
+ * replica_offsets [E+1], replica_experts [replica_offsets[E]]: the physical
+ * experts (in [0, num_physical)) holding copies of e.  phys_ids[s] = -1 when
+ * the slot is unused, its expert is outside [0, E), e has no replica, or the
+ * chosen physical id is outside [0, num_physical).  Returns the number of
+ * slots with an invalid replica table entry. */
+int32_t oracle_map_replicas(int T, int E, int k_max, const int32_t* ids,
+                            const int32_t* replica_offsets, const int32_t* replica_experts,
+                            int num_physical, int32_t* phys_ids) {
+  int32_t n_total = replica_offsets[E];
+  int64_t* load = (int64_t*)calloc((size_t)(n_total > 0 ? n_total : 1), sizeof(int64_t));
+  int32_t bad = 0;
+  for (int t = 0; t < T; ++t) {
+    for (int j = 0; j < k_max; ++j) {
+      int64_t s = (int64_t)t * k_max + j;
+      int e = ids[s];
+      phys_ids[s] = -1;
+      if (e < 0 || e >= E) continue;
+      int32_t r0 = replica_offsets[e], r1 = replica_offsets[e + 1];
+      if (r1 <= r0) { bad++; continue; }
+      int32_t best = r0;
+      for (int32_t r = r0 + 1; r < r1; ++r)
+        if (load[r] < load[best]) best = r;
+      load[best]++;
+      int32_t p = replica_experts[best];
+      if (p < 0 || p >= num_physical) { bad++; continue; }
+      phys_ids[s] = p;
+    }
+  }
+  free(load);
+  return bad;
+}
+
 /* ---- one expert's SwiGLU FFN on one activation row -----------------------
  * y = Wd . (silu(Wg . x) * (Wu . x)), silu(z) = z / (1 + e^-z); fp64 sums.
  * wg, wu: [I][H] rows for this expert; wd: [H][I]. */

@@ -512,3 +512,111 @@ def test_deepseek_shaped_bias_reaches_hotspot_ratio():
     counts = np.bincount(ids.reshape(-1), minlength=cfg.experts)
     assert counts.mean() > 0 and counts.max() / counts.mean() >= thr
     del torch
+
+
+# ---- redundant experts: replica choice ------------------------------------------------------
+
+
+def _rank_in_expert(ids):
+    """Token-major rank of every slot among the slots of the same expert (numpy, no oracle)."""
+    flat = ids.reshape(-1)
+    rank = np.full(flat.shape, -1, np.int64)
+    seen = {}
+    for s, e in enumerate(flat.tolist()):
+        if e >= 0:
+            rank[s] = seen.get(e, 0)
+            seen[e] = rank[s] + 1
+    return rank.reshape(ids.shape)
+
+
+def _random_replica_table(rng, E, max_rep):
+    n = rng.integers(1, max_rep + 1, size=E)
+    off = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    P = int(off[-1])
+    rex = rng.permutation(P).astype(np.int32)      # every physical expert holds one replica
+    return off, rex, P
+
+
+def test_replicas_identity_table_keeps_ids():
+    rng = np.random.default_rng(7)
+    ids = rng.integers(-1, 9, size=(40, 3)).astype(np.int32)
+    phys, bad = oracle.map_replicas(ids, np.arange(10, dtype=np.int32), np.arange(9, dtype=np.int32), 9)
+    assert bad == 0
+    assert np.array_equal(phys, np.where(ids >= 0, ids, -1))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_replicas_follow_round_robin_in_token_order(seed):
+    # least-loaded with ties to the lower replica index, from an empty batch, is the
+    # rank-mod-n rotation: the r-th slot of e takes replica r mod n_e
+    rng = np.random.default_rng(seed)
+    T, E, k = 60, 6, 3
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    ids[rng.random((T, k)) < 0.1] = -1
+    off, rex, P = _random_replica_table(rng, E, 3)
+    phys, bad = oracle.map_replicas(ids, off, rex, P)
+    assert bad == 0
+    rank = _rank_in_expert(ids)
+    for t in range(T):
+        for j in range(k):
+            e = ids[t, j]
+            if e < 0:
+                assert phys[t, j] == -1
+                continue
+            n = off[e + 1] - off[e]
+            assert phys[t, j] == rex[off[e] + rank[t, j] % n]
+
+
+def test_replica_loads_differ_by_at_most_one():
+    rng = np.random.default_rng(11)
+    T, E, k = 500, 8, 2
+    logits = W.make_logits(T, E, seed=4, bias=W.log_zipf_bias(E, 1.2)).numpy()
+    ids, _ = oracle.route(logits, k)
+    off, rex, P = _random_replica_table(rng, E, 4)
+    phys, _ = oracle.map_replicas(ids, off, rex, P)
+    counts = np.bincount(ids[ids >= 0], minlength=E)
+    pc = np.bincount(phys[phys >= 0], minlength=P)
+    for e in range(E):
+        reps = pc[rex[off[e]:off[e + 1]]]
+        assert reps.sum() == counts[e]
+        assert reps.max() - reps.min() <= 1
+        assert np.all(np.diff(reps) <= 0)           # the extra slots go to the lower replica indices
+
+
+def test_replicas_lower_the_hottest_load():
+    # replicating the hottest experts of the DeepSeek-V3-shaped routing lowers max/mean
+    cfg = W.CONFIGS["deepseek_v3"]
+    T, E = 1024, cfg.experts
+    logits = W.make_logits(T, E, seed=9, bias=W.log_zipf_bias(E, 1.1)).numpy()
+    ids, _ = oracle.route(logits, cfg.top_k, None, cfg.score, cfg.renormalize, cfg.routed_scale,
+                          cfg.num_groups, cfg.topk_groups, cfg.group_topn)
+    counts = np.bincount(ids[ids >= 0], minlength=E)
+    hot = np.argsort(-counts, kind="stable")[:16]
+    n = np.ones(E, np.int64)
+    n[hot] = 3                                      # two extra replicas for the 16 hottest
+    off = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    rex = np.arange(off[-1], dtype=np.int32)
+    phys, bad = oracle.map_replicas(ids, off, rex, int(off[-1]))
+    assert bad == 0
+    pc = np.bincount(phys[phys >= 0], minlength=int(off[-1]))
+    assert pc.sum() == counts.sum()
+    top = hot[0]
+    assert pc[rex[off[top]:off[top + 1]]].max() == -(-counts[top] // 3)
+    assert pc.max() / pc.mean() < counts.max() / counts.mean()
+
+
+def test_replicas_invalid_table_entries():
+    ids = np.array([[0, 1], [1, 2], [2, 0]], np.int32)
+    off = np.array([0, 1, 1, 3], np.int32)          # expert 1 has no replica
+    rex = np.array([0, 1, 7], np.int32)             # expert 2's second replica is out of range
+    phys, bad = oracle.map_replicas(ids, off, rex, 3)
+    assert np.array_equal(phys, [[0, -1], [-1, 1], [-1, 0]])
+    assert bad == 3
+
+
+def test_replicas_hand_worked():
+    # expert 0 on physical 0 and 3 (in that order), experts 1 and 2 on one copy each
+    ids = np.array([[0, 1], [0, 2], [0, 1], [1, 0]], np.int32)
+    phys, bad = oracle.map_replicas(ids, [0, 2, 3, 4], [0, 3, 1, 2], 4)
+    assert bad == 0
+    assert np.array_equal(phys, [[0, 1], [3, 2], [0, 1], [1, 3]])
