@@ -98,6 +98,41 @@ def cpu_baseline(cfg, inp, budget_s=15.0):
                        f"({t_n - t_route:.2f} s); fp64-accumulating C oracle, OpenMP over tokens")
 
 
+def replica_leg(spec, cfg, shape, ws, step, hiprt, stream, K, torch, abi):
+    """Times moe_map_replicas on this workload's routing (K calls between events)
+    with EXTRA more copies of the HOT most loaded experts."""
+    hot, extra = (int(v) for v in spec.split(":"))
+    dev = torch.device("cuda:0")
+    T, E, k = cfg.tokens, cfg.experts, cfg.top_k
+    ids = torch.empty(T * k, dtype=torch.int32, device=dev)
+    step(dict(topk_ids=ids))
+    torch.cuda.synchronize()
+    ids_h = ids.cpu().numpy()
+    counts = np.bincount(ids_h[ids_h >= 0], minlength=E)
+    n = np.ones(E, np.int64)
+    n[np.argsort(-counts, kind="stable")[:hot]] += extra
+    off = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    P = int(off[-1])
+    rex = np.arange(P, dtype=np.int32)
+    off_d, rex_d = torch.from_numpy(off).to(dev), torch.from_numpy(rex).to(dev)
+    phys = torch.empty(T * k, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        abi.moe_map_replicas(shape, ids, off_d, rex_d, P, phys, ws, stream=stream)
+    a, b = hiprt.event_create(), hiprt.event_create()
+    torch.cuda.synchronize()
+    hiprt.event_record(a, stream)
+    for _ in range(K):
+        abi.moe_map_replicas(shape, ids, off_d, rex_d, P, phys, ws, stream=stream)
+    hiprt.event_record(b, stream)
+    torch.cuda.synchronize()
+    us = hiprt.elapsed_ms(a, b) / K * 1e3
+    ph = phys.cpu().numpy()
+    pc = np.bincount(ph[ph >= 0], minlength=P)
+    return {"hot_experts": hot, "extra_copies": extra, "physical_experts": P, "us_per_call": round(us, 2),
+            "slots": int(T * k), "max_over_mean_logical": round(float(counts.max() / counts.mean()), 3),
+            "max_over_mean_physical": round(float(pc.max() / pc.mean()), 3)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,6 +141,9 @@ def main():
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--replicas", default=None, metavar="HOT:EXTRA",
+                    help="also time the redundant-expert routing step (moe_map_replicas) with EXTRA more "
+                         "copies of the HOT most loaded experts, and report the load balance it gives")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device-to-device copy first (a kernel of known HBM traffic "
                          "for scaling profiler byte counters)")
@@ -248,6 +286,8 @@ def main():
                     "max_over_mean_load": round(float(cnt.max() / max(cnt.mean(), 1e-9)), 3)},
         "host_wall_s": round(wall, 3),
     }
+    if args.replicas:
+        line["replica_map"] = replica_leg(args.replicas, cfg, shape, ws, step, hiprt, stream, K, torch, abi)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)

@@ -18,11 +18,11 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
-MOE_FLAG_BAD_K, MOE_FLAG_BAD_EXPERT, MOE_FLAG_H_RANGE = 1, 2, 4
+MOE_FLAG_BAD_K, MOE_FLAG_BAD_EXPERT, MOE_FLAG_H_RANGE, MOE_FLAG_BAD_REPLICA = 1, 2, 4, 8
 
-EXPORTED = ("moe_workspace_size", "moe_route_topk", "moe_dispatch", "moe_grouped_ffn", "moe_combine",
-            "moe_layer_forward", "moe_group_score_sigmoid", "moe_status_string", "moe_last_hip_error",
-            "moe_read_device_flags")
+EXPORTED = ("moe_workspace_size", "moe_route_topk", "moe_dispatch", "moe_map_replicas", "moe_grouped_ffn",
+            "moe_combine", "moe_layer_forward", "moe_group_score_sigmoid", "moe_status_string",
+            "moe_last_hip_error", "moe_read_device_flags")
 
 
 class MoeShape(ctypes.Structure):
@@ -71,6 +71,7 @@ def lib():
         L.moe_workspace_size.argtypes = [sp, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_route_topk.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_dispatch.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_map_replicas.argtypes = [sp, vp, vp, vp, ctypes.c_int32, vp, vp, sz, vp]
         L.moe_grouped_ffn.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_combine.argtypes = [sp, vp, vp, vp, vp, vp, vp]
         L.moe_layer_forward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -142,6 +143,14 @@ def moe_dispatch(shape, x, topk_ids, expert_counts, expert_offsets, row_of_slot,
                               _ptr(expert_offsets), _ptr(row_of_slot), _ptr(row_token), _ptr(num_dropped),
                               _ptr(x_perm), _ptr(ws), ws.numel() if ws_bytes is None else ws_bytes,
                               _stream(stream)), "moe_dispatch")
+
+
+def moe_map_replicas(shape, topk_ids, replica_offsets, replica_experts, num_physical, phys_ids, ws,
+                     ws_bytes=None, stream=None):
+    _check(lib().moe_map_replicas(ctypes.byref(shape), _ptr(topk_ids), _ptr(replica_offsets),
+                                  _ptr(replica_experts), int(num_physical), _ptr(phys_ids), _ptr(ws),
+                                  ws.numel() if ws_bytes is None else ws_bytes, _stream(stream)),
+           "moe_map_replicas")
 
 
 def moe_grouped_ffn(shape, x_perm, expert_offsets, w_gate, w_up, w_down, y_perm, ws, ws_bytes=None,

@@ -344,6 +344,37 @@ __global__ __launch_bounds__(512) void k_build_sched(const int32_t* __restrict__
   }
 }
 
+// Replica of each slot: the r-th slot of logical expert e (token-major, r =
+// its row in the uncapped dispatch minus offsets[e]) takes replica r mod n_e.
+__global__ __launch_bounds__(256) void k_map_replicas(const int32_t* __restrict__ ids,
+                                                      int total_slots, int E,
+                                                      const int32_t* __restrict__ row_of_slot,
+                                                      const int32_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ rep_off,
+                                                      const int32_t* __restrict__ rep_exp,
+                                                      int num_physical,
+                                                      int32_t* __restrict__ phys,
+                                                      uint32_t* __restrict__ flags) {
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= total_slots) return;
+  const int e = ids[s];
+  int p = -1;
+  if (e >= 0 && e < E) {
+    const int r0 = rep_off[e], n = rep_off[e + 1] - r0;
+    bool bad = n <= 0;
+    if (!bad) {
+      const int rank = row_of_slot[s] - offsets[e];
+      p = rep_exp[r0 + rank % n];
+      if (p < 0 || p >= num_physical) {
+        p = -1;
+        bad = true;
+      }
+    }
+    if (bad) atomicOr(flags, (uint32_t)MOE_FLAG_BAD_REPLICA);
+  }
+  phys[s] = p;
+}
+
 __global__ void k_clear_flags(uint32_t* flags) { *flags = 0u; }
 
 }  // namespace
@@ -373,6 +404,17 @@ hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, int32_t* coun
                      s.capacity_factor, counts, offsets, num_dropped, cap);
   hipLaunchKernelGGL(k_rank_scatter, dim3(n_tiles), dim3(256), 0, st, ids, total, s.top_k, E,
                      tile_counts, offsets, cap, row_of_slot, row_token);
+  return hipGetLastError();
+}
+
+hipError_t launch_map_replicas(const moe_shape& s, const int32_t* ids, const int32_t* row_of_slot,
+                               const int32_t* offsets, const int32_t* rep_off,
+                               const int32_t* rep_exp, int num_physical, int32_t* phys,
+                               uint32_t* flags, hipStream_t st) {
+  const int total = s.num_tokens * s.top_k;
+  hipLaunchKernelGGL(k_map_replicas, dim3((total + 255) / 256), dim3(256), 0, st, ids, total,
+                     s.num_experts, row_of_slot, offsets, rep_off, rep_exp, num_physical, phys,
+                     flags);
   return hipGetLastError();
 }
 

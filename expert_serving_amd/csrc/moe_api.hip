@@ -305,6 +305,38 @@ moe_status moe_dispatch(const moe_shape* shape, const void* x, const int32_t* to
   return MOE_OK;
 }
 
+moe_status moe_map_replicas(const moe_shape* shape, const int32_t* topk_ids,
+                            const int32_t* replica_offsets, const int32_t* replica_experts,
+                            int32_t num_physical, int32_t* phys_ids, void* ws, size_t ws_bytes,
+                            void* stream) {
+  MOE_TRY(check_shape(shape));
+  MOE_TRY(need4(topk_ids));
+  MOE_TRY(need4(replica_offsets));
+  MOE_TRY(need4(replica_experts));
+  MOE_TRY(need4(phys_ids));
+  MOE_TRY(need(ws));
+  if (num_physical < 1) return MOE_ERR_INVALID_ARG;
+  // the token-major rank of every slot comes from an uncapped dispatch of the
+  // logical ids into the workspace
+  moe_shape s = *shape;
+  s.capacity_factor = 0.0f;
+  const WsLayout L = plan_workspace(s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (s.num_tokens == 0) return MOE_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t* flags = at<uint32_t>(ws, L.flags);
+  int32_t* counts = at<int32_t>(ws, L.counts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* ros = at<int32_t>(ws, L.row_of_slot);
+  MOE_HIP(launch_clear_flags(flags, st));
+  MOE_HIP(launch_dispatch(s, topk_ids, counts, offsets, ros, at<int32_t>(ws, L.row_token),
+                          at<int32_t>(ws, L.num_dropped), at<int32_t>(ws, L.tile_counts),
+                          L.n_dispatch_tiles, flags, st));
+  MOE_HIP(launch_map_replicas(s, topk_ids, ros, offsets, replica_offsets, replica_experts,
+                              num_physical, phys_ids, flags, st));
+  return MOE_OK;
+}
+
 moe_status moe_grouped_ffn(const moe_shape* shape, const void* x_perm,
                            const int32_t* expert_offsets, const void* w_gate, const void* w_up,
                            const void* w_down, float* y_perm, void* ws, size_t ws_bytes,

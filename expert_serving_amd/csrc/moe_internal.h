@@ -65,6 +65,12 @@ hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, int32_t* coun
                            int32_t* num_dropped, int32_t* tile_counts, int n_tiles,
                            uint32_t* flags, hipStream_t st);
 
+// phys[s] = replica of slot s's expert (rank in the uncapped dispatch mod n_e)
+hipError_t launch_map_replicas(const moe_shape& s, const int32_t* ids, const int32_t* row_of_slot,
+                               const int32_t* offsets, const int32_t* rep_off,
+                               const int32_t* rep_exp, int num_physical, int32_t* phys,
+                               uint32_t* flags, hipStream_t st);
+
 hipError_t launch_gather(const moe_shape& s, const void* x, const int32_t* row_token,
                          const int32_t* offsets, void* x_perm, hipStream_t st);
 

@@ -69,6 +69,7 @@ typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
 #define MOE_FLAG_BAD_K 1u       /* some k_per_token[t] outside [1, top_k]: token routed nowhere */
 #define MOE_FLAG_BAD_EXPERT 2u  /* some topk_ids entry outside [-1, E): slot treated as unused  */
 #define MOE_FLAG_H_RANGE 4u     /* some SwiGLU activation h exceeded fp16 range (bf16 layers)   */
+#define MOE_FLAG_BAD_REPLICA 8u /* a routed expert without a replica, or a replica id out of range */
 
 typedef struct {
   int32_t num_tokens;          /* T >= 0                                                  */
@@ -181,6 +182,31 @@ moe_status moe_grouped_ffn(const moe_shape* shape, const void* x_perm,
                            const int32_t* expert_offsets, const void* w_gate, const void* w_up,
                            const void* w_down, float* y_perm, void* ws, size_t ws_bytes,
                            void* stream);
+
+/* Redundant experts: the replica each routed slot goes to.  A hot expert may
+ * have identical copies ("LLM MoE Expert Parallel production practice", step
+ * 3: selective replicas, the router picks the copy with the lower load;
+ * "Expert Parallelism: MoE model parallel split" §6.2: static replicas, the
+ * router splits by load).  Logical expert e (of shape->num_experts) has the
+ * replicas replica_experts[replica_offsets[e] .. replica_offsets[e+1]),
+ * physical expert ids in [0, num_physical).  Slots are visited in token-major
+ * order; each goes to the replica of its expert with the fewest slots of this
+ * batch assigned so far, ties to the lower replica index -- so the r-th slot
+ * of e (token-major) takes replica r mod n_e.
+ *   phys_ids[s] = physical expert of slot s, -1 when topk_ids[s] is unused,
+ *                 outside [0, E), or e has no valid replica       [T][top_k]
+ * topk_ids as moe_route_topk writes them; replica_offsets [E+1] and
+ * replica_experts are device arrays (contents checked on the device: an
+ * empty replica list or an id outside [0, num_physical) sets
+ * MOE_FLAG_BAD_REPLICA and leaves the slot at -1).  The physical ids then go
+ * through moe_dispatch / moe_grouped_ffn / moe_combine with num_experts =
+ * num_physical and weights [num_physical][..] in which every replica holds its
+ * expert's weights; no capacity applies here.  Uses the workspace of
+ * `shape`; clears its flag word. */
+moe_status moe_map_replicas(const moe_shape* shape, const int32_t* topk_ids,
+                            const int32_t* replica_offsets, const int32_t* replica_experts,
+                            int32_t num_physical, int32_t* phys_ids, void* ws, size_t ws_bytes,
+                            void* stream);
 
 /* S10: combine ("Expert Parallelism: MoE model parallel split" §1 weighted
  * sum, §12 Q2 combine).  out[t] = sum over j ascending with

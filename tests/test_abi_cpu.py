@@ -116,6 +116,11 @@ def test_null_and_misaligned_pointers_rejected_before_launch():
     ws2 = abi.moe_workspace_size(s2)
     assert L.moe_layer_forward(ctypes.byref(s2), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, None, None,
                                FAKE, None, FAKE, ws2, None) == -1
+    # replica map: no physical experts, missing tables or output
+    assert L.moe_map_replicas(ref, FAKE, FAKE, FAKE, 0, FAKE, FAKE, ws, None) == -1
+    assert L.moe_map_replicas(ref, FAKE, None, FAKE, 4, FAKE, FAKE, ws, None) == -1
+    assert L.moe_map_replicas(ref, FAKE, FAKE, FAKE, 4, None, FAKE, ws, None) == -1
+    assert L.moe_map_replicas(ref, FAKE, FAKE, FAKE, 4, FAKE, FAKE, ws - 1, None) == -3
     assert L.moe_group_score_sigmoid(FAKE, FAKE, -1, None) == -1
     assert L.moe_read_device_flags(None, None, None) == -1
 
@@ -131,6 +136,7 @@ def test_zero_tokens_is_a_no_op():
     assert L.moe_combine(ref, FAKE, FAKE, FAKE, None, FAKE, None) == 0
     assert L.moe_layer_forward(ref, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, None, None, FAKE, None,
                                FAKE, ws, None) == 0
+    assert L.moe_map_replicas(ref, FAKE, FAKE, FAKE, 4, FAKE, FAKE, ws, None) == 0
     assert L.moe_group_score_sigmoid(FAKE, FAKE, 0, None) == 0
 
 
