@@ -144,6 +144,10 @@ def main():
     ap.add_argument("--replicas", default=None, metavar="HOT:EXTRA",
                     help="also time the redundant-expert routing step (moe_map_replicas) with EXTRA more "
                          "copies of the HOT most loaded experts, and report the load balance it gives")
+    ap.add_argument("--set", action="append", default=[], metavar="FIELD=VALUE",
+                    help="override a field of the workload's layer shape (e.g. top_k=8, k_choices=none, "
+                         "capacity_factor=0); the overrides are echoed in the config; the seeds stay those "
+                         "of the named workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device-to-device copy first (a kernel of known HBM traffic "
                          "for scaling profiler byte counters)")
@@ -160,6 +164,19 @@ def main():
     from expert_serving_amd import abi, hiprt
 
     cfg = W.CONFIGS[args.workload]
+    overrides = {}
+    for item in args.set:
+        key, val = item.split("=", 1)
+        cur = getattr(cfg, key)
+        if val.lower() == "none":
+            v = None
+        elif key == "k_choices":
+            v = tuple(int(c) for c in val.split(","))
+        else:
+            v = type(cur)(float(val)) if isinstance(cur, (int, float)) and not isinstance(cur, bool) else val
+        overrides[key] = v
+    if overrides:
+        cfg = cfg.replace(**overrides)
     dev = torch.device("cuda:0")
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -270,7 +287,8 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
         "config": {"workload": cfg.name, "tokens": cfg.tokens, "hidden": cfg.hidden, "experts": cfg.experts,
                    "top_k": cfg.top_k, "intermediate": cfg.inter, "shared_intermediate": cfg.shared_inter,
-                   "capacity_factor": cfg.capacity_factor, "parallelism": "one GPU's expert-parallel share"},
+                   "capacity_factor": cfg.capacity_factor, "parallelism": "one GPU's expert-parallel share",
+                   **({"overrides": {k: v for k, v in overrides.items()}} if overrides else {})},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
                      "kernel_ms": round(dom_ms, 4),

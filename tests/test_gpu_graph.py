@@ -52,3 +52,53 @@ def test_layer_graph_replay_matches_eager(name, T):
         torch.cuda.synchronize()
         assert torch.equal(out, ref)
     assert abi.moe_read_device_flags(ws) == 0
+
+
+def test_one_graph_serves_every_k_mix():
+    """Per-token k ("MoE-Prism: Disentangling Monolithic Experts...", the
+    k-aware execution part: MoE graph segments specialised per k) is read on
+    the device here, so one captured layer call serves any mix of k values:
+    rewriting k_per_token in place between replays must give what an eager
+    call with the new k gives, bit for bit."""
+    cfg = W.CONFIGS["qwen3_skewed"].with_tokens(2048)
+    say("graph capture qwen3_skewed T=2048, k rewritten between replays")
+    inp = W.make_layer_inputs(cfg, dev(), salt=6)
+    shape = abi.make_shape(cfg)
+    ws = workspace(shape)
+    out = torch.empty(cfg.tokens, cfg.hidden, dtype=torch.float32, device=dev())
+    k = inp["k_per_token"]
+    assert k is not None and k.dtype == torch.int32
+
+    def call():
+        abi.moe_layer_forward(shape, inp["x"], inp["w_router"], inp["bias"], k, inp["w_gate"], inp["w_up"],
+                              inp["w_down"], inp["ws_gate"], inp["ws_up"], inp["ws_down"], out, None, ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+
+    gen = torch.Generator().manual_seed(11)
+    mixes = {
+        "all k_max": torch.full((cfg.tokens,), cfg.top_k, dtype=torch.int32),
+        "all 2": torch.full((cfg.tokens,), 2, dtype=torch.int32),
+        "k in 1..k_max": torch.randint(1, cfg.top_k + 1, (cfg.tokens,), generator=gen, dtype=torch.int32),
+        "sorted tiers": torch.sort(torch.tensor(cfg.k_choices, dtype=torch.int32)[
+            torch.randint(0, len(cfg.k_choices), (cfg.tokens,), generator=gen)])[0].to(torch.int32),
+    }
+    for name, kk in mixes.items():
+        k.copy_(kk.to(dev()))
+        call()
+        torch.cuda.synchronize()
+        ref = out.clone()
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay with k mix '{name}' differs from the eager call"
+        assert abi.moe_read_device_flags(ws) == 0
