@@ -61,6 +61,10 @@ def lib():
         L.oracle_map_replicas.restype = i32
         L.oracle_grouped_ffn.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp]
         L.oracle_combine.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+        L.oracle_e4m3_value.argtypes = [i32]
+        L.oracle_e4m3_value.restype = ctypes.c_double
+        L.oracle_mxfp8_quantize.argtypes = [i32, i32, i32, vp, vp, vp]
+        L.oracle_grouped_ffn_mxfp8.argtypes = [i32, i32, i32] + [vp] * 9 + [vp, i32, vp]
         L.oracle_layer_forward.argtypes = (
             [i32] * 6 + [vp, vp, vp, vp] + [i32, i32, f32, i32, i32, i32, f32] + [vp, vp, vp]
             + [i32, vp, vp, vp] + [vp, i32, vp] + [vp] * 8)
@@ -228,3 +232,81 @@ def layer_forward_cfg(cfg, inputs_np, tokens=None):
                          group_topn=cfg.group_topn, capacity_factor=cfg.capacity_factor,
                          ws_gate=i.get("ws_gate"), ws_up=i.get("ws_up"), ws_down=i.get("ws_down"),
                          tokens=tokens)
+
+
+# ---- MXFP8 (OCP Microscaling MXFP8, E4M3 elements, 32-element blocks) --------
+
+def e4m3_value(codes) -> np.ndarray:
+    """Value of each E4M3 code (float64; NaN for 0x7F / 0xFF)."""
+    c = np.asarray(codes, dtype=np.int64)
+    L = lib()
+    table = np.array([L.oracle_e4m3_value(i) for i in range(256)], np.float64)
+    return table[c]
+
+
+def mxfp8_quantize(a):
+    """MXFP8 quantisation along the last axis: (codes uint8 [..., K],
+    scales uint8 [..., K/32]); a is float32 or raw bf16 (uint16)."""
+    a, dt = _act(a)
+    K = a.shape[-1]
+    if K % 32:
+        raise ValueError("the last axis must be a multiple of 32")
+    rows = a.size // K
+    codes = np.empty(a.shape, np.uint8)
+    scales = np.empty(a.shape[:-1] + (K // 32,), np.uint8)
+    lib().oracle_mxfp8_quantize(rows, K, dt, _p(a), _p(codes), _p(scales))
+    return codes, scales
+
+
+def mxfp8_decode(codes, scales) -> np.ndarray:
+    """code * 2^(scale - 127), float64 (exact)."""
+    v = e4m3_value(codes)
+    sc = np.repeat(np.asarray(scales, dtype=np.int64), 32, axis=-1)
+    return np.ldexp(v, sc - 127)
+
+
+def grouped_ffn_mxfp8(xq, xs, offsets, w_gate, w_up, w_down, rows=None) -> np.ndarray:
+    """Grouped SwiGLU FFN on MXFP8 permuted rows; each weight is a
+    (codes, scales) pair from mxfp8_quantize ([E,I,H] gate/up, [E,H,I] down)."""
+    xq = np.ascontiguousarray(xq, dtype=np.uint8)
+    xs = np.ascontiguousarray(xs, dtype=np.uint8)
+    (gq, gs), (uq, us), (dq, ds) = [(np.ascontiguousarray(c, dtype=np.uint8),
+                                     np.ascontiguousarray(sc, dtype=np.uint8))
+                                    for c, sc in (w_gate, w_up, w_down)]
+    E, I, H = gq.shape
+    off = np.ascontiguousarray(offsets, dtype=np.int32)
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+    n = int(off[E]) if r is None else len(r)
+    y = np.empty((n, H), np.float32)
+    lib().oracle_grouped_ffn_mxfp8(E, H, I, _p(xq), _p(xs), _p(off), _p(gq), _p(gs), _p(uq), _p(us),
+                                   _p(dq), _p(ds), _p(r), 0 if r is None else len(r), _p(y))
+    return y
+
+
+def layer_forward_mxfp8(x, w_router, wq, k_max, bias=None, k_per_token=None, score=0, renorm=1,
+                        routed_scale=1.0, num_groups=1, topk_groups=1, group_topn=0,
+                        capacity_factor=0.0, shared=None, tokens=None):
+    """Layer with MXFP8 experts: routing on the high-precision x and router
+    (as layer_forward), x quantised to MXFP8 per token, the kept rows through
+    grouped_ffn_mxfp8, the weighted sum as combine.  wq / shared: dicts with
+    (codes, scales) pairs under "gate", "up", "down".  Returns dict(out=[n,H]
+    for `tokens` (or all tokens), plus the routing)."""
+    logits = router_logits(x, w_router, bias)
+    ids, gates = route(logits, k_max, k_per_token, score, renorm, routed_scale, num_groups,
+                       topk_groups, group_topn)
+    E = wq["gate"][0].shape[0]
+    d = dispatch(ids, E, capacity_factor)
+    xq, xs = mxfp8_quantize(x)
+    T, H = xq.shape
+    tok = np.arange(T, dtype=np.int32) if tokens is None else np.asarray(tokens, dtype=np.int32)
+    ros = d["row_of_slot"][tok]
+    need = np.unique(ros[ros >= 0]).astype(np.int32)
+    rt = d["row_token"][:d["R"]]
+    y = grouped_ffn_mxfp8(xq[rt], xs[rt], d["offsets"], wq["gate"], wq["up"], wq["down"], rows=need)
+    ros_c = np.where(ros >= 0, np.searchsorted(need, np.maximum(ros, 0)), -1).astype(np.int32)
+    y_sh = None
+    if shared is not None:
+        y_sh = grouped_ffn_mxfp8(xq[tok], xs[tok], np.array([0, len(tok)], np.int32),
+                                 *[tuple(a[None] for a in shared[n]) for n in ("gate", "up", "down")])
+    out = combine(y if len(need) else np.zeros((1, H), np.float32), ros_c, gates[tok], y_sh)
+    return dict(out=out, logits=logits, ids=ids, gates=gates, xq=xq, xs=xs, **d)

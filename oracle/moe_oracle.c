@@ -436,3 +436,151 @@ void oracle_layer_forward(int T, int H, int E, int I, int k_max, int dtype, cons
     free(acc);
   }
 }
+
+/* ---- MXFP8: 8-bit expert weights and activations ------------------------
+ * "LLM MoE Expert Parallel production practice" (oh-bug.com), the
+ * deployment examples, serve the experts with FP8 quantisation and keep the
+ * router in higher precision ("Expert parallelism for MoE serving", FAQ on
+ * router precision).  The pages give no scaling granularity; the format here
+ * is MXFP8 from the OCP Microscaling Formats specification v1.0: blocks of 32
+ * consecutive elements along the reduction axis share one E8M0 scale
+ * X = 2^s, and each element is an E4M3 code (1 sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits; no infinities; 0x7F and 0xFF are NaN; largest
+ * finite value 448; subnormals m * 2^-9).
+ *
+ * Value of an E4M3 code, from the bit fields. */
+double oracle_e4m3_value(int code) {
+  const int sign = (code >> 7) & 1, ex = (code >> 3) & 15, man = code & 7;
+  if (ex == 15 && man == 7) return NAN;
+  double mag = ex == 0 ? ldexp((double)man, -9) : ldexp(1.0 + man / 8.0, ex - 7);
+  return sign ? -mag : mag;
+}
+
+/* Nearest E4M3 value to q (|q| < 512 here), ties to the even code; values at
+ * or beyond 448 in magnitude saturate to 448.  The sign is kept, so a
+ * negative value that rounds to zero gives 0x80. */
+static uint8_t e4m3_encode(double q) {
+  const int neg = signbit(q) != 0;
+  double a = fabs(q);
+  uint8_t mag;
+  if (a >= 448.0) {
+    mag = 0x7E;
+  } else {
+    /* the spacing of E4M3 values around a: 2^(e-3) for a in [2^e, 2^(e+1)),
+     * e >= -6; subnormals share the spacing 2^-9 of the first binade */
+    int e2;
+    (void)frexp(a, &e2); /* a = f * 2^e2, f in [0.5, 1) */
+    int e = a > 0.0 ? e2 - 1 : -6;
+    if (e < -6) e = -6;
+    const double ulp = ldexp(1.0, e - 3);
+    const double r = rint(a / ulp) * ulp; /* default rounding: to nearest, ties to even */
+    /* the code whose value is r (r is representable) */
+    mag = 0;
+    for (int c = 0; c <= 0x7E; ++c)
+      if (oracle_e4m3_value(c) == r) {
+        mag = (uint8_t)c;
+        break;
+      }
+  }
+  return (uint8_t)(mag | (neg ? 0x80 : 0));
+}
+
+/* Quantise a [rows][cols] fp32 / bf16 matrix to MXFP8 along its rows:
+ * codes [rows][cols] (one byte each) and scales [rows][cols/32] (E8M0 bytes,
+ * value 2^(byte-127)).  Per block of 32: amax = max |v|; the shared exponent
+ * is floor(log2 amax) - 8 (8 = exponent of E4M3's largest binade), clamped to
+ * [-127, 127], and -127 for an all-zero block; each element is v / 2^s
+ * rounded to E4M3 as above.  cols must be a multiple of 32. */
+void oracle_mxfp8_quantize(int rows, int cols, int dtype, const void* src, uint8_t* codes,
+                           uint8_t* scales) {
+  const int nb = cols / 32;
+#pragma omp parallel for schedule(static)
+  for (int r = 0; r < rows; ++r) {
+    for (int b = 0; b < nb; ++b) {
+      const size_t o = (size_t)r * cols + (size_t)b * 32;
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i) {
+        const double v = fabs(elem(src, dtype, o + i));
+        if (v > amax) amax = v;
+      }
+      int s = -127;
+      if (amax > 0.0) {
+        int e2;
+        (void)frexp(amax, &e2);
+        s = (e2 - 1) - 8;
+        if (s < -127) s = -127;
+        if (s > 127) s = 127;
+      }
+      scales[(size_t)r * nb + b] = (uint8_t)(s + 127);
+      for (int i = 0; i < 32; ++i) codes[o + i] = e4m3_encode(ldexp(elem(src, dtype, o + i), -s));
+    }
+  }
+}
+
+/* element i of an MXFP8 matrix with `cols` columns: code * 2^(scale - 127) */
+static double mx_elem(const uint8_t* codes, const uint8_t* scales, int cols, size_t row, int col) {
+  return ldexp(oracle_e4m3_value(codes[row * cols + col]),
+               (int)scales[row * (cols / 32) + col / 32] - 127);
+}
+
+/* One expert's SwiGLU FFN on one MXFP8 activation row, with MXFP8 weights:
+ * a = Wg . x and u = Wu . x over the decoded values (fp64 sums); h = silu(a)*u
+ * is rounded to fp32 and re-quantised to MXFP8 along I (the input of the down
+ * projection is 8-bit as well); y = Wd . h over the decoded h (fp64).
+ * wg/wu rows e*I .. e*I+I-1 of [E*I][H]; wd rows e*H .. of [E*H][I]. */
+static void ffn_row_mxfp8(int H, int I, const uint8_t* xq, const uint8_t* xs, size_t xrow,
+                          const uint8_t* wgq, const uint8_t* wgs, const uint8_t* wuq,
+                          const uint8_t* wus, const uint8_t* wdq, const uint8_t* wds, int e,
+                          float* h32, uint8_t* hq, uint8_t* hs, double* y) {
+  for (int i = 0; i < I; ++i) {
+    double a = 0.0, u = 0.0;
+    const size_t wr = (size_t)e * I + i;
+    for (int k = 0; k < H; ++k) {
+      const double xv = mx_elem(xq, xs, H, xrow, k);
+      a += mx_elem(wgq, wgs, H, wr, k) * xv;
+      u += mx_elem(wuq, wus, H, wr, k) * xv;
+    }
+    h32[i] = (float)(a / (1.0 + exp(-a)) * u);
+  }
+  oracle_mxfp8_quantize(1, I, OR_F32, h32, hq, hs);
+  for (int c = 0; c < H; ++c) {
+    double s = 0.0;
+    const size_t wr = (size_t)e * H + c;
+    for (int i = 0; i < I; ++i) s += mx_elem(wdq, wds, I, wr, i) * mx_elem(hq, hs, I, 0, i);
+    y[c] = s;
+  }
+}
+
+/* Grouped FFN on permuted MXFP8 rows: y_perm[r] = FFN_{e(r)}(x_perm[r]) with
+ * e(r) the expert whose range [offsets[e], offsets[e+1]) holds r.  xq/xs are
+ * the quantised permuted rows ([R][H] codes, [R][H/32] scales); rows/n_rows
+ * select a subset as in oracle_grouped_ffn. */
+void oracle_grouped_ffn_mxfp8(int E, int H, int I, const uint8_t* xq, const uint8_t* xs,
+                              const int32_t* offsets, const uint8_t* wgq, const uint8_t* wgs,
+                              const uint8_t* wuq, const uint8_t* wus, const uint8_t* wdq,
+                              const uint8_t* wds, const int32_t* rows, int n_rows, float* y) {
+  int n = rows ? n_rows : offsets[E];
+#pragma omp parallel
+  {
+    float* h32 = (float*)malloc(sizeof(float) * (size_t)I);
+    uint8_t* hq = (uint8_t*)malloc((size_t)I);
+    uint8_t* hs = (uint8_t*)malloc((size_t)I / 32 + 1);
+    double* yb = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(dynamic, 1)
+    for (int q = 0; q < n; ++q) {
+      int r = rows ? rows[q] : q;
+      int e = 0;
+      while (e < E && !(r >= offsets[e] && r < offsets[e + 1])) ++e;
+      if (e == E) {
+        for (int c = 0; c < H; ++c) y[(size_t)q * H + c] = 0.0f;
+        continue;
+      }
+      ffn_row_mxfp8(H, I, xq, xs, (size_t)r, wgq, wgs, wuq, wus, wdq, wds, e, h32, hq, hs, yb);
+      for (int c = 0; c < H; ++c) y[(size_t)q * H + c] = (float)yb[c];
+    }
+    free(h32);
+    free(hq);
+    free(hs);
+    free(yb);
+  }
+}
