@@ -517,36 +517,48 @@ void oracle_mxfp8_quantize(int rows, int cols, int dtype, const void* src, uint8
   }
 }
 
-/* element i of an MXFP8 matrix with `cols` columns: code * 2^(scale - 127) */
-static double mx_elem(const uint8_t* codes, const uint8_t* scales, int cols, size_t row, int col) {
-  return ldexp(oracle_e4m3_value(codes[row * cols + col]),
-               (int)scales[row * (cols / 32) + col / 32] - 127);
+/* Decodes row `row` of an MXFP8 matrix with `cols` columns into out[cols]:
+ * element = value(code) * 2^(scale - 127), exact in fp64 (tbl[c] is the
+ * value of code c). */
+static void mx_decode_row(const double* tbl, const uint8_t* codes, const uint8_t* scales, int cols,
+                          size_t row, double* out) {
+  const uint8_t* c = codes + row * (size_t)cols;
+  const uint8_t* s = scales + row * (size_t)(cols / 32);
+  for (int b = 0; b < cols / 32; ++b) {
+    const double p = ldexp(1.0, (int)s[b] - 127);
+    for (int i = 0; i < 32; ++i) out[b * 32 + i] = tbl[c[b * 32 + i]] * p;
+  }
 }
 
 /* One expert's SwiGLU FFN on one MXFP8 activation row, with MXFP8 weights:
- * a = Wg . x and u = Wu . x over the decoded values (fp64 sums); h = silu(a)*u
- * is rounded to fp32 and re-quantised to MXFP8 along I (the input of the down
- * projection is 8-bit as well); y = Wd . h over the decoded h (fp64).
- * wg/wu rows e*I .. e*I+I-1 of [E*I][H]; wd rows e*H .. of [E*H][I]. */
-static void ffn_row_mxfp8(int H, int I, const uint8_t* xq, const uint8_t* xs, size_t xrow,
-                          const uint8_t* wgq, const uint8_t* wgs, const uint8_t* wuq,
+ * a = Wg . x and u = Wu . x over the decoded values (fp64 sums in ascending
+ * k); h = silu(a)*u is rounded to fp32 and re-quantised to MXFP8 along I (the
+ * input of the down projection is 8-bit as well); y = Wd . h over the decoded
+ * h (fp64, ascending i).  wg/wu rows e*I .. e*I+I-1 of [E*I][H]; wd rows
+ * e*H .. of [E*H][I].  Scratch: xd, wgd, wud [H]; hd, wdd [I]. */
+static void ffn_row_mxfp8(const double* tbl, int H, int I, const uint8_t* xq, const uint8_t* xs,
+                          size_t xrow, const uint8_t* wgq, const uint8_t* wgs, const uint8_t* wuq,
                           const uint8_t* wus, const uint8_t* wdq, const uint8_t* wds, int e,
-                          float* h32, uint8_t* hq, uint8_t* hs, double* y) {
+                          float* h32, uint8_t* hq, uint8_t* hs, double* xd, double* wgd,
+                          double* wud, double* hd, double* wdd, double* y) {
+  mx_decode_row(tbl, xq, xs, H, xrow, xd);
   for (int i = 0; i < I; ++i) {
-    double a = 0.0, u = 0.0;
     const size_t wr = (size_t)e * I + i;
+    mx_decode_row(tbl, wgq, wgs, H, wr, wgd);
+    mx_decode_row(tbl, wuq, wus, H, wr, wud);
+    double a = 0.0, u = 0.0;
     for (int k = 0; k < H; ++k) {
-      const double xv = mx_elem(xq, xs, H, xrow, k);
-      a += mx_elem(wgq, wgs, H, wr, k) * xv;
-      u += mx_elem(wuq, wus, H, wr, k) * xv;
+      a += wgd[k] * xd[k];
+      u += wud[k] * xd[k];
     }
     h32[i] = (float)(a / (1.0 + exp(-a)) * u);
   }
   oracle_mxfp8_quantize(1, I, OR_F32, h32, hq, hs);
+  mx_decode_row(tbl, hq, hs, I, 0, hd);
   for (int c = 0; c < H; ++c) {
+    mx_decode_row(tbl, wdq, wds, I, (size_t)e * H + c, wdd);
     double s = 0.0;
-    const size_t wr = (size_t)e * H + c;
-    for (int i = 0; i < I; ++i) s += mx_elem(wdq, wds, I, wr, i) * mx_elem(hq, hs, I, 0, i);
+    for (int i = 0; i < I; ++i) s += wdd[i] * hd[i];
     y[c] = s;
   }
 }
@@ -560,12 +572,15 @@ void oracle_grouped_ffn_mxfp8(int E, int H, int I, const uint8_t* xq, const uint
                               const uint8_t* wuq, const uint8_t* wus, const uint8_t* wdq,
                               const uint8_t* wds, const int32_t* rows, int n_rows, float* y) {
   int n = rows ? n_rows : offsets[E];
+  double tbl[256];
+  for (int c = 0; c < 256; ++c) tbl[c] = oracle_e4m3_value(c);
 #pragma omp parallel
   {
     float* h32 = (float*)malloc(sizeof(float) * (size_t)I);
     uint8_t* hq = (uint8_t*)malloc((size_t)I);
     uint8_t* hs = (uint8_t*)malloc((size_t)I / 32 + 1);
     double* yb = (double*)malloc(sizeof(double) * (size_t)H);
+    double* dec = (double*)malloc(sizeof(double) * (3 * (size_t)H + 2 * (size_t)I));
 #pragma omp for schedule(dynamic, 1)
     for (int q = 0; q < n; ++q) {
       int r = rows ? rows[q] : q;
@@ -575,12 +590,14 @@ void oracle_grouped_ffn_mxfp8(int E, int H, int I, const uint8_t* xq, const uint
         for (int c = 0; c < H; ++c) y[(size_t)q * H + c] = 0.0f;
         continue;
       }
-      ffn_row_mxfp8(H, I, xq, xs, (size_t)r, wgq, wgs, wuq, wus, wdq, wds, e, h32, hq, hs, yb);
+      ffn_row_mxfp8(tbl, H, I, xq, xs, (size_t)r, wgq, wgs, wuq, wus, wdq, wds, e, h32, hq, hs, dec,
+                    dec + H, dec + 2 * (size_t)H, dec + 3 * (size_t)H, dec + 3 * (size_t)H + I, yb);
       for (int c = 0; c < H; ++c) y[(size_t)q * H + c] = (float)yb[c];
     }
     free(h32);
     free(hq);
     free(hs);
     free(yb);
+    free(dec);
   }
 }
