@@ -22,7 +22,8 @@ MOE_FLAG_BAD_K, MOE_FLAG_BAD_EXPERT, MOE_FLAG_H_RANGE, MOE_FLAG_BAD_REPLICA = 1,
 
 EXPORTED = ("moe_workspace_size", "moe_route_topk", "moe_dispatch", "moe_map_replicas", "moe_grouped_ffn",
             "moe_combine", "moe_layer_forward", "moe_group_score_sigmoid", "moe_status_string",
-            "moe_last_hip_error", "moe_read_device_flags")
+            "moe_last_hip_error", "moe_read_device_flags", "moe_quantize_mxfp8", "moe_workspace_size_mxfp8",
+            "moe_grouped_ffn_mxfp8", "moe_layer_forward_mxfp8")
 
 
 class MoeShape(ctypes.Structure):
@@ -46,6 +47,13 @@ class MoeDebug(ctypes.Structure):
                 ("num_dropped", ctypes.c_void_p),
                 ("stage_start", ctypes.c_void_p * len(MOE_STAGES)),
                 ("stage_stop", ctypes.c_void_p * len(MOE_STAGES))]
+
+
+class MoeMxfp8Ffn(ctypes.Structure):
+    """moe_mxfp8_ffn: E4M3 codes and MX scales of the gate, up and down weights."""
+    _fields_ = [("gate", ctypes.c_void_p), ("gate_scales", ctypes.c_void_p),
+                ("up", ctypes.c_void_p), ("up_scales", ctypes.c_void_p),
+                ("down", ctypes.c_void_p), ("down_scales", ctypes.c_void_p)]
 
 
 class MoeError(RuntimeError):
@@ -81,6 +89,12 @@ def lib():
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_last_hip_error.restype = ctypes.c_int32
         L.moe_read_device_flags.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
+        i32, mp = ctypes.c_int32, ctypes.POINTER(MoeMxfp8Ffn)
+        L.moe_quantize_mxfp8.argtypes = [i32, i32, i32, vp, i32, vp, vp, vp]
+        L.moe_workspace_size_mxfp8.argtypes = [sp, ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_grouped_ffn_mxfp8.argtypes = [sp, vp, vp, i32, vp, mp, vp, vp, sz, vp]
+        L.moe_layer_forward_mxfp8.argtypes = [sp, vp, vp, vp, vp, mp, mp, vp, ctypes.POINTER(MoeDebug), vp,
+                                              sz, vp]
         for name in EXPORTED:
             if name not in ("moe_status_string", "moe_last_hip_error"):
                 getattr(L, name).restype = st
@@ -198,3 +212,73 @@ def moe_status_string(status: int) -> str:
 
 def moe_last_hip_error() -> int:
     return int(lib().moe_last_hip_error())
+
+
+# ---- MXFP8 experts -----------------------------------------------------------
+
+def moe_quantize_mxfp8(rows, cols, src_dtype, src, scale_stride, codes, scales, stream=None):
+    _check(lib().moe_quantize_mxfp8(int(rows), int(cols), int(src_dtype), _ptr(src), int(scale_stride),
+                                    _ptr(codes), _ptr(scales), _stream(stream)), "moe_quantize_mxfp8")
+
+
+def mx_scale_bytes(rows: int, cols: int, stride: Optional[int] = None) -> int:
+    """Bytes of the MX scales of a [rows][cols] matrix with the given stride."""
+    return (cols // 128) * (rows if stride is None else stride) * 4
+
+
+def quantize_mxfp8(t, scale_stride: Optional[int] = None, stream=None):
+    """(codes uint8 [..., K], scales uint8) of a bf16 / fp32 device tensor whose
+    leading dimensions are flattened into rows; the codes keep t's shape."""
+    import torch
+    K = t.shape[-1]
+    rows = t.numel() // K
+    stride = rows if scale_stride is None else scale_stride
+    codes = torch.empty(t.shape, dtype=torch.uint8, device=t.device)
+    scales = torch.empty(max(mx_scale_bytes(rows, K, stride), 16), dtype=torch.uint8, device=t.device)
+    dt = MOE_BF16 if t.dtype == torch.bfloat16 else MOE_F32
+    moe_quantize_mxfp8(rows, K, dt, t.contiguous(), stride, codes, scales, stream)
+    return codes, scales
+
+
+def mxfp8_ffn(gate, up, down, stream=None):
+    """Quantised weights of one FFN (routed [E][I][H] / [E][H][I], or shared
+    [Is][H] / [H][Is]): dict of the device tensors plus the struct under "abi"."""
+    g = quantize_mxfp8(gate, stream=stream)
+    u = quantize_mxfp8(up, stream=stream)
+    d = quantize_mxfp8(down, stream=stream)
+    st = MoeMxfp8Ffn(_ptr(g[0]), _ptr(g[1]), _ptr(u[0]), _ptr(u[1]), _ptr(d[0]), _ptr(d[1]))
+    return dict(gate=g, up=u, down=d, abi=st)
+
+
+def _mx(w):
+    if w is None:
+        return None
+    return ctypes.byref(w["abi"] if isinstance(w, dict) else w)
+
+
+def moe_workspace_size_mxfp8(shape: MoeShape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_workspace_size_mxfp8(ctypes.byref(shape), ctypes.byref(n)), "moe_workspace_size_mxfp8")
+    return int(n.value)
+
+
+def moe_grouped_ffn_mxfp8(shape, x_codes, x_scales, x_scale_stride, expert_offsets, experts, y_perm, ws,
+                          ws_bytes=None, stream=None):
+    _check(lib().moe_grouped_ffn_mxfp8(ctypes.byref(shape), _ptr(x_codes), _ptr(x_scales), int(x_scale_stride),
+                                       _ptr(expert_offsets), _mx(experts), _ptr(y_perm), _ptr(ws),
+                                       ws.numel() if ws_bytes is None else ws_bytes, _stream(stream)),
+           "moe_grouped_ffn_mxfp8")
+
+
+def moe_layer_forward_mxfp8(shape, x, w_router, router_bias, k_per_token, experts, shared, out,
+                            dbg: Optional[dict], ws, ws_bytes=None, stream=None):
+    d = None
+    if isinstance(dbg, MoeDebug):
+        d = dbg
+    elif dbg:
+        d = MoeDebug(**{k: _ptr(v) for k, v in dbg.items()})
+    _check(lib().moe_layer_forward_mxfp8(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(router_bias),
+                                         _ptr(k_per_token), _mx(experts), _mx(shared), _ptr(out),
+                                         ctypes.byref(d) if d is not None else None, _ptr(ws),
+                                         ws.numel() if ws_bytes is None else ws_bytes, _stream(stream)),
+           "moe_layer_forward_mxfp8")

@@ -35,6 +35,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kGroupM = 16;
 
@@ -79,7 +80,51 @@ __device__ __forceinline__ bool block_tile(int mtiles, int ntiles, int& m, int& 
 //            staged into LDS (exact for |w| in fp16's normal range);
 //            out y (fp32) = A.B0^T
 //   kPlain:  A = bf16 rows, B0 = bf16 weights; out fp32 = A.B0^T + bias
-enum GemmMode { kGateUp = 0, kDown = 1, kPlain = 2 };
+//   kGateUpMX: A = MXFP8 token rows, B0/B1 = MXFP8 gate/up weights; out h =
+//            silu(A.B0^T) * (A.B1^T) re-quantised to MXFP8 (codes + scales)
+//   kDownMX: A = MXFP8 h rows, B0 = MXFP8 down weights; out y (fp32)
+// The MX modes take every row length, K and lda in 16-bit units (two E4M3
+// codes), so the byte layout of their tiles is that of the bf16 modes.
+enum GemmMode { kGateUp = 0, kDown = 1, kPlain = 2, kGateUpMX = 3, kDownMX = 4 };
+
+// Scales of the MXFP8 operands (E8M0 bytes, four blocks of a 128-column group
+// per 32-bit word, words group-major: the word of group g of row r is
+// g * stride + r): token rows (sa), weight rows (sb0 / sb1; expert e's rows
+// start at e * N), and the scales of the h output (sout).
+struct MxArgs {
+  const uint8_t* sa;
+  const uint8_t* sb0;
+  const uint8_t* sb1;
+  uint8_t* sout;
+  int sa_stride, sb_stride, sout_stride;
+};
+
+// E8M0 byte of a block with maximum magnitude amax (finite, >= 0):
+// floor(log2 amax) - 8 + 127, at least 0 (also the byte of an all-zero block)
+__device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
+  const int e = (int)(__float_as_uint(amax) >> 23);
+  return e > 8 ? (uint32_t)(e - 8) : 0u;
+}
+
+// four values already divided by their block scale -> four E4M3 bytes
+// (element 0 lowest), nearest-even, saturated to +-448
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -448.f), 448.f);
+  b = fminf(fmaxf(b, -448.f), 448.f);
+  c = fminf(fmaxf(c, -448.f), 448.f);
+  d = fminf(fmaxf(d, -448.f), 448.f);
+  int p = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  p = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, p, true);
+  return (uint32_t)p;
+}
+
+// the 32 E4M3 codes of one lane for v_mfma_scale_f32_32x32x64_f8f6f4: bytes
+// 0-15 belong to the slice's first 32-element block, bytes 16-31 to its
+// second (lanes 32-63 hold the upper 16 of each block)
+__device__ __forceinline__ i32x8 cat8(u32x4 lo, u32x4 hi) {
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
 
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
   const float lo = __uint_as_float(w << 16);
@@ -110,10 +155,11 @@ constexpr int kSK = 32;            // K elements per step (and per LDS row of 4-
 constexpr int kPingRowElems = 64;  // K elements per LDS row of 8-wave blocks (128 bytes)
 
 // Rows of one stage, padded to whole wavefront loads per wave: 16 rows per
-// load for 4-wave blocks, 8 rows per load for 8-wave blocks.
+// load for 4-wave blocks; for 8-wave blocks 8 rows per load and an even
+// number of loads per wave (the stage is written in two halves).
 constexpr int gemm_stage_rows(int BM, int BNB, int MODE, int NW) {
-  return (BM + BNB * (MODE == kGateUp ? 2 : 1) + (NW == 8 ? 8 : 16) * NW - 1) /
-         ((NW == 8 ? 8 : 16) * NW) * ((NW == 8 ? 8 : 16) * NW);
+  return (BM + BNB * ((MODE == kGateUp || MODE == kGateUpMX) ? 2 : 1) + 16 * NW - 1) / (16 * NW) *
+         (16 * NW);
 }
 // Bytes of LDS one block of k_gemm_mfma<BM, BNB, MODE, NS, NW> uses.
 constexpr int gemm_lds_bytes(int BM, int BNB, int MODE, int NS, int NW) {
@@ -156,8 +202,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
     const uint16_t* __restrict__ B1, long long strideB, int N, int K, void* __restrict__ Out,
     int ldo, const float* __restrict__ bias, const MTile* __restrict__ sched,
     const int32_t* __restrict__ count, int mslots, int ntiles, int static_rows,
-    uint32_t* __restrict__ flags) {
-  constexpr bool DUAL = MODE == kGateUp;
+    uint32_t* __restrict__ flags, const MxArgs mx) {
+  constexpr bool DUAL = MODE == kGateUp || MODE == kGateUpMX;
+  constexpr bool MX = MODE == kGateUpMX || MODE == kDownMX;
   constexpr int WAVES_M = BM >= 64 ? 2 : 1, WAVES_N = NW / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BNB / WAVES_N;
   constexpr int FM = WM / 32, FN = WN / 32;
@@ -171,6 +218,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
   constexpr bool CVT_ON_READ = MODE == kDown && !PING;
   static_assert(BM % 32 == 0 && BNB % 32 == 0 && FM >= 1 && FN >= 1, "tile shape");
   static_assert(!PING || NS == 2, "ping-pong uses two LDS stages");
+  static_assert(!MX || PING, "MXFP8 modes run the 8-wave schedule");
 
   int mi, ni;
   const int mtiles = sched ? min(*count, mslots) : (static_rows + BM - 1) / BM;
@@ -215,7 +263,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
   const int fr = lane & 31;   // row of a 32-row fragment this lane feeds
   const int fk = lane >> 5;   // which 8-element K chunk (of 2) of a slice this lane feeds
 
-  u32x4 xa[2][FM], wb0[2][FN], wb1[2][DUAL ? FN : 1];
+  u32x4 xa[MX ? 1 : 2][FM], wb0[MX ? 1 : 2][FN], wb1[MX ? 1 : 2][DUAL ? FN : 1];
+  // MXFP8 fragments: both 16-byte halves of a step in one 8-register operand
+  i32x8 xa8[MX ? FM : 1], wg8[MX ? FN : 1], wu8[MX && DUAL ? FN : 1];
 #define MOE_MFMAS(set_)                                                                 \
   do {                                                                                  \
     _Pragma("unroll") for (int a = 0; a < FN; ++a) {                                    \
@@ -223,6 +273,23 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
       _Pragma("unroll") for (int b = 0; b < FM; ++b) {                                  \
         acc0[a][b] = mfma32<MODE>(w0_, xa[set_][b], acc0[a][b]);                        \
         if constexpr (DUAL) acc1[a][b] = mfma32<MODE>(wb1[set_][a], xa[set_][b], acc1[a][b]); \
+      }                                                                                 \
+    }                                                                                   \
+  } while (0)
+  // MXFP8: one v_mfma_scale_f32_32x32x64_f8f6f4 per fragment pair and step
+  // (K = 64 codes, two 32-element blocks: a lane's bytes 0-15 are its 16 codes
+  // of the first block, bytes 16-31 of the second); the scale words are
+  // pre-shifted so that byte 2h selects this lane's block of slice h.
+#define MOE_MFMAS_MX(h_)                                                                \
+  do {                                                                                  \
+    _Pragma("unroll") for (int a = 0; a < FN; ++a) {                                    \
+      _Pragma("unroll") for (int b = 0; b < FM; ++b) {                                  \
+        acc0[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                   \
+            wg8[a], xa8[b], acc0[a][b], 0, 0, 2 * (h_), scc[FM + a], 2 * (h_), scc[b]); \
+        if constexpr (DUAL)                                                             \
+          acc1[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                 \
+              wu8[a], xa8[b], acc1[a][b], 0, 0, 2 * (h_), scc[FM + FN + a], 2 * (h_),   \
+              scc[b]);                                                                  \
       }                                                                                 \
     }                                                                                   \
   } while (0)
@@ -285,12 +352,65 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
         wb1[set_][a] = *reinterpret_cast<const u32x4*>(sB1_ + r * RW + ((c_ ^ ((r >> 1) & 7)) << 3)); \
     }                                                                                   \
   } while (0)
+    // MXFP8: chunks c and c + 2 of a step (set 0 and set 1 above) form one operand
+#define MOE_READ_FRAGS_MX(step_)                                                        \
+  do {                                                                                  \
+    const uint16_t* sA_ = smem + (((step_) >> 1) & 1) * PSTAGE;                         \
+    const uint16_t* sB0_ = sA_ + BM * RW;                                               \
+    const uint16_t* sB1_ = sB0_ + BNB * RW;                                             \
+    const int c_ = ((step_) & 1) * 4 + fk;                                              \
+    _Pragma("unroll") for (int b = 0; b < FM; ++b) {                                    \
+      const int r = wm * WM + b * 32 + fr;                                              \
+      const uint16_t* row_ = sA_ + r * RW;                                              \
+      xa8[b] = cat8(*reinterpret_cast<const u32x4*>(row_ + ((c_ ^ ((r >> 1) & 7)) << 3)), \
+                    *reinterpret_cast<const u32x4*>(row_ + (((c_ + 2) ^ ((r >> 1) & 7)) << 3))); \
+    }                                                                                   \
+    _Pragma("unroll") for (int a = 0; a < FN; ++a) {                                    \
+      const int r = wn * WN + a * 32 + fr;                                              \
+      const uint16_t* row0_ = sB0_ + r * RW;                                            \
+      wg8[a] = cat8(*reinterpret_cast<const u32x4*>(row0_ + ((c_ ^ ((r >> 1) & 7)) << 3)), \
+                    *reinterpret_cast<const u32x4*>(row0_ + (((c_ + 2) ^ ((r >> 1) & 7)) << 3))); \
+      if constexpr (DUAL) {                                                             \
+        const uint16_t* row1_ = sB1_ + r * RW;                                          \
+        wu8[a] = cat8(*reinterpret_cast<const u32x4*>(row1_ + ((c_ ^ ((r >> 1) & 7)) << 3)), \
+                      *reinterpret_cast<const u32x4*>(row1_ + (((c_ + 2) ^ ((r >> 1) & 7)) << 3))); \
+      }                                                                                 \
+    }                                                                                   \
+  } while (0)
     const bool lag = wave >= NW / 2;
     const int stages = K / RW;
     int goff[NI];
 #pragma unroll
     for (int j = 0; j < NI; ++j) goff[j] = row_goff(8 * (wave + NW * j) + (lane >> 3), lane & 7);
     u32x4 ldr[2][NH];
+    // MXFP8 scale words: one per fragment (token fragments, then gate / down
+    // weight fragments, then up weight fragments) and stage.  The words of
+    // stage s+1 are loaded during the first step of stage s (scn) and become
+    // current (scc) at the start of stage s+1.
+    constexpr int NSC = MX ? FM + NB * FN : 0;
+    uint32_t scc[MX ? NSC : 1], scn[MX ? NSC : 1];
+    int sc_row[MX ? FM + FN : 1];  // gate and up weight rows coincide
+    if constexpr (MX) {
+#pragma unroll
+      for (int b = 0; b < FM; ++b) {
+        const int r = min(wm * WM + b * 32 + fr, rows - 1);
+        sc_row[b] = a_rows ? a_rows[row0 + r] : row0 + r;
+      }
+#pragma unroll
+      for (int a = 0; a < FN; ++a) sc_row[FM + a] = expert * N + min(n0 + wn * WN + a * 32 + fr, N - 1);
+    }
+#define MOE_ISSUE_SC(stage_)                                                            \
+  do {                                                                                  \
+    if constexpr (MX) {                                                                 \
+      const int st_ = (stage_) < stages ? (stage_) : stages - 1;                        \
+      _Pragma("unroll") for (int f = 0; f < NSC; ++f) {                                 \
+        const uint32_t* base_ = reinterpret_cast<const uint32_t*>(                      \
+            f < FM ? mx.sa : (f < FM + FN ? mx.sb0 : mx.sb1));                          \
+        const int strd_ = f < FM ? mx.sa_stride : mx.sb_stride;                         \
+        scn[f] = base_[(size_t)st_ * strd_ + sc_row[f < FM + FN ? f : f - FN]];         \
+      }                                                                                 \
+    }                                                                                   \
+  } while (0)
 #define MOE_ISSUE(set_, stage_, half_, jj0_, jj1_)                                      \
   do {                                                                                  \
     const int st_ = (stage_) < stages ? (stage_) : stages - 1;                          \
@@ -315,24 +435,39 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
   } while (0)
 #define MOE_PP_STEP(tt_, h_)                                                            \
   do {                                                                                  \
-    MOE_READ_FRAGS_P(0, (tt_), 0);                                                      \
-    MOE_READ_FRAGS_P(1, (tt_), 1);                                                      \
+    if constexpr (MX) {                                                                 \
+      MOE_READ_FRAGS_MX(tt_);                                                           \
+    } else {                                                                            \
+      MOE_READ_FRAGS_P(0, (tt_), 0);                                                    \
+      MOE_READ_FRAGS_P(1, (tt_), 1);                                                    \
+    }                                                                                   \
     MOE_STORE(h_, ((tt_) >> 1) + 1, h_);                                                \
     __builtin_amdgcn_sched_barrier(0);                                                  \
     MOE_WAIT_LGKM0();                                                                   \
     raw_barrier();                                                                      \
     __builtin_amdgcn_sched_barrier(0);                                                  \
     __builtin_amdgcn_s_setprio(1);                                                      \
+    if constexpr (MX) {                                                                 \
+      if ((h_) == 0) {                                                                  \
+        _Pragma("unroll") for (int f = 0; f < NSC; ++f) scc[f] = scn[f] >> (8 * fk);    \
+        MOE_ISSUE_SC(((tt_) >> 1) + 1);                                                 \
+      }                                                                                 \
+    }                                                                                   \
     MOE_ISSUE(h_, ((tt_) >> 1) + 2, h_, 0, NH);                                         \
-    MOE_MFMAS(0);                                                                       \
-    MOE_MFMAS(1);                                                                       \
-    __builtin_amdgcn_sched_group_barrier(0x020, NH, 3);                                 \
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NMF, 3);                            \
+    if constexpr (MX) {                                                                 \
+      MOE_MFMAS_MX(h_);                                                                 \
+    } else {                                                                            \
+      MOE_MFMAS(0);                                                                     \
+      MOE_MFMAS(1);                                                                     \
+    }                                                                                   \
+    __builtin_amdgcn_sched_group_barrier(0x020, NH + ((h_) == 0 ? NSC : 0), 3);         \
+    __builtin_amdgcn_sched_group_barrier(0x008, MX ? NMF : 2 * NMF, 3);                 \
     __builtin_amdgcn_s_setprio(0);                                                      \
     __builtin_amdgcn_sched_barrier(0);                                                  \
     raw_barrier();                                                                      \
     __builtin_amdgcn_sched_barrier(0);                                                  \
   } while (0)
+    MOE_ISSUE_SC(0);
     MOE_ISSUE(0, 0, 0, 0, NH);
     MOE_ISSUE(1, 0, 1, 0, NH);
     MOE_STORE(0, 0, 0);
@@ -349,6 +484,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
     }
     if (!lag) raw_barrier();
 #undef MOE_PP_STEP
+#undef MOE_READ_FRAGS_MX
+#undef MOE_ISSUE_SC
 #undef MOE_STORE
 #undef MOE_ISSUE
 #undef MOE_READ_FRAGS_P
@@ -446,11 +583,46 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
 #undef MOE_LOAD_STAGE
   }
 #undef MOE_MFMAS
+#undef MOE_MFMAS_MX
   __builtin_amdgcn_s_waitcnt(0);  // drain the clamped tail loads before the block ends
 
   // epilogue: accumulator q of fragment (a, b) is output column
   // n = a*32 + 8*(q/4) + 4*(lane/32) + q%4 of token row m = b*32 + lane%32
   bool overflow = false;
+  if constexpr (MODE == kGateUpMX) {
+    // h of one 32-column block of a token row sits in lanes l and l^32 (16
+    // each): its maximum magnitude sets the block's E8M0 scale, and each lane
+    // writes its 16 codes (4 words) and lane l < 32 the scale byte
+#pragma unroll
+    for (int b = 0; b < FM; ++b) {
+      const int m = wm * WM + b * 32 + fr;
+#pragma unroll
+      for (int a = 0; a < FN; ++a) {
+        const int nb = n0 + wn * WN + a * 32;
+        float hv[16];
+        float amax = 0.f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          hv[q] = silu_mul(acc0[a][b][q], acc1[a][b][q]);
+          amax = fmaxf(amax, fabsf(hv[q]));
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        if (m >= rows || nb >= N) continue;
+        overflow |= !(amax <= 3.402823466e38f);
+        const uint32_t sb = mx_scale_byte(amax);
+        const int sh = 127 - (int)sb;
+        uint8_t* dst = static_cast<uint8_t*>(Out) + (size_t)(row0 + m) * ldo + nb + 4 * fk;
+#pragma unroll
+        for (int qi = 0; qi < 4; ++qi)
+          *reinterpret_cast<uint32_t*>(dst + 8 * qi) =
+              e4m3x4(ldexpf(hv[4 * qi], sh), ldexpf(hv[4 * qi + 1], sh),
+                     ldexpf(hv[4 * qi + 2], sh), ldexpf(hv[4 * qi + 3], sh));
+        if (fk == 0)
+          mx.sout[((size_t)(nb >> 7) * mx.sout_stride + row0 + m) * 4 + ((nb >> 5) & 3)] =
+              (uint8_t)sb;
+      }
+    }
+  } else {
 #pragma unroll
   for (int b = 0; b < FM; ++b) {
     const int m = wm * WM + b * 32 + fr;
@@ -495,6 +667,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
         }
       }
     }
+  }
   }
   if constexpr (DUAL) {
     if (overflow && flags) atomicOr(flags, (uint32_t)MOE_FLAG_H_RANGE);
@@ -588,7 +761,7 @@ hipError_t launch_mfma(const void* A, const int32_t* a_rows, int lda, const void
                        const void* B1, int N, int K,
                        void* out, int ldo, const float* bias, const MTile* sched,
                        const int32_t* count, int mslots, int static_rows, uint32_t* flags,
-                       hipStream_t st) {
+                       hipStream_t st, const MxArgs mx = MxArgs{}) {
   constexpr int lds = gemm_lds_bytes(BM, BNB, MODE, NS, NW);
   static_assert(lds <= 160 * 1024, "LDS");
   if constexpr (lds > 65536) {
@@ -612,7 +785,7 @@ hipError_t launch_mfma(const void* A, const int32_t* a_rows, int lda, const void
                      static_cast<const uint16_t*>(A), a_rows, lda,
                      static_cast<const uint16_t*>(B0), static_cast<const uint16_t*>(B1),
                      (long long)N * K, N, K, out, ldo, bias,
-                     sched, count, mslots, ntiles, static_rows, flags);
+                     sched, count, mslots, ntiles, static_rows, flags, mx);
   return hipGetLastError();
 }
 
@@ -687,6 +860,52 @@ hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int 
                                          mslots, static_rows, nullptr, st);
   return launch_mfma<32, 128, kPlain, 4, 4>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, bias, sched, count,
                                       mslots, static_rows, nullptr, st);
+}
+
+// MXFP8 gate/up + SwiGLU: A = E4M3 token rows (K = H codes each, gathered
+// through a_rows when given; scales sa, stride sa_stride), Bg/Bu = E4M3 weights
+// [E][N][K] (scales stride sb_stride = E * N); h = MXFP8 codes [rows][N] with
+// scales hsc (stride hs_stride).  bm: 256, 128 or 32 (the 32-row tiles span
+// 256 weight rows so that eight wavefronts still split the columns).
+hipError_t launch_gemm_gateup_mx(int bm, const void* A, const int32_t* a_rows, const uint8_t* sa,
+                                 int sa_stride, const void* Bg, const uint8_t* sbg, const void* Bu,
+                                 const uint8_t* sbu, int sb_stride, int N, int K, void* h,
+                                 uint8_t* hsc, int hs_stride, const MTile* sched,
+                                 const int32_t* count, int max_tiles, int static_rows,
+                                 uint32_t* flags, hipStream_t st) {
+  const int mslots = sched ? max_tiles : (static_rows + bm - 1) / bm;
+  if (mslots == 0) return hipSuccess;
+  const MxArgs mx{sa, sbg, sbu, hsc, sa_stride, sb_stride, hs_stride};
+  const int K2 = K / 2;  // 16-bit units
+  if (bm == 256)
+    return launch_mfma<256, 128, kGateUpMX, 2, 8>(A, a_rows, K2, Bg, Bu, N, K2, h, N, nullptr, sched,
+                                                  count, mslots, static_rows, flags, st, mx);
+  if (bm == 128)
+    return launch_mfma<128, 128, kGateUpMX, 2, 8>(A, a_rows, K2, Bg, Bu, N, K2, h, N, nullptr, sched,
+                                                  count, mslots, static_rows, flags, st, mx);
+  return launch_mfma<32, 256, kGateUpMX, 2, 8>(A, a_rows, K2, Bg, Bu, N, K2, h, N, nullptr, sched,
+                                               count, mslots, static_rows, flags, st, mx);
+}
+
+// MXFP8 down projection: A = MXFP8 h rows [rows][K] (scales hsc, stride
+// hs_stride), B = E4M3 weights [E][N][K] (scales sb, stride sb_stride = E * N);
+// Y fp32 [rows][ldy].
+hipError_t launch_gemm_down_mx(int bm, const void* A, const uint8_t* hsc, int hs_stride,
+                               const void* B, const uint8_t* sb, int sb_stride, int N, int K,
+                               float* Y, int ldy, const MTile* sched, const int32_t* count,
+                               int max_tiles, int static_rows, hipStream_t st) {
+  const int mslots = sched ? max_tiles : (static_rows + bm - 1) / bm;
+  if (mslots == 0) return hipSuccess;
+  const MxArgs mx{hsc, sb, nullptr, nullptr, hs_stride, sb_stride, 0};
+  const int K2 = K / 2;
+  if (bm == 256)
+    return launch_mfma<256, 256, kDownMX, 2, 8>(A, nullptr, K2, B, nullptr, N, K2, Y, ldy, nullptr,
+                                                sched, count, mslots, static_rows, nullptr, st, mx);
+  if (bm == 128)
+    return launch_mfma<128, 128, kDownMX, 2, 8>(A, nullptr, K2, B, nullptr, N, K2, Y, ldy, nullptr,
+                                                sched, count, mslots, static_rows, nullptr, st, mx);
+  return launch_mfma<32, 256, kDownMX, 2, 8>(A, nullptr, K2, B, nullptr, N, K2, Y, ldy, nullptr,
+                                             sched, count, mslots, static_rows, nullptr, st, mx);
 }
 
 }  // namespace moe

@@ -84,6 +84,26 @@ inline moe_status need4(const void* p) {
 }
 inline moe_status opt4(const void* p) { return p ? need4(p) : MOE_OK; }
 
+// MXFP8 layers: bf16 x and router, 128-column groups along every K
+moe_status check_mx_shape(const moe_shape* s) {
+  MOE_TRY(check_shape(s));
+  if (s->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (s->hidden % 128 || s->intermediate % 128 || s->shared_intermediate % 128)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_mx_ffn(const moe_mxfp8_ffn* w) {
+  if (!w) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(need(w->gate));
+  MOE_TRY(need(w->gate_scales));
+  MOE_TRY(need(w->up));
+  MOE_TRY(need(w->up_scales));
+  MOE_TRY(need(w->down));
+  MOE_TRY(need(w->down_scales));
+  return MOE_OK;
+}
+
 // Records the stage event when the caller asked for it.
 inline hipError_t stage_mark(const moe_debug* d, int stage, bool start, hipStream_t st) {
   if (!d) return hipSuccess;
@@ -118,11 +138,11 @@ GemmPlan choose_gemm_plan(const moe_shape& s) {
   return p;
 }
 
-WsLayout plan_workspace(const moe_shape& s) {
+WsLayout plan_workspace(const moe_shape& s, bool mx) {
   WsLayout w{};
   const size_t T = (size_t)s.num_tokens, E = (size_t)s.num_experts, k = (size_t)s.top_k;
   const size_t H = (size_t)s.hidden, I = (size_t)s.intermediate, Is = (size_t)s.shared_intermediate;
-  const size_t eb = (size_t)elem_bytes(s.act_dtype);
+  const size_t eb = mx ? 1 : (size_t)elem_bytes(s.act_dtype);  // bytes of an h element
   const size_t slots = T * k;
   const GemmPlan gp = choose_gemm_plan(s);
   w.n_dispatch_tiles = (int)((slots + kDispatchTileSlots - 1) / kDispatchTileSlots);
@@ -159,6 +179,12 @@ WsLayout plan_workspace(const moe_shape& s) {
   w.y = take(slots * H * 4);
   w.hs = take(T * Is * eb);
   w.ys = take(Is ? T * H * 4 : 0);
+  if (mx) {
+    w.xq = take(T * H);
+    w.xsc = take(T * H / 32);
+    w.hsc = take(slots * I / 32);
+    w.hssc = take(T * Is / 32);
+  }
   w.total = o;
   return w;
 }
@@ -211,6 +237,61 @@ moe_status run_ffn(const moe_shape& s, const void* x_perm, const int32_t* a_rows
     MOE_HIP(launch_gemm_plain(s.act_dtype, gp.bm_small, true, h, I, w_down, H, I, nullptr, y, H,
                               ss, cnt + 1, L.max_tiles_small, 0, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_DOWN, false, st));
+  return MOE_OK;
+}
+
+// MXFP8 S7-S8: xq rows (gathered through a_rows when given) with scales of
+// stride xs_stride; h codes and scales (stride T*top_k) in the workspace.
+moe_status run_ffn_mx(const moe_shape& s, const void* xq, const int32_t* a_rows,
+                      const uint8_t* xsc, int xs_stride, const int32_t* offsets,
+                      const moe_mxfp8_ffn& w, float* y, void* ws, const WsLayout& L,
+                      hipStream_t st, const moe_debug* dbg = nullptr) {
+  const GemmPlan gp = choose_gemm_plan(s);
+  const int E = s.num_experts, H = s.hidden, I = s.intermediate;
+  const int slots = s.num_tokens * s.top_k;
+  MTile* sb = at<MTile>(ws, L.sched_big);
+  MTile* ss = at<MTile>(ws, L.sched_small);
+  int32_t* cnt = at<int32_t>(ws, L.sched_count);
+  uint32_t* flags = at<uint32_t>(ws, L.flags);
+  MOE_HIP(launch_build_schedule(offsets, E, gp, sb, L.max_tiles_big, ss, L.max_tiles_small, cnt,
+                                st));
+  void* h = at<void>(ws, L.h);
+  uint8_t* hsc = at<uint8_t>(ws, L.hsc);
+  const auto gsc = w.gate_scales, usc = w.up_scales, dsc = w.down_scales;
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_GATE_UP, true, st));
+  if (gp.has_big())
+    MOE_HIP(launch_gemm_gateup_mx(gp.bm_big, xq, a_rows, xsc, xs_stride, w.gate, gsc, w.up, usc,
+                                  E * I, I, H, h, hsc, slots, sb, cnt, L.max_tiles_big, 0, flags,
+                                  st));
+  if (gp.has_small())
+    MOE_HIP(launch_gemm_gateup_mx(gp.bm_small, xq, a_rows, xsc, xs_stride, w.gate, gsc, w.up, usc,
+                                  E * I, I, H, h, hsc, slots, ss, cnt + 1, L.max_tiles_small, 0,
+                                  flags, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_GATE_UP, false, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_DOWN, true, st));
+  if (gp.has_big())
+    MOE_HIP(launch_gemm_down_mx(gp.bm_big, h, hsc, slots, w.down, dsc, E * H, H, I, y, H, sb, cnt,
+                                L.max_tiles_big, 0, st));
+  if (gp.has_small())
+    MOE_HIP(launch_gemm_down_mx(gp.bm_small, h, hsc, slots, w.down, dsc, E * H, H, I, y, H, ss,
+                                cnt + 1, L.max_tiles_small, 0, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_DOWN, false, st));
+  return MOE_OK;
+}
+
+// MXFP8 shared expert on all T quantised rows (scales of stride T)
+moe_status run_shared_mx(const moe_shape& s, const void* xq, const uint8_t* xsc,
+                         const moe_mxfp8_ffn& w, void* ws, const WsLayout& L, hipStream_t st) {
+  const int T = s.num_tokens, H = s.hidden, Is = s.shared_intermediate;
+  const int bm = T >= 2048 ? 256 : (T >= 128 ? 128 : 32);
+  void* hs = at<void>(ws, L.hs);
+  uint8_t* hssc = at<uint8_t>(ws, L.hssc);
+  float* ys = at<float>(ws, L.ys);
+  MOE_HIP(launch_gemm_gateup_mx(bm, xq, nullptr, xsc, T, w.gate, w.gate_scales, w.up, w.up_scales,
+                                Is, Is, H, hs, hssc, T, nullptr, nullptr, 0, T,
+                                at<uint32_t>(ws, L.flags), st));
+  MOE_HIP(launch_gemm_down_mx(bm, hs, hssc, T, w.down, w.down_scales, H, H, Is, ys, H, nullptr,
+                              nullptr, 0, T, st));
   return MOE_OK;
 }
 
@@ -439,6 +520,122 @@ moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* 
   MOE_HIP(stage_mark(dbg, MOE_STAGE_SHARED, true, st));
   if (s.shared_intermediate > 0) {
     MOE_TRY(run_shared(s, x, ws_gate, ws_up, ws_down, ws, L, st));
+    ys = at<float>(ws, L.ys);
+  }
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_SHARED, false, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_COMBINE, true, st));
+  MOE_HIP(launch_combine(s, y, ros, gates, ys, out, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_COMBINE, false, st));
+  return MOE_OK;
+}
+
+moe_status moe_quantize_mxfp8(int32_t rows, int32_t cols, int32_t src_dtype, const void* src,
+                              int32_t scale_stride, void* codes, uint8_t* scales, void* stream) {
+  if (rows < 0 || cols <= 0 || scale_stride < rows) return MOE_ERR_INVALID_ARG;
+  if (src_dtype != MOE_BF16 && src_dtype != MOE_F32) return MOE_ERR_INVALID_ARG;
+  if (cols % 128) return MOE_ERR_UNSUPPORTED;
+  MOE_TRY(need(src));
+  MOE_TRY(need(codes));
+  MOE_TRY(need(scales));
+  if (rows == 0) return MOE_OK;
+  MOE_HIP(launch_quant_mxfp8(src_dtype, src, rows, cols, scale_stride, static_cast<uint8_t*>(codes),
+                             scales, nullptr, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_workspace_size_mxfp8(const moe_shape* shape, size_t* bytes) {
+  MOE_TRY(check_mx_shape(shape));
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = plan_workspace(*shape, true).total;
+  return MOE_OK;
+}
+
+moe_status moe_grouped_ffn_mxfp8(const moe_shape* shape, const void* x_codes,
+                                 const uint8_t* x_scales, int32_t x_scale_stride,
+                                 const int32_t* expert_offsets, const moe_mxfp8_ffn* experts,
+                                 float* y_perm, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_mx_shape(shape));
+  const moe_shape& s = *shape;
+  MOE_TRY(need(x_codes));
+  MOE_TRY(need(x_scales));
+  MOE_TRY(need4(expert_offsets));
+  MOE_TRY(check_mx_ffn(experts));
+  MOE_TRY(need(y_perm));
+  MOE_TRY(need(ws));
+  if ((long long)x_scale_stride < (long long)s.num_tokens * s.top_k) return MOE_ERR_INVALID_ARG;
+  const WsLayout L = plan_workspace(s, true);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (s.num_tokens == 0) return MOE_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  MOE_HIP(launch_clear_flags(at<uint32_t>(ws, L.flags), st));
+  return run_ffn_mx(s, x_codes, nullptr, x_scales, x_scale_stride, expert_offsets, *experts,
+                    y_perm, ws, L, st);
+}
+
+moe_status moe_layer_forward_mxfp8(const moe_shape* shape, const void* x, const void* w_router,
+                                   const float* router_bias, const int32_t* k_per_token,
+                                   const moe_mxfp8_ffn* experts, const moe_mxfp8_ffn* shared,
+                                   void* out, const moe_debug* dbg, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  MOE_TRY(check_mx_shape(shape));
+  const moe_shape& s = *shape;
+  MOE_TRY(need(x));
+  MOE_TRY(need(w_router));
+  MOE_TRY(opt4(router_bias));
+  MOE_TRY(opt4(k_per_token));
+  MOE_TRY(check_mx_ffn(experts));
+  if (s.shared_intermediate > 0) MOE_TRY(check_mx_ffn(shared));
+  MOE_TRY(need(out));
+  MOE_TRY(need(ws));
+  if (dbg) {
+    if (dbg->logits) MOE_TRY(need(dbg->logits));
+    MOE_TRY(opt4(dbg->topk_ids));
+    MOE_TRY(opt4(dbg->topk_gates));
+    MOE_TRY(opt4(dbg->expert_counts));
+    MOE_TRY(opt4(dbg->expert_offsets));
+    MOE_TRY(opt4(dbg->row_of_slot));
+    MOE_TRY(opt4(dbg->num_dropped));
+  }
+  const WsLayout L = plan_workspace(s, true);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (s.num_tokens == 0) return MOE_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int T = s.num_tokens;
+
+  float* logits = (dbg && dbg->logits) ? dbg->logits : at<float>(ws, L.logits);
+  int32_t* ids = (dbg && dbg->topk_ids) ? dbg->topk_ids : at<int32_t>(ws, L.ids);
+  float* gates = (dbg && dbg->topk_gates) ? dbg->topk_gates : at<float>(ws, L.gates);
+  int32_t* counts = (dbg && dbg->expert_counts) ? dbg->expert_counts : at<int32_t>(ws, L.counts);
+  int32_t* offsets = (dbg && dbg->expert_offsets) ? dbg->expert_offsets : at<int32_t>(ws, L.offsets);
+  int32_t* ros = (dbg && dbg->row_of_slot) ? dbg->row_of_slot : at<int32_t>(ws, L.row_of_slot);
+  int32_t* nd = (dbg && dbg->num_dropped) ? dbg->num_dropped : at<int32_t>(ws, L.num_dropped);
+  uint32_t* flags = at<uint32_t>(ws, L.flags);
+  int32_t* row_token = at<int32_t>(ws, L.row_token);
+  float* y = at<float>(ws, L.y);
+  uint8_t* xq = at<uint8_t>(ws, L.xq);
+  uint8_t* xsc = at<uint8_t>(ws, L.xsc);
+
+  MOE_HIP(launch_clear_flags(flags, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTER, true, st));
+  MOE_TRY(run_router(s, x, w_router, router_bias, logits, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTER, false, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTE, true, st));
+  MOE_HIP(launch_route_topk(s, logits, k_per_token, ids, gates, flags, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTE, false, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_DISPATCH, true, st));
+  MOE_HIP(launch_dispatch(s, ids, counts, offsets, ros, row_token, nd,
+                          at<int32_t>(ws, L.tile_counts), L.n_dispatch_tiles, flags, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_DISPATCH, false, st));
+  // S6: the dispatch payload is x quantised once per token; the row gather
+  // itself is fused into the gate/up GEMM's tile loads
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_GATHER, true, st));
+  MOE_HIP(launch_quant_mxfp8(MOE_BF16, x, T, s.hidden, T, xq, xsc, flags, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_GATHER, false, st));
+  MOE_TRY(run_ffn_mx(s, xq, row_token, xsc, T, offsets, *experts, y, ws, L, st, dbg));
+  const float* ys = nullptr;
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_SHARED, true, st));
+  if (s.shared_intermediate > 0) {
+    MOE_TRY(run_shared_mx(s, xq, xsc, *shared, ws, L, st));
     ys = at<float>(ws, L.ys);
   }
   MOE_HIP(stage_mark(dbg, MOE_STAGE_SHARED, false, st));

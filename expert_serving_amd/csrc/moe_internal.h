@@ -23,9 +23,12 @@ struct MTile {
 };
 
 // Byte offsets of every region inside the caller's workspace.
+// MXFP8 layers add the quantised x (xq, scales xsc with stride T) and the
+// scales of h (hsc, stride T*top_k) and of the shared expert's h (hssc,
+// stride T); h and hs then hold one-byte codes.
 struct WsLayout {
   size_t flags, logits, ids, gates, counts, offsets, tile_counts, row_of_slot, row_token,
-      num_dropped, sched_big, sched_small, sched_count, h, y, hs, ys, total;
+      num_dropped, sched_big, sched_small, sched_count, h, y, hs, ys, xq, xsc, hsc, hssc, total;
   int n_dispatch_tiles;
   int max_tiles_big, max_tiles_small;
 };
@@ -42,7 +45,7 @@ struct GemmPlan {
 };
 
 GemmPlan choose_gemm_plan(const moe_shape& s);
-WsLayout plan_workspace(const moe_shape& s);
+WsLayout plan_workspace(const moe_shape& s, bool mx = false);
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -95,6 +98,23 @@ hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int 
                              const void* B, int N, int K, const float* bias, float* Y, int ldy,
                              const MTile* sched, const int32_t* count, int max_tiles,
                              int static_rows, hipStream_t st);
+
+// MXFP8 path (codes + E8M0 scales; scale words group-major, see mxfp8.hip).
+// Quantises rows x cols (cols a multiple of 128) of bf16 / fp32 src; inf/NaN
+// inputs set MOE_FLAG_H_RANGE when flags is given.
+hipError_t launch_quant_mxfp8(int src_dtype, const void* src, int rows, int cols, int stride,
+                              uint8_t* codes, uint8_t* scales, uint32_t* flags, hipStream_t st);
+// gate/up + SwiGLU with h re-quantised to MXFP8; bm 256 / 128 / 32
+hipError_t launch_gemm_gateup_mx(int bm, const void* A, const int32_t* a_rows, const uint8_t* sa,
+                                 int sa_stride, const void* Bg, const uint8_t* sbg, const void* Bu,
+                                 const uint8_t* sbu, int sb_stride, int N, int K, void* h,
+                                 uint8_t* hsc, int hs_stride, const MTile* sched,
+                                 const int32_t* count, int max_tiles, int static_rows,
+                                 uint32_t* flags, hipStream_t st);
+hipError_t launch_gemm_down_mx(int bm, const void* A, const uint8_t* hsc, int hs_stride,
+                               const void* B, const uint8_t* sb, int sb_stride, int N, int K,
+                               float* Y, int ldy, const MTile* sched, const int32_t* count,
+                               int max_tiles, int static_rows, hipStream_t st);
 
 // Row-tile height the GEMM launchers use for a dtype and a requested height.
 int gemm_tile_rows(int dtype, int bm_hint);

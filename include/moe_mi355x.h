@@ -68,7 +68,8 @@ typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
 /* device flag bits (moe_read_device_flags) */
 #define MOE_FLAG_BAD_K 1u       /* some k_per_token[t] outside [1, top_k]: token routed nowhere */
 #define MOE_FLAG_BAD_EXPERT 2u  /* some topk_ids entry outside [-1, E): slot treated as unused  */
-#define MOE_FLAG_H_RANGE 4u     /* some SwiGLU activation h exceeded fp16 range (bf16 layers)   */
+#define MOE_FLAG_H_RANGE 4u     /* some SwiGLU activation h exceeded fp16 range (bf16 layers)
+                                   or was not finite (MXFP8 layers)                           */
 #define MOE_FLAG_BAD_REPLICA 8u /* a routed expert without a replica, or a replica id out of range */
 
 typedef struct {
@@ -226,6 +227,71 @@ moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* 
                              const void* ws_gate, const void* ws_up, const void* ws_down,
                              void* out, const moe_debug* dbg, void* ws, size_t ws_bytes,
                              void* stream);
+
+/* ---- 8-bit experts (MXFP8) ---------------------------------------------
+ * The pages serve the experts with FP8 quantisation and keep the router in
+ * higher precision ("LLM MoE Expert Parallel production practice", deployment
+ * examples; "Expert parallelism for MoE serving", FAQ on router precision);
+ * they fix no scaling granularity.  The format is MXFP8 of the OCP
+ * Microscaling Formats specification v1.0, whose 32-element block scales
+ * CDNA4's scaled MFMA applies in hardware:
+ *   - each run of 32 consecutive elements of a row (the reduction axis of the
+ *     GEMM that reads it) shares one E8M0 scale byte, value 2^(byte - 127);
+ *   - each element is an E4M3 byte (OCP FP8: exponent bias 7, largest finite
+ *     448, no infinities, 0x7F / 0xFF NaN);
+ *   - quantisation: s = floor(log2 amax) - 8, at least -127 (byte 0 for an
+ *     all-zero block); element = v / 2^s rounded to the nearest E4M3 value,
+ *     ties to even, saturated to +-448, sign kept (a negative value that
+ *     rounds to zero is 0x80).
+ * Codes are [rows][cols] bytes.  Scales "with stride S" (S >= rows): the
+ * four scales of columns [128 g, 128 g + 128) of row r form 32-bit word
+ * g * S + r, the block of columns [128 g + 32 i, +32) in byte i.  cols must
+ * be a multiple of 128.  The MXFP8 layer keeps x and the router in bf16 for
+ * routing, quantises x per token, and re-quantises h per token along I
+ * inside the gate/up GEMM.  H, I and Is must be multiples of 128, act_dtype
+ * MOE_BF16. */
+typedef struct {
+  const void* gate;            /* [E][I][H] codes                      */
+  const uint8_t* gate_scales;  /* MX scales, stride E*I                */
+  const void* up;              /* [E][I][H] codes                      */
+  const uint8_t* up_scales;    /* stride E*I                           */
+  const void* down;            /* [E][H][I] codes                      */
+  const uint8_t* down_scales;  /* stride E*H                           */
+} moe_mxfp8_ffn;
+/* The shared expert uses the same struct with E = 1: gate/up [Is][H] (scale
+ * stride Is), down [H][Is] (scale stride H). */
+
+/* Quantises src [rows][cols] (src_dtype MOE_BF16 or MOE_F32) to MXFP8 codes
+ * [rows][cols] and scales with stride scale_stride >= rows.  Inputs are
+ * assumed finite (inf / NaN give unspecified codes).  Expert weights are
+ * quantised once with this call (rows = E*I or E*H). */
+moe_status moe_quantize_mxfp8(int32_t rows, int32_t cols, int32_t src_dtype, const void* src,
+                              int32_t scale_stride, void* codes, uint8_t* scales, void* stream);
+
+/* Workspace of the two MXFP8 calls below (host only). */
+moe_status moe_workspace_size_mxfp8(const moe_shape* shape, size_t* bytes);
+
+/* S7-S8 with MXFP8 operands: as moe_grouped_ffn, with x_perm given as MXFP8
+ * codes [T*top_k][H] and scales with stride x_scale_stride >= T*top_k; the
+ * dot products accumulate the decoded products in fp32; h = silu(a) * u is
+ * rounded from fp32 to MXFP8 along I (blocks of 32 per row) before the down
+ * projection; y_perm fp32.  A non-finite h sets
+ * MOE_FLAG_H_RANGE.  Clears the workspace flag word. */
+moe_status moe_grouped_ffn_mxfp8(const moe_shape* shape, const void* x_codes,
+                                 const uint8_t* x_scales, int32_t x_scale_stride,
+                                 const int32_t* expert_offsets, const moe_mxfp8_ffn* experts,
+                                 float* y_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* The whole layer with MXFP8 experts: S1-S5 as moe_layer_forward on the bf16
+ * x and router; x quantised to MXFP8 per token (timed as the gather stage:
+ * it is the dispatch payload); S7-S8 as moe_grouped_ffn_mxfp8 on the
+ * gathered rows; the shared expert (shape->shared_intermediate > 0, `shared`
+ * then required) on the quantised x; S10 as moe_combine. */
+moe_status moe_layer_forward_mxfp8(const moe_shape* shape, const void* x, const void* w_router,
+                                   const float* router_bias, const int32_t* k_per_token,
+                                   const moe_mxfp8_ffn* experts, const moe_mxfp8_ffn* shared,
+                                   void* out, const moe_debug* dbg, void* ws, size_t ws_bytes,
+                                   void* stream);
 
 /* The fp32 logistic function that group-limited routing sums into group
  * scores, evaluated elementwise: y[i] = sigma(x[i]) for i < n (device

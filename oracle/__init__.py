@@ -64,7 +64,7 @@ def lib():
         L.oracle_e4m3_value.argtypes = [i32]
         L.oracle_e4m3_value.restype = ctypes.c_double
         L.oracle_mxfp8_quantize.argtypes = [i32, i32, i32, vp, vp, vp]
-        L.oracle_grouped_ffn_mxfp8.argtypes = [i32, i32, i32] + [vp] * 9 + [vp, i32, vp]
+        L.oracle_grouped_ffn_mxfp8.argtypes = [i32, i32, i32] + [vp] * 9 + [vp, i32, vp, vp]
         L.oracle_layer_forward.argtypes = (
             [i32] * 6 + [vp, vp, vp, vp] + [i32, i32, f32, i32, i32, i32, f32] + [vp, vp, vp]
             + [i32, vp, vp, vp] + [vp, i32, vp] + [vp] * 8)
@@ -265,9 +265,11 @@ def mxfp8_decode(codes, scales) -> np.ndarray:
     return np.ldexp(v, sc - 127)
 
 
-def grouped_ffn_mxfp8(xq, xs, offsets, w_gate, w_up, w_down, rows=None) -> np.ndarray:
+def grouped_ffn_mxfp8(xq, xs, offsets, w_gate, w_up, w_down, rows=None, return_h=False):
     """Grouped SwiGLU FFN on MXFP8 permuted rows; each weight is a
-    (codes, scales) pair from mxfp8_quantize ([E,I,H] gate/up, [E,H,I] down)."""
+    (codes, scales) pair from mxfp8_quantize ([E,I,H] gate/up, [E,H,I] down).
+    Returns y [n,H] fp32, or (y, h) with h [n,I] the fp32 SwiGLU activations
+    before their MXFP8 rounding when return_h."""
     xq = np.ascontiguousarray(xq, dtype=np.uint8)
     xs = np.ascontiguousarray(xs, dtype=np.uint8)
     (gq, gs), (uq, us), (dq, ds) = [(np.ascontiguousarray(c, dtype=np.uint8),
@@ -278,9 +280,10 @@ def grouped_ffn_mxfp8(xq, xs, offsets, w_gate, w_up, w_down, rows=None) -> np.nd
     r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
     n = int(off[E]) if r is None else len(r)
     y = np.empty((n, H), np.float32)
+    h = np.empty((n, I), np.float32) if return_h else None
     lib().oracle_grouped_ffn_mxfp8(E, H, I, _p(xq), _p(xs), _p(off), _p(gq), _p(gs), _p(uq), _p(us),
-                                   _p(dq), _p(ds), _p(r), 0 if r is None else len(r), _p(y))
-    return y
+                                   _p(dq), _p(ds), _p(r), 0 if r is None else len(r), _p(y), _p(h))
+    return (y, h) if return_h else y
 
 
 def layer_forward_mxfp8(x, w_router, wq, k_max, bias=None, k_per_token=None, score=0, renorm=1,
@@ -290,7 +293,10 @@ def layer_forward_mxfp8(x, w_router, wq, k_max, bias=None, k_per_token=None, sco
     (as layer_forward), x quantised to MXFP8 per token, the kept rows through
     grouped_ffn_mxfp8, the weighted sum as combine.  wq / shared: dicts with
     (codes, scales) pairs under "gate", "up", "down".  Returns dict(out=[n,H]
-    for `tokens` (or all tokens), plus the routing)."""
+    for `tokens` (or all tokens), the routing, and the FFN rows computed:
+    need (kept rows, ascending), ros_c (row_of_slot of `tokens` as indices
+    into need), h / h_shared (fp32 SwiGLU activations before their MXFP8
+    rounding, per need row / per token))."""
     logits = router_logits(x, w_router, bias)
     ids, gates = route(logits, k_max, k_per_token, score, renorm, routed_scale, num_groups,
                        topk_groups, group_topn)
@@ -302,11 +308,14 @@ def layer_forward_mxfp8(x, w_router, wq, k_max, bias=None, k_per_token=None, sco
     ros = d["row_of_slot"][tok]
     need = np.unique(ros[ros >= 0]).astype(np.int32)
     rt = d["row_token"][:d["R"]]
-    y = grouped_ffn_mxfp8(xq[rt], xs[rt], d["offsets"], wq["gate"], wq["up"], wq["down"], rows=need)
+    y, h = grouped_ffn_mxfp8(xq[rt], xs[rt], d["offsets"], wq["gate"], wq["up"], wq["down"], rows=need,
+                             return_h=True)
     ros_c = np.where(ros >= 0, np.searchsorted(need, np.maximum(ros, 0)), -1).astype(np.int32)
-    y_sh = None
+    y_sh = h_sh = None
     if shared is not None:
-        y_sh = grouped_ffn_mxfp8(xq[tok], xs[tok], np.array([0, len(tok)], np.int32),
-                                 *[tuple(a[None] for a in shared[n]) for n in ("gate", "up", "down")])
+        y_sh, h_sh = grouped_ffn_mxfp8(xq[tok], xs[tok], np.array([0, len(tok)], np.int32),
+                                       *[tuple(a[None] for a in shared[n]) for n in ("gate", "up", "down")],
+                                       return_h=True)
     out = combine(y if len(need) else np.zeros((1, H), np.float32), ros_c, gates[tok], y_sh)
-    return dict(out=out, logits=logits, ids=ids, gates=gates, xq=xq, xs=xs, **d)
+    return dict(out=out, logits=logits, ids=ids, gates=gates, xq=xq, xs=xs, need=need, ros_c=ros_c, h=h,
+                h_shared=h_sh, **d)

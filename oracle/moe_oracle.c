@@ -566,11 +566,13 @@ static void ffn_row_mxfp8(const double* tbl, int H, int I, const uint8_t* xq, co
 /* Grouped FFN on permuted MXFP8 rows: y_perm[r] = FFN_{e(r)}(x_perm[r]) with
  * e(r) the expert whose range [offsets[e], offsets[e+1]) holds r.  xq/xs are
  * the quantised permuted rows ([R][H] codes, [R][H/32] scales); rows/n_rows
- * select a subset as in oracle_grouped_ffn. */
+ * select a subset as in oracle_grouped_ffn.  h_out (nullable) receives each
+ * computed row's fp32 h before its MXFP8 rounding, [n][I]. */
 void oracle_grouped_ffn_mxfp8(int E, int H, int I, const uint8_t* xq, const uint8_t* xs,
                               const int32_t* offsets, const uint8_t* wgq, const uint8_t* wgs,
                               const uint8_t* wuq, const uint8_t* wus, const uint8_t* wdq,
-                              const uint8_t* wds, const int32_t* rows, int n_rows, float* y) {
+                              const uint8_t* wds, const int32_t* rows, int n_rows, float* y,
+                              float* h_out) {
   int n = rows ? n_rows : offsets[E];
   double tbl[256];
   for (int c = 0; c < 256; ++c) tbl[c] = oracle_e4m3_value(c);
@@ -588,11 +590,13 @@ void oracle_grouped_ffn_mxfp8(int E, int H, int I, const uint8_t* xq, const uint
       while (e < E && !(r >= offsets[e] && r < offsets[e + 1])) ++e;
       if (e == E) {
         for (int c = 0; c < H; ++c) y[(size_t)q * H + c] = 0.0f;
+        if (h_out) memset(h_out + (size_t)q * I, 0, sizeof(float) * (size_t)I);
         continue;
       }
       ffn_row_mxfp8(tbl, H, I, xq, xs, (size_t)r, wgq, wgs, wuq, wus, wdq, wds, e, h32, hq, hs, dec,
                     dec + H, dec + 2 * (size_t)H, dec + 3 * (size_t)H, dec + 3 * (size_t)H + I, yb);
       for (int c = 0; c < H; ++c) y[(size_t)q * H + c] = (float)yb[c];
+      if (h_out) memcpy(h_out + (size_t)q * I, h32, sizeof(float) * (size_t)I);
     }
     free(h32);
     free(hq);
