@@ -1,12 +1,17 @@
 """Benchmark: one GPU's share of an expert-parallel MoE layer forward on MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--experts bf16|mxfp8]
+                    [--no-cpu-baseline]
 
 A step is one moe_layer_forward call (router, top-k, dispatch, gather,
 grouped gate/up + SwiGLU, grouped down, shared expert, combine) over one batch
 of seeded synthetic input already resident in HBM.  The default workload is
 the Mixtral-8x7B-shaped prefill layer (T=4096, H=4096, E=8, top-2, I=14336,
-bf16 with fp32 accumulation).  Prints one JSON line on stdout.
+bf16 with fp32 accumulation).  With --experts mxfp8 the expert weights are
+quantised once to MXFP8 before timing and each step is one
+moe_layer_forward_mxfp8 call (routing on the bf16 x and router, x quantised
+per token, scaled fp8 MFMA GEMMs, h re-quantised to MXFP8).  Prints one JSON
+line on stdout.
 
 Timing: W untimed warm-up steps; then up to five untimed steps with events
 around every stage (moe_debug stage events) for the per-stage breakdown,
@@ -31,6 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
+PEAK_FP8_FLOPS = 5.0e15       # MI355X dense fp8 MFMA
 PEAK_F32_FLOPS = 157.3e12     # MI355X fp32 vector
 PEAK_HBM = 8.0e12             # MI355X HBM3E bytes/s
 
@@ -40,7 +46,9 @@ def log(*a):
 
 
 def gemm_model(cfg, counts_kept, eb):
-    """Algorithmic flops and bytes of the grouped-GEMM stages from realized counts."""
+    """Algorithmic flops and bytes of the grouped-GEMM stages from realized counts.
+    eb: bytes per activation / weight element (2 for bf16, 1 + 1/32 for MXFP8:
+    one code byte plus a 32nd of a scale byte); y and out are fp32."""
     H, I, Is, T = cfg.hidden, cfg.inter, cfg.shared_inter, cfg.tokens
     R = int(counts_kept.sum())
     touched = int((counts_kept > 0).sum())
@@ -54,8 +62,10 @@ def gemm_model(cfg, counts_kept, eb):
     return st
 
 
-def cpu_baseline(cfg, inp, budget_s=15.0):
-    """The oracle as it stands, on a bounded token sample of the workload."""
+def cpu_baseline(cfg, inp, budget_s=15.0, mx=False):
+    """The oracle as it stands, on a bounded token sample of the workload
+    (its MXFP8 layer when mx, with the weights of the sample's experts
+    quantised by the oracle outside the timed part)."""
     import oracle
     import workloads as W
     x, wr = W.to_numpy_raw(inp["x"]), W.to_numpy_raw(inp["w_router"])
@@ -69,17 +79,35 @@ def cpu_baseline(cfg, inp, budget_s=15.0):
     host = {k: W.to_numpy_raw(v) for k, v in inp.items() if k not in ("w_gate", "w_up", "w_down")}
     rng = np.random.default_rng(0)
 
+    shared_q = None
+    if mx and cfg.shared_inter:
+        shared_q = {n: oracle.mxfp8_quantize(host[key])
+                    for key, n in (("ws_gate", "gate"), ("ws_up", "up"), ("ws_down", "down"))}
+
     def run(n):
         tok = np.sort(rng.choice(cfg.tokens, size=n, replace=False)).astype(np.int32)
         used = sorted(set(int(e) for e in ids[tok].reshape(-1) if e >= 0))
+        wq = {}
         for key in ("w_gate", "w_up", "w_down"):
             w = inp[key]
             arr = np.empty(tuple(w.shape), np.uint16 if cfg.dtype == W.DT_BF16 else np.float32)
             for e in used:
                 arr[e] = W.to_numpy_raw(w[e])
             host[key] = arr
+            if mx:
+                c = np.zeros(arr.shape, np.uint8)
+                sc = np.zeros(arr.shape[:-1] + (arr.shape[-1] // 32,), np.uint8)
+                for e in used:
+                    c[e], sc[e] = oracle.mxfp8_quantize(arr[e])
+                wq[key[2:]] = (c, sc)
         t1 = time.perf_counter()
-        oracle.layer_forward_cfg(cfg, host, tokens=tok)
+        if mx:
+            oracle.layer_forward_mxfp8(host["x"], host["w_router"], wq, cfg.top_k, host["bias"],
+                                       host["k_per_token"], cfg.score, cfg.renormalize, cfg.routed_scale,
+                                       cfg.num_groups, cfg.topk_groups, cfg.group_topn, cfg.capacity_factor,
+                                       shared_q, tokens=tok)
+        else:
+            oracle.layer_forward_cfg(cfg, host, tokens=tok)
         t_all = time.perf_counter() - t1
         return t_all
 
@@ -94,8 +122,9 @@ def cpu_baseline(cfg, inp, budget_s=15.0):
     t_sample = max(t_n - t_route, 1e-9) + t_route * n / cfg.tokens
     return dict(value=n / t_sample, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
                 sample=f"{n} of {cfg.tokens} tokens of the {cfg.name} workload: routing of all tokens "
-                       f"({t_route:.2f} s, charged pro rata) + per-token FFN and combine of the sample "
-                       f"({t_n - t_route:.2f} s); fp64-accumulating C oracle, OpenMP over tokens")
+                       f"({t_route:.2f} s, charged pro rata) + per-token {'MXFP8 ' if mx else ''}FFN and "
+                       f"combine of the sample ({t_n - t_route:.2f} s); fp64-accumulating C oracle, OpenMP "
+                       f"over tokens")
 
 
 def replica_leg(spec, cfg, shape, ws, step, hiprt, stream, K, torch, abi):
@@ -139,6 +168,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--experts", choices=("bf16", "mxfp8"), default="bf16",
+                    help="expert weight format: the workload's bf16, or MXFP8 (E4M3 codes, one E8M0 scale "
+                         "per 32 elements) quantised once before timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--replicas", default=None, metavar="HOT:EXTRA",
@@ -186,7 +218,17 @@ def main():
         del src, dst
     inp = W.make_layer_inputs(cfg, dev)
     shape = abi.make_shape(cfg)
-    ws = torch.empty(abi.moe_workspace_size(shape), dtype=torch.uint8, device=dev)
+    mx = args.experts == "mxfp8"
+    if mx and cfg.dtype != W.DT_BF16:
+        print(json.dumps({"error": "MXFP8 experts need a bf16 workload"}))
+        sys.exit(2)
+    if mx:
+        mw = abi.mxfp8_ffn(inp["w_gate"], inp["w_up"], inp["w_down"], stream=None)
+        mws = abi.mxfp8_ffn(inp["ws_gate"], inp["ws_up"], inp["ws_down"]) if cfg.shared_inter else None
+        torch.cuda.synchronize()
+        ws = torch.empty(abi.moe_workspace_size_mxfp8(shape), dtype=torch.uint8, device=dev)
+    else:
+        ws = torch.empty(abi.moe_workspace_size(shape), dtype=torch.uint8, device=dev)
     out = torch.empty(cfg.tokens, cfg.hidden, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
     counts = torch.empty(cfg.experts, dtype=torch.int32, device=dev)
@@ -194,9 +236,13 @@ def main():
     dropped = torch.empty(1, dtype=torch.int32, device=dev)
 
     def step(dbg=None):
-        abi.moe_layer_forward(shape, inp["x"], inp["w_router"], inp["bias"], inp["k_per_token"], inp["w_gate"],
-                              inp["w_up"], inp["w_down"], inp["ws_gate"], inp["ws_up"], inp["ws_down"], out, dbg,
-                              ws, stream=stream)
+        if mx:
+            abi.moe_layer_forward_mxfp8(shape, inp["x"], inp["w_router"], inp["bias"], inp["k_per_token"], mw, mws,
+                                        out, dbg, ws, stream=stream)
+        else:
+            abi.moe_layer_forward(shape, inp["x"], inp["w_router"], inp["bias"], inp["k_per_token"],
+                                  inp["w_gate"], inp["w_up"], inp["w_down"], inp["ws_gate"], inp["ws_up"],
+                                  inp["ws_down"], out, dbg, ws, stream=stream)
 
     # one call with inspection outputs for the realized counts
     step(dict(expert_counts=counts, expert_offsets=offsets, num_dropped=dropped))
@@ -210,7 +256,7 @@ def main():
 
     K = args.steps
     nst = len(abi.MOE_STAGES)
-    eb = cfg.elem_bytes
+    eb = 1.0 + 1.0 / 32 if mx else cfg.elem_bytes
     model = gemm_model(cfg, kept, eb)
 
     def stage_dbg(stages):
@@ -250,7 +296,7 @@ def main():
     ms_per_step = total_ms / K
     tokens_per_s = cfg.tokens / (ms_per_step / 1e3)
 
-    peak_f = PEAK_BF16_FLOPS if cfg.dtype == W.DT_BF16 else PEAK_F32_FLOPS
+    peak_f = PEAK_FP8_FLOPS if mx else (PEAK_BF16_FLOPS if cfg.dtype == W.DT_BF16 else PEAK_F32_FLOPS)
     m = model[dom]
     t_s = dom_ms / 1e3
     bound = "mfma" if m["flops"] / peak_f >= m["bytes"] / PEAK_HBM else "hbm"
@@ -268,7 +314,8 @@ def main():
     # only while the kernel source is the one the counters were taken on
     from expert_serving_amd import profiling
     traffic = None
-    rec = profiling.read_traffic(os.path.join(ROOT, "profiles", f"{dom}_gemm_{cfg.name}_traffic.md"))
+    rec = profiling.read_traffic(os.path.join(ROOT, "profiles",
+                                              f"{dom}_gemm_{'mxfp8_' if mx else ''}{cfg.name}_traffic.md"))
     if rec and rec.get("source_sha256") == profiling.source_sha256():
         traffic = float(rec["traffic_bytes"])
 
@@ -283,11 +330,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.dtype == W.DT_BF16 else "f32",
+        "dtype": "fp8 (MXFP8 experts; bf16 router)" if mx else ("bf16" if cfg.dtype == W.DT_BF16 else "f32"),
         "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
         "config": {"workload": cfg.name, "tokens": cfg.tokens, "hidden": cfg.hidden, "experts": cfg.experts,
                    "top_k": cfg.top_k, "intermediate": cfg.inter, "shared_intermediate": cfg.shared_inter,
                    "capacity_factor": cfg.capacity_factor, "parallelism": "one GPU's expert-parallel share",
+                   "expert_format": args.experts,
                    **({"overrides": {k: v for k, v in overrides.items()}} if overrides else {})},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
@@ -296,6 +344,7 @@ def main():
         "grouped_gemm": {"ms": round(t_gemm * 1e3, 4), "tflops": round(f_gemm / t_gemm / 1e12, 2),
                          "frac_of_roofline": round(t_roof_gemm / t_gemm, 4),
                          "frac_of_mfma_peak": round(f_gemm / t_gemm / peak_f, 4),
+                         "mfma_peak_tflops": peak_f / 1e12,
                          "frac_of_hbm_peak": round(b_gemm / t_gemm / PEAK_HBM, 4)},
         # from the separate breakdown steps (events around every stage)
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
@@ -308,7 +357,7 @@ def main():
         line["replica_map"] = replica_leg(args.replicas, cfg, shape, ws, step, hiprt, stream, K, torch, abi)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget, mx=mx)
     print(json.dumps(line), flush=True)
 
 

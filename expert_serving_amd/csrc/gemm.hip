@@ -155,15 +155,17 @@ constexpr int kSK = 32;            // K elements per step (and per LDS row of 4-
 constexpr int kPingRowElems = 64;  // K elements per LDS row of 8-wave blocks (128 bytes)
 
 // Rows of one stage, padded to whole wavefront loads per wave: 16 rows per
-// load for 4-wave blocks; for 8-wave blocks 8 rows per load and an even
-// number of loads per wave (the stage is written in two halves).
+// load for 4-wave blocks, 8 rows per load for 8-wave blocks.
 constexpr int gemm_stage_rows(int BM, int BNB, int MODE, int NW) {
-  return (BM + BNB * ((MODE == kGateUp || MODE == kGateUpMX) ? 2 : 1) + 16 * NW - 1) / (16 * NW) *
-         (16 * NW);
+  return (BM + BNB * ((MODE == kGateUp || MODE == kGateUpMX) ? 2 : 1) + (NW == 8 ? 8 : 16) * NW - 1) /
+         ((NW == 8 ? 8 : 16) * NW) * ((NW == 8 ? 8 : 16) * NW);
 }
-// Bytes of LDS one block of k_gemm_mfma<BM, BNB, MODE, NS, NW> uses.
+// Bytes of LDS one block of k_gemm_mfma<BM, BNB, MODE, NS, NW> uses: NS
+// stages of tiles, and for the MXFP8 modes one 32-bit scale word per tile row
+// and stage.
 constexpr int gemm_lds_bytes(int BM, int BNB, int MODE, int NS, int NW) {
-  return NS * gemm_stage_rows(BM, BNB, MODE, NW) * (NW == 8 ? kPingRowElems : kSK) * 2;
+  return NS * gemm_stage_rows(BM, BNB, MODE, NW) *
+         ((NW == 8 ? kPingRowElems : kSK) * 2 + ((MODE == kGateUpMX || MODE == kDownMX) ? 4 : 0));
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -239,7 +241,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lets chunk offsets live in SGPRs
+  __builtin_assume(wave >= 0 && wave < NW);
   const int wm = wave % WAVES_M, wn = wave / WAVES_M;
 
   // A rows are contiguous from row0, or gathered: tile row r is row a_rows[row0 + r]
@@ -330,11 +333,27 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
     // s+1's buffer last held stage s-1, read by both groups before the
     // barrier that precedes the first write; all four writes of stage s+1
     // land before the leading group's first read of it, two phases later.
+    //
+    // MXFP8 modes: the same schedule on E4M3 codes (a 128-byte LDS row holds
+    // 128 codes, a step K = 64 codes, one scaled MFMA per fragment pair).
+    // The E8M0 scale words (four blocks of a row per 128-code stage) travel
+    // with the tiles: each wave loads the words of the 8-row chunks it
+    // stages (lane L: chunk L/8, row L%8) with its first half stage, writes
+    // them into the stage's scale area of LDS (one word per tile row) with
+    // that half's rows, and reads the words of its fragment rows with the
+    // fragments of the stage's first step.  Weight chunks never straddle the
+    // end of the weight matrix (N is a multiple of 128), so their rows are
+    // clamped per chunk and their offsets differ from one chunk to the next
+    // only by a uniform term.
     constexpr int RW = kPingRowElems;
     constexpr int PSTAGE = ROWS * RW;   // elements of one stage
     constexpr int NI = ROWS / (8 * NW); // 8-row loads per wave per stage
-    constexpr int NH = NI / 2;          // ... per half stage
-    static_assert(NI % 2 == 0, "half stages");
+    constexpr int NH0 = (NI + 1) / 2;   // ... in the first half stage
+    constexpr int NH1 = NI / 2;         // ... in the second
+    constexpr int NA = MX ? (BM + 8 * NW - 1) / (8 * NW) : NI;  // chunks that may hold token rows
+    static_assert(MX || NI % 2 == 0, "half stages");
+    static_assert(!MX || NI <= 16, "scale words: at most two per lane and stage");
+    uint32_t* const sc_lds = reinterpret_cast<uint32_t*>(smem + 2 * PSTAGE);  // [2][ROWS] (MX)
 #define MOE_READ_FRAGS_P(set_, step_, ks_)                                              \
   do {                                                                                  \
     const uint16_t* sA_ = smem + (((step_) >> 1) & 1) * PSTAGE;                         \
@@ -352,7 +371,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
         wb1[set_][a] = *reinterpret_cast<const u32x4*>(sB1_ + r * RW + ((c_ ^ ((r >> 1) & 7)) << 3)); \
     }                                                                                   \
   } while (0)
-    // MXFP8: chunks c and c + 2 of a step (set 0 and set 1 above) form one operand
+    // MXFP8: chunks c and c + 2 of a step form one 32-byte operand; on the
+    // first step of a stage also the scale words of the fragment rows
 #define MOE_READ_FRAGS_MX(step_)                                                        \
   do {                                                                                  \
     const uint16_t* sA_ = smem + (((step_) >> 1) & 1) * PSTAGE;                         \
@@ -376,62 +396,109 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
                       *reinterpret_cast<const u32x4*>(row1_ + (((c_ + 2) ^ ((r >> 1) & 7)) << 3))); \
       }                                                                                 \
     }                                                                                   \
+    if (((step_) & 1) == 0) {                                                           \
+      const uint32_t* sc_ = sc_lds + (((step_) >> 1) & 1) * ROWS;                       \
+      _Pragma("unroll") for (int b = 0; b < FM; ++b) scc[b] = sc_[wm * WM + b * 32 + fr]; \
+      _Pragma("unroll") for (int a = 0; a < FN; ++a) {                                  \
+        scc[FM + a] = sc_[BM + wn * WN + a * 32 + fr];                                  \
+        if constexpr (DUAL) scc[FM + FN + a] = sc_[BM + BNB + wn * WN + a * 32 + fr];   \
+      }                                                                                 \
+    }                                                                                   \
   } while (0)
     const bool lag = wave >= NW / 2;
     const int stages = K / RW;
-    int goff[NI];
+    // per-lane global offsets: every chunk (bf16 modes) or the chunks that may
+    // hold token rows (MX); MX weight chunks share one lane offset
+    int goff[NA];
 #pragma unroll
-    for (int j = 0; j < NI; ++j) goff[j] = row_goff(8 * (wave + NW * j) + (lane >> 3), lane & 7);
-    u32x4 ldr[2][NH];
-    // MXFP8 scale words: one per fragment (token fragments, then gate / down
-    // weight fragments, then up weight fragments) and stage.  The words of
-    // stage s+1 are loaded during the first step of stage s (scn) and become
-    // current (scc) at the start of stage s+1.
-    constexpr int NSC = MX ? FM + NB * FN : 0;
-    uint32_t scc[MX ? NSC : 1], scn[MX ? NSC : 1];
-    int sc_row[MX ? FM + FN : 1];  // gate and up weight rows coincide
+    for (int j = 0; j < NA; ++j) goff[j] = row_goff(8 * (wave + NW * j) + (lane >> 3), lane & 7);
+    const int lw = (lane >> 3) * K + (lane & 7) * 8;
+    u32x4 ldr[2][NH0];
+    // MX scale words: the current stage's words of this lane's fragments
+    // (token fragments, then gate / down weight fragments, then up weight
+    // fragments), shifted so that byte 2h selects the lane's block of step h
+    constexpr int NSC = MX ? FM + NB * FN : 1;
+    constexpr int NSL = MX ? (NI > 8 ? 2 : 1) : 1;  // scale-word loads per lane and stage
+    uint32_t scc[NSC];
+    uint32_t scl[NSL];           // staged words (loaded with half 0, written with half 0)
+    const uint32_t* scp[NSL];    // this lane's scale rows (group 0) ...
+    int scs[NSL];                // ... and their group stride
     if constexpr (MX) {
 #pragma unroll
-      for (int b = 0; b < FM; ++b) {
-        const int r = min(wm * WM + b * 32 + fr, rows - 1);
-        sc_row[b] = a_rows ? a_rows[row0 + r] : row0 + r;
+      for (int q = 0; q < NSL; ++q) {
+        const int rho = 8 * (wave + NW * (8 * q + (lane >> 3))) + (lane & 7);
+        const uint32_t* base;
+        int row, strd;
+        if (rho < BM) {
+          const int r = min(rho, rows - 1);
+          base = reinterpret_cast<const uint32_t*>(mx.sa);
+          row = a_rows ? a_rows[row0 + r] : row0 + r;
+          strd = mx.sa_stride;
+        } else if (rho < BM + NB * BNB) {
+          base = reinterpret_cast<const uint32_t*>(rho < BM + BNB ? mx.sb0 : mx.sb1);
+          row = expert * N + min(n0 + (rho - BM) % BNB, N - 1);
+          strd = mx.sb_stride;
+        } else {  // pad rows: any valid word (never read back)
+          base = reinterpret_cast<const uint32_t*>(mx.sb0);
+          row = expert * N;
+          strd = mx.sb_stride;
+        }
+        scp[q] = base + row;
+        scs[q] = strd;
       }
-#pragma unroll
-      for (int a = 0; a < FN; ++a) sc_row[FM + a] = expert * N + min(n0 + wn * WN + a * 32 + fr, N - 1);
     }
 #define MOE_ISSUE_SC(stage_)                                                            \
   do {                                                                                  \
     if constexpr (MX) {                                                                 \
       const int st_ = (stage_) < stages ? (stage_) : stages - 1;                        \
-      _Pragma("unroll") for (int f = 0; f < NSC; ++f) {                                 \
-        const uint32_t* base_ = reinterpret_cast<const uint32_t*>(                      \
-            f < FM ? mx.sa : (f < FM + FN ? mx.sb0 : mx.sb1));                          \
-        const int strd_ = f < FM ? mx.sa_stride : mx.sb_stride;                         \
-        scn[f] = base_[(size_t)st_ * strd_ + sc_row[f < FM + FN ? f : f - FN]];         \
+      _Pragma("unroll") for (int q = 0; q < NSL; ++q) {                                 \
+        if (8 * q + (lane >> 3) < NI) scl[q] = scp[q][(size_t)st_ * scs[q]];            \
       }                                                                                 \
     }                                                                                   \
   } while (0)
-#define MOE_ISSUE(set_, stage_, half_, jj0_, jj1_)                                      \
+#define MOE_STORE_SC(stage_)                                                            \
+  do {                                                                                  \
+    if constexpr (MX) {                                                                 \
+      _Pragma("unroll") for (int q = 0; q < NSL; ++q) {                                 \
+        if (8 * q + (lane >> 3) < NI)                                                   \
+          sc_lds[((stage_) & 1) * ROWS + 8 * (wave + NW * (8 * q + (lane >> 3))) + (lane & 7)] = scl[q]; \
+      }                                                                                 \
+    }                                                                                   \
+  } while (0)
+#define MOE_ISSUE(set_, stage_, half_)                                                  \
   do {                                                                                  \
     const int st_ = (stage_) < stages ? (stage_) : stages - 1;                          \
-    _Pragma("unroll") for (int jj = (jj0_); jj < (jj1_); ++jj) {                        \
-      const int j_ = (half_) * NH + jj;                                                 \
+    _Pragma("unroll") for (int jj = 0; jj < ((half_) ? NH1 : NH0); ++jj) {              \
+      const int j_ = (half_) * NH0 + jj;                                                \
       const int r0_ = 8 * (wave + NW * j_);                                             \
-      const uint16_t* src_ = r0_ < BM ? Ab : (r0_ < BM + BNB ? B0b : (r0_ < BM + NB * BNB ? B1b : Ab)); \
-      ldr[set_][jj] = *reinterpret_cast<const u32x4*>(src_ + goff[j_] + st_ * RW);      \
+      const uint16_t* src_;                                                             \
+      if constexpr (MX) {                                                               \
+        if (j_ < NA && r0_ < BM) {                                                      \
+          src_ = Ab + goff[j_ < NA ? j_ : 0];                                           \
+        } else if (r0_ < BM + NB * BNB) {                                               \
+          const int rb_ = min(n0 + (r0_ - BM) % BNB, N - 8);                            \
+          src_ = (r0_ < BM + BNB ? B0b : B1b) + (size_t)rb_ * K + lw;                   \
+        } else {                                                                        \
+          src_ = Ab + (lane & 7) * 8;                                                   \
+        }                                                                               \
+      } else {                                                                          \
+        src_ = (r0_ < BM ? Ab : (r0_ < BM + BNB ? B0b : (r0_ < BM + NB * BNB ? B1b : Ab))) + goff[j_]; \
+      }                                                                                 \
+      ldr[set_][jj] = *reinterpret_cast<const u32x4*>(src_ + st_ * RW);                 \
     }                                                                                   \
   } while (0)
 #define MOE_STORE(set_, stage_, half_)                                                  \
   do {                                                                                  \
     uint16_t* base_ = smem + ((stage_) & 1) * PSTAGE;                                   \
-    _Pragma("unroll") for (int jj = 0; jj < NH; ++jj) {                                 \
-      const int j_ = (half_) * NH + jj;                                                 \
+    _Pragma("unroll") for (int jj = 0; jj < ((half_) ? NH1 : NH0); ++jj) {              \
+      const int j_ = (half_) * NH0 + jj;                                                \
       const int r0_ = 8 * (wave + NW * j_);                                             \
       const int row_ = r0_ + (lane >> 3);                                               \
       u32x4 v_ = ldr[set_][jj];                                                         \
       if (MODE == kDown && r0_ >= BM && r0_ < BM + BNB) v_ = bf16x8_to_f16x8(v_);       \
       *reinterpret_cast<u32x4*>(base_ + row_ * RW + (((lane & 7) ^ ((row_ >> 1) & 7)) << 3)) = v_; \
     }                                                                                   \
+    if ((half_) == 0) MOE_STORE_SC(stage_);                                             \
   } while (0)
 #define MOE_PP_STEP(tt_, h_)                                                            \
   do {                                                                                  \
@@ -449,18 +516,18 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
     __builtin_amdgcn_s_setprio(1);                                                      \
     if constexpr (MX) {                                                                 \
       if ((h_) == 0) {                                                                  \
-        _Pragma("unroll") for (int f = 0; f < NSC; ++f) scc[f] = scn[f] >> (8 * fk);    \
-        MOE_ISSUE_SC(((tt_) >> 1) + 1);                                                 \
+        _Pragma("unroll") for (int f = 0; f < NSC; ++f) scc[f] >>= 8 * fk;              \
+        MOE_ISSUE_SC(((tt_) >> 1) + 2);                                                 \
       }                                                                                 \
     }                                                                                   \
-    MOE_ISSUE(h_, ((tt_) >> 1) + 2, h_, 0, NH);                                         \
+    MOE_ISSUE(h_, ((tt_) >> 1) + 2, h_);                                                \
     if constexpr (MX) {                                                                 \
       MOE_MFMAS_MX(h_);                                                                 \
     } else {                                                                            \
       MOE_MFMAS(0);                                                                     \
       MOE_MFMAS(1);                                                                     \
     }                                                                                   \
-    __builtin_amdgcn_sched_group_barrier(0x020, NH + ((h_) == 0 ? NSC : 0), 3);         \
+    __builtin_amdgcn_sched_group_barrier(0x020, ((h_) ? NH1 : NH0) + (MX && (h_) == 0 ? NSL : 0), 3); \
     __builtin_amdgcn_sched_group_barrier(0x008, MX ? NMF : 2 * NMF, 3);                 \
     __builtin_amdgcn_s_setprio(0);                                                      \
     __builtin_amdgcn_sched_barrier(0);                                                  \
@@ -468,12 +535,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
     __builtin_amdgcn_sched_barrier(0);                                                  \
   } while (0)
     MOE_ISSUE_SC(0);
-    MOE_ISSUE(0, 0, 0, 0, NH);
-    MOE_ISSUE(1, 0, 1, 0, NH);
+    MOE_ISSUE(0, 0, 0);
+    MOE_ISSUE(1, 0, 1);
     MOE_STORE(0, 0, 0);
     MOE_STORE(1, 0, 1);
-    MOE_ISSUE(0, 1, 0, 0, NH);
-    MOE_ISSUE(1, 1, 1, 0, NH);
+    MOE_ISSUE_SC(1);
+    MOE_ISSUE(0, 1, 0);
+    MOE_ISSUE(1, 1, 1);
     MOE_WAIT_LGKM0();
     raw_barrier();
     if (lag) raw_barrier();
@@ -486,6 +554,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
 #undef MOE_PP_STEP
 #undef MOE_READ_FRAGS_MX
 #undef MOE_ISSUE_SC
+#undef MOE_STORE_SC
 #undef MOE_STORE
 #undef MOE_ISSUE
 #undef MOE_READ_FRAGS_P

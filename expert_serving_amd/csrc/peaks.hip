@@ -95,6 +95,39 @@ __global__ __launch_bounds__(256) void k_mfma32_rand(float* out, int iters) {
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands and E8M0 block scales
+// (the MXFP8 GEMM's instruction), CH independent chains; RAND: random codes
+// (exponent field kept below 8, so no NaN) and random scales near 2^0, a
+// different operand pair per chain
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+template <bool RAND>
+__global__ __launch_bounds__(256) void k_mfma_fp8(float* out, int iters) {
+  constexpr int CH = 4;
+  i32x8 a[CH], b[CH];
+  int sa[CH], sb[CH];
+  for (int j = 0; j < CH; ++j) {
+    for (int i = 0; i < 8; ++i) {
+      const unsigned ha = hash32((blockIdx.x * 256 + threadIdx.x) * 64 + j * 8 + i);
+      const unsigned hb = hash32(ha ^ 0x9e3779b9u);
+      a[j][i] = RAND ? (int)(ha & 0xBFBFBFBFu) : 0x38383838;
+      b[j][i] = RAND ? (int)(hb & 0xBFBFBFBFu) : 0x30303030;
+    }
+    sa[j] = RAND ? 120 + (int)(hash32(j + 77 * threadIdx.x) & 7) : 127;
+    sb[j] = RAND ? 120 + (int)(hash32(j + 91 * threadIdx.x) & 7) : 127;
+  }
+  f32x16 c[CH];
+  for (int j = 0; j < CH; ++j)
+    for (int q = 0; q < 16; ++q) c[j][q] = 0;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+      c[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j], b[j], c[j], 0, 0, 0, sa[j], 0, sb[j]);
+  }
+  float s = 0;
+  for (int j = 0; j < CH; ++j) s += c[j][0] + c[j][5] + c[j][10] + c[j][15];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 // 16-byte LDS reads from a 32 KiB buffer; the address changes every iteration
 __global__ __launch_bounds__(256) void k_lds(unsigned* out, int iters) {
   __shared__ __attribute__((aligned(16))) unsigned lds[8192];
@@ -264,6 +297,12 @@ int main() {
     ms = time_ms([&] { hipLaunchKernelGGL(k_mfma32_rand, dim3(grid), dim3(256), 0, 0, o, iters); });
     printf("mfma bf16 32x32x16, %d wave(s)/SIMD,  4 chains, random operands: %.1f TFLOP/s\n", bpc,
            (double)grid * 4 * iters * 4 * 32768.0 / ms / 1e9);
+    ms = time_ms([&] { hipLaunchKernelGGL(k_mfma_fp8<false>, dim3(grid), dim3(256), 0, 0, o, iters / 2); });
+    printf("mfma scaled fp8 32x32x64, %d wave(s)/SIMD,  4 chains: %.1f TFLOP/s\n", bpc,
+           (double)grid * 4 * (iters / 2) * 4 * 131072.0 / ms / 1e9);
+    ms = time_ms([&] { hipLaunchKernelGGL(k_mfma_fp8<true>, dim3(grid), dim3(256), 0, 0, o, iters / 2); });
+    printf("mfma scaled fp8 32x32x64, %d wave(s)/SIMD,  4 chains, random operands: %.1f TFLOP/s\n", bpc,
+           (double)grid * 4 * (iters / 2) * 4 * 131072.0 / ms / 1e9);
   }
   for (int bpc : {1, 4}) {
     const int grid = CUs * bpc;
