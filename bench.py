@@ -350,7 +350,13 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "routing": {"rows_kept": int(kept.sum()), "dropped": int(cnt.sum() - kept.sum()),
                     "experts_touched": int((kept > 0).sum()),
-                    "max_over_mean_load": round(float(cnt.max() / max(cnt.mean(), 1e-9)), 3)},
+                    "max_over_mean_load": round(float(cnt.max() / max(cnt.mean(), 1e-9)), 3),
+                    # experts by row count: the grouped GEMMs give experts below 128 kept
+                    # rows 32-row tiles when the layer mixes big and small loads
+                    "experts_ge_128_rows": int((kept >= 128).sum()),
+                    "rows_in_experts_ge_128": int(kept[kept >= 128].sum()),
+                    "experts_1_to_127_rows": int(((kept > 0) & (kept < 128)).sum()),
+                    "rows_in_experts_1_to_127": int(kept[(kept > 0) & (kept < 128)].sum())},
         "host_wall_s": round(wall, 3),
     }
     if args.replicas:

@@ -17,36 +17,52 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (b + (((b >> 16) & 1u) + 0x7FFFu)) >> 16;
 }
 
-// One block per token; thread i owns 4 consecutive columns per pass.
-template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
+// One block per token; thread i owns 4 consecutive columns per pass.  KM is
+// a compile-time bound on k_max (2, 4, 8 or 16), so the loads of all of a
+// token's rows are issued before the first multiply-add waits on them.  y may
+// come in `parts` partial sums (a K-split down projection), each `part_stride`
+// floats apart; they are added in part order before the gate multiplies.
+template <bool OUT_BF16, int KM>
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, int parts,
+                                                 long long part_stride,
                                                  const int32_t* __restrict__ row_of_slot,
                                                  const float* __restrict__ gates,
                                                  const float* __restrict__ y_shared, int H,
                                                  int k_max, void* __restrict__ out) {
   const int t = blockIdx.x;
-  __shared__ int s_row[kMaxTopK];
-  __shared__ float s_g[kMaxTopK];
-  if (threadIdx.x < k_max) {
-    s_row[threadIdx.x] = row_of_slot[(size_t)t * k_max + threadIdx.x];
-    s_g[threadIdx.x] = gates[(size_t)t * k_max + threadIdx.x];
+  __shared__ int s_row[KM];
+  __shared__ float s_g[KM];
+  if (threadIdx.x < KM) {
+    const bool live = (int)threadIdx.x < k_max;
+    s_row[threadIdx.x] = live ? row_of_slot[(size_t)t * k_max + threadIdx.x] : -1;
+    s_g[threadIdx.x] = live ? gates[(size_t)t * k_max + threadIdx.x] : 0.f;
   }
   __syncthreads();
   for (int c = threadIdx.x * 4; c < H; c += blockDim.x * 4) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k_max; ++j) {
+    f32x4 v[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
       const int r = s_row[j];
-      if (r < 0) continue;
+      v[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (r >= 0) {
+        v[j] = *reinterpret_cast<const f32x4*>(y + (size_t)r * H + c);
+        for (int p = 1; p < parts; ++p)
+          v[j] += *reinterpret_cast<const f32x4*>(y + p * part_stride + (size_t)r * H + c);
+      }
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      if (s_row[j] < 0) continue;
       const float g = s_g[j];
-      const f32x4 v = *reinterpret_cast<const f32x4*>(y + (size_t)r * H + c);
-      acc[0] = fmaf(g, v[0], acc[0]);
-      acc[1] = fmaf(g, v[1], acc[1]);
-      acc[2] = fmaf(g, v[2], acc[2]);
-      acc[3] = fmaf(g, v[3], acc[3]);
+      acc[0] = fmaf(g, v[j][0], acc[0]);
+      acc[1] = fmaf(g, v[j][1], acc[1]);
+      acc[2] = fmaf(g, v[j][2], acc[2]);
+      acc[3] = fmaf(g, v[j][3], acc[3]);
     }
     if (y_shared) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(y_shared + (size_t)t * H + c);
-      acc += v;
+      const f32x4 w = *reinterpret_cast<const f32x4*>(y_shared + (size_t)t * H + c);
+      acc += w;
     }
     if constexpr (OUT_BF16) {
       uint2 pk;
@@ -59,18 +75,32 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
   }
 }
 
+template <int KM>
+hipError_t launch_combine_k(const moe_shape& s, const float* y, int parts, long long part_stride,
+                            const int32_t* row_of_slot, const float* gates, const float* y_shared,
+                            void* out, hipStream_t st) {
+  const dim3 grid(s.num_tokens);
+  if (s.out_dtype == MOE_BF16)
+    hipLaunchKernelGGL((k_combine<true, KM>), grid, dim3(256), 0, st, y, parts, part_stride, row_of_slot,
+                       gates, y_shared, s.hidden, s.top_k, out);
+  else
+    hipLaunchKernelGGL((k_combine<false, KM>), grid, dim3(256), 0, st, y, parts, part_stride, row_of_slot,
+                       gates, y_shared, s.hidden, s.top_k, out);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_combine(const moe_shape& s, const float* y_perm, const int32_t* row_of_slot,
-                          const float* gates, const float* y_shared, void* out, hipStream_t st) {
-  const dim3 grid(s.num_tokens);
-  if (s.out_dtype == MOE_BF16)
-    hipLaunchKernelGGL(k_combine<true>, grid, dim3(256), 0, st, y_perm, row_of_slot, gates,
-                       y_shared, s.hidden, s.top_k, out);
-  else
-    hipLaunchKernelGGL(k_combine<false>, grid, dim3(256), 0, st, y_perm, row_of_slot, gates,
-                       y_shared, s.hidden, s.top_k, out);
-  return hipGetLastError();
+                          const float* gates, const float* y_shared, void* out, hipStream_t st,
+                          int parts, long long part_stride) {
+  if (s.top_k <= 2)
+    return launch_combine_k<2>(s, y_perm, parts, part_stride, row_of_slot, gates, y_shared, out, st);
+  if (s.top_k <= 4)
+    return launch_combine_k<4>(s, y_perm, parts, part_stride, row_of_slot, gates, y_shared, out, st);
+  if (s.top_k <= 8)
+    return launch_combine_k<8>(s, y_perm, parts, part_stride, row_of_slot, gates, y_shared, out, st);
+  return launch_combine_k<kMaxTopK>(s, y_perm, parts, part_stride, row_of_slot, gates, y_shared, out, st);
 }
 
 }  // namespace moe

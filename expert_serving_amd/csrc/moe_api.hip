@@ -156,6 +156,20 @@ WsLayout plan_workspace(const moe_shape& s, bool mx) {
                                                                                       : per_expert * E)
                                        : 0;
   }
+  // Decode-sized layers (every expert small, few 32-row tiles) leave most
+  // compute units idle in the down projection; splitting its long K (= I)
+  // into partial sums that the combine adds gives every unit weight rows to
+  // stream.
+  {
+    const int bnb = mx ? 256 : 128;  // column tile of the 32-row down kernels
+    const long long blocks = (long long)w.max_tiles_small * ((H + bnb - 1) / bnb);
+    w.ksplit = 1;
+    if (!gp.has_big() && gp.has_small() && s.act_dtype == MOE_BF16 && blocks > 0 && blocks < 512) {
+      const int want = (int)std::min<long long>(4, 1024 / blocks);
+      const int stages = (int)(I / 64);
+      w.ksplit = std::max(1, std::min(want, stages / 4));
+    }
+  }
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at_ = o;
@@ -176,7 +190,7 @@ WsLayout plan_workspace(const moe_shape& s, bool mx) {
   w.sched_small = take((size_t)w.max_tiles_small * sizeof(MTile));
   w.sched_count = take(16);
   w.h = take(slots * I * eb);
-  w.y = take(slots * H * 4);
+  w.y = take((size_t)w.ksplit * slots * H * 4);
   w.hs = take(T * Is * eb);
   w.ys = take(Is ? T * H * 4 : 0);
   if (mx) {
@@ -211,7 +225,8 @@ moe_status run_router(const moe_shape& s, const void* x, const void* w_router, c
 moe_status run_ffn(const moe_shape& s, const void* x_perm, const int32_t* a_rows,
                    const int32_t* offsets, const void* w_gate, const void* w_up,
                    const void* w_down, float* y, void* ws,
-                   const WsLayout& L, hipStream_t st, const moe_debug* dbg = nullptr) {
+                   const WsLayout& L, hipStream_t st, const moe_debug* dbg = nullptr,
+                   int ksplit = 1) {
   const GemmPlan gp = choose_gemm_plan(s);
   const int E = s.num_experts, H = s.hidden, I = s.intermediate;
   MTile* sb = at<MTile>(ws, L.sched_big);
@@ -221,21 +236,36 @@ moe_status run_ffn(const moe_shape& s, const void* x_perm, const int32_t* a_rows
   MOE_HIP(launch_build_schedule(offsets, E, gp, sb, L.max_tiles_big, ss, L.max_tiles_small, cnt,
                                 st));
   void* h = at<void>(ws, L.h);
+  // skewed loads (both tile classes) on bf16: one interleaved launch per
+  // projection, so small experts stream weights while big ones run MFMAs
+  const bool merged = gp.has_big() && gp.has_small() && s.act_dtype == MOE_BF16 &&
+                      gp.bm_big == 256 && gp.bm_small == 32;
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATE_UP, true, st));
-  if (gp.has_big())
-    MOE_HIP(launch_gemm_gateup(s.act_dtype, gp.bm_big, x_perm, a_rows, H, w_gate, w_up, I, H, h,
-                               I, sb, cnt, L.max_tiles_big, 0, flags, st));
-  if (gp.has_small())
-    MOE_HIP(launch_gemm_gateup(s.act_dtype, gp.bm_small, x_perm, a_rows, H, w_gate, w_up, I, H,
-                               h, I, ss, cnt + 1, L.max_tiles_small, 0, flags, st));
+  if (merged) {
+    MOE_HIP(launch_gemm_gateup2(x_perm, a_rows, H, w_gate, w_up, I, H, h, I, sb, cnt, L.max_tiles_big, ss,
+                                cnt + 1, L.max_tiles_small, flags, st));
+  } else {
+    if (gp.has_big())
+      MOE_HIP(launch_gemm_gateup(s.act_dtype, gp.bm_big, x_perm, a_rows, H, w_gate, w_up, I, H, h,
+                                 I, sb, cnt, L.max_tiles_big, 0, flags, st));
+    if (gp.has_small())
+      MOE_HIP(launch_gemm_gateup(s.act_dtype, gp.bm_small, x_perm, a_rows, H, w_gate, w_up, I, H,
+                                 h, I, ss, cnt + 1, L.max_tiles_small, 0, flags, st));
+  }
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATE_UP, false, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_DOWN, true, st));
-  if (gp.has_big())
-    MOE_HIP(launch_gemm_plain(s.act_dtype, gp.bm_big, true, h, I, w_down, H, I, nullptr, y, H, sb,
-                              cnt, L.max_tiles_big, 0, st));
-  if (gp.has_small())
-    MOE_HIP(launch_gemm_plain(s.act_dtype, gp.bm_small, true, h, I, w_down, H, I, nullptr, y, H,
-                              ss, cnt + 1, L.max_tiles_small, 0, st));
+  if (merged) {
+    MOE_HIP(launch_gemm_down2(h, I, w_down, H, I, y, H, sb, cnt, L.max_tiles_big, ss, cnt + 1,
+                              L.max_tiles_small, st));
+  } else {
+    if (gp.has_big())
+      MOE_HIP(launch_gemm_plain(s.act_dtype, gp.bm_big, true, h, I, w_down, H, I, nullptr, y, H, sb,
+                                cnt, L.max_tiles_big, 0, st));
+    if (gp.has_small())
+      MOE_HIP(launch_gemm_plain(s.act_dtype, gp.bm_small, true, h, I, w_down, H, I, nullptr, y, H,
+                                ss, cnt + 1, L.max_tiles_small, 0, st, gp.has_big() ? 1 : ksplit,
+                                (long long)s.num_tokens * s.top_k * H));
+  }
   MOE_HIP(stage_mark(dbg, MOE_STAGE_DOWN, false, st));
   return MOE_OK;
 }
@@ -245,7 +275,7 @@ moe_status run_ffn(const moe_shape& s, const void* x_perm, const int32_t* a_rows
 moe_status run_ffn_mx(const moe_shape& s, const void* xq, const int32_t* a_rows,
                       const uint8_t* xsc, int xs_stride, const int32_t* offsets,
                       const moe_mxfp8_ffn& w, float* y, void* ws, const WsLayout& L,
-                      hipStream_t st, const moe_debug* dbg = nullptr) {
+                      hipStream_t st, const moe_debug* dbg = nullptr, int ksplit = 1) {
   const GemmPlan gp = choose_gemm_plan(s);
   const int E = s.num_experts, H = s.hidden, I = s.intermediate;
   const int slots = s.num_tokens * s.top_k;
@@ -258,23 +288,36 @@ moe_status run_ffn_mx(const moe_shape& s, const void* xq, const int32_t* a_rows,
   void* h = at<void>(ws, L.h);
   uint8_t* hsc = at<uint8_t>(ws, L.hsc);
   const auto gsc = w.gate_scales, usc = w.up_scales, dsc = w.down_scales;
+  const bool merged = gp.has_big() && gp.has_small() && gp.bm_big == 256 && gp.bm_small == 32;
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATE_UP, true, st));
-  if (gp.has_big())
-    MOE_HIP(launch_gemm_gateup_mx(gp.bm_big, xq, a_rows, xsc, xs_stride, w.gate, gsc, w.up, usc,
-                                  E * I, I, H, h, hsc, slots, sb, cnt, L.max_tiles_big, 0, flags,
-                                  st));
-  if (gp.has_small())
-    MOE_HIP(launch_gemm_gateup_mx(gp.bm_small, xq, a_rows, xsc, xs_stride, w.gate, gsc, w.up, usc,
-                                  E * I, I, H, h, hsc, slots, ss, cnt + 1, L.max_tiles_small, 0,
-                                  flags, st));
+  if (merged) {
+    MOE_HIP(launch_gemm_gateup_mx2(xq, a_rows, xsc, xs_stride, w.gate, gsc, w.up, usc, E * I, I, H, h, hsc,
+                                   slots, sb, cnt, L.max_tiles_big, ss, cnt + 1, L.max_tiles_small, flags,
+                                   st));
+  } else {
+    if (gp.has_big())
+      MOE_HIP(launch_gemm_gateup_mx(gp.bm_big, xq, a_rows, xsc, xs_stride, w.gate, gsc, w.up, usc,
+                                    E * I, I, H, h, hsc, slots, sb, cnt, L.max_tiles_big, 0, flags,
+                                    st));
+    if (gp.has_small())
+      MOE_HIP(launch_gemm_gateup_mx(gp.bm_small, xq, a_rows, xsc, xs_stride, w.gate, gsc, w.up, usc,
+                                    E * I, I, H, h, hsc, slots, ss, cnt + 1, L.max_tiles_small, 0,
+                                    flags, st));
+  }
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATE_UP, false, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_DOWN, true, st));
-  if (gp.has_big())
-    MOE_HIP(launch_gemm_down_mx(gp.bm_big, h, hsc, slots, w.down, dsc, E * H, H, I, y, H, sb, cnt,
-                                L.max_tiles_big, 0, st));
-  if (gp.has_small())
-    MOE_HIP(launch_gemm_down_mx(gp.bm_small, h, hsc, slots, w.down, dsc, E * H, H, I, y, H, ss,
-                                cnt + 1, L.max_tiles_small, 0, st));
+  if (merged) {
+    MOE_HIP(launch_gemm_down_mx2(h, hsc, slots, w.down, dsc, E * H, H, I, y, H, sb, cnt, L.max_tiles_big, ss,
+                                 cnt + 1, L.max_tiles_small, st));
+  } else {
+    if (gp.has_big())
+      MOE_HIP(launch_gemm_down_mx(gp.bm_big, h, hsc, slots, w.down, dsc, E * H, H, I, y, H, sb, cnt,
+                                  L.max_tiles_big, 0, st));
+    if (gp.has_small())
+      MOE_HIP(launch_gemm_down_mx(gp.bm_small, h, hsc, slots, w.down, dsc, E * H, H, I, y, H, ss,
+                                  cnt + 1, L.max_tiles_small, 0, st, gp.has_big() ? 1 : ksplit,
+                                  (long long)slots * H));
+  }
   MOE_HIP(stage_mark(dbg, MOE_STAGE_DOWN, false, st));
   return MOE_OK;
 }
@@ -515,7 +558,7 @@ moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* 
   // S6 gather: fused into the gate/up GEMM's tile loads (rows x[row_token[r]])
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATHER, true, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATHER, false, st));
-  MOE_TRY(run_ffn(s, x, row_token, offsets, w_gate, w_up, w_down, y, ws, L, st, dbg));
+  MOE_TRY(run_ffn(s, x, row_token, offsets, w_gate, w_up, w_down, y, ws, L, st, dbg, L.ksplit));
   const float* ys = nullptr;
   MOE_HIP(stage_mark(dbg, MOE_STAGE_SHARED, true, st));
   if (s.shared_intermediate > 0) {
@@ -524,7 +567,8 @@ moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* 
   }
   MOE_HIP(stage_mark(dbg, MOE_STAGE_SHARED, false, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_COMBINE, true, st));
-  MOE_HIP(launch_combine(s, y, ros, gates, ys, out, st));
+  MOE_HIP(launch_combine(s, y, ros, gates, ys, out, st, L.ksplit,
+                         (long long)s.num_tokens * s.top_k * s.hidden));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_COMBINE, false, st));
   return MOE_OK;
 }
@@ -631,7 +675,7 @@ moe_status moe_layer_forward_mxfp8(const moe_shape* shape, const void* x, const 
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATHER, true, st));
   MOE_HIP(launch_quant_mxfp8(MOE_BF16, x, T, s.hidden, T, xq, xsc, flags, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATHER, false, st));
-  MOE_TRY(run_ffn_mx(s, xq, row_token, xsc, T, offsets, *experts, y, ws, L, st, dbg));
+  MOE_TRY(run_ffn_mx(s, xq, row_token, xsc, T, offsets, *experts, y, ws, L, st, dbg, L.ksplit));
   const float* ys = nullptr;
   MOE_HIP(stage_mark(dbg, MOE_STAGE_SHARED, true, st));
   if (s.shared_intermediate > 0) {
@@ -640,7 +684,8 @@ moe_status moe_layer_forward_mxfp8(const moe_shape* shape, const void* x, const 
   }
   MOE_HIP(stage_mark(dbg, MOE_STAGE_SHARED, false, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_COMBINE, true, st));
-  MOE_HIP(launch_combine(s, y, ros, gates, ys, out, st));
+  MOE_HIP(launch_combine(s, y, ros, gates, ys, out, st, L.ksplit,
+                         (long long)s.num_tokens * s.top_k * s.hidden));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_COMBINE, false, st));
   return MOE_OK;
 }

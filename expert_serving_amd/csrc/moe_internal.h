@@ -30,6 +30,9 @@ struct WsLayout {
   size_t flags, logits, ids, gates, counts, offsets, tile_counts, row_of_slot, row_token,
       num_dropped, sched_big, sched_small, sched_count, h, y, hs, ys, xq, xsc, hsc, hssc, total;
   int n_dispatch_tiles;
+  // K-split of the layer's down projection: y holds ksplit partial sums,
+  // part p at y + p * slots * H floats (1: no split)
+  int ksplit;
   int max_tiles_big, max_tiles_small;
 };
 
@@ -94,10 +97,13 @@ hipError_t launch_gemm_gateup(int dtype, int bm, const void* A, const int32_t* a
                               int static_rows, uint32_t* flags, hipStream_t st);
 // plain: Y[r][n] = A[r].B[e][n] (+ bias[n]), fp32 out.  a_is_h: A is the
 // fp16 h of a bf16 layer (down projection), B is converted to fp16 on load.
+// ksplit > 1 (32-row down tiles): K in ksplit ranges of whole 64-element
+// stages, range p's partial sums at Y + p * part_elems.
 hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int lda,
                              const void* B, int N, int K, const float* bias, float* Y, int ldy,
                              const MTile* sched, const int32_t* count, int max_tiles,
-                             int static_rows, hipStream_t st);
+                             int static_rows, hipStream_t st,
+                             int ksplit = 1, long long part_elems = 0);
 
 // MXFP8 path (codes + E8M0 scales; scale words group-major, see mxfp8.hip).
 // Quantises rows x cols (cols a multiple of 128) of bf16 / fp32 src; inf/NaN
@@ -114,12 +120,33 @@ hipError_t launch_gemm_gateup_mx(int bm, const void* A, const int32_t* a_rows, c
 hipError_t launch_gemm_down_mx(int bm, const void* A, const uint8_t* hsc, int hs_stride,
                                const void* B, const uint8_t* sb, int sb_stride, int N, int K,
                                float* Y, int ldy, const MTile* sched, const int32_t* count,
-                               int max_tiles, int static_rows, hipStream_t st);
+                               int max_tiles, int static_rows, hipStream_t st,
+                               int ksplit = 1, long long part_elems = 0);
+
+// Both row-tile classes (256-row and 32-row tiles of the big and small
+// schedules) in one interleaved launch.
+hipError_t launch_gemm_gateup2(const void* A, const int32_t* a_rows, int lda, const void* Bg,
+                               const void* Bu, int N, int K, void* h, int ldh, const MTile* sb,
+                               const int32_t* cb, int mb, const MTile* ss, const int32_t* cs, int ms,
+                               uint32_t* flags, hipStream_t st);
+hipError_t launch_gemm_down2(const void* A, int lda, const void* B, int N, int K, float* Y, int ldy,
+                             const MTile* sb, const int32_t* cb, int mb, const MTile* ss,
+                             const int32_t* cs, int ms, hipStream_t st);
+hipError_t launch_gemm_gateup_mx2(const void* A, const int32_t* a_rows, const uint8_t* sa, int sa_stride,
+                                  const void* Bg, const uint8_t* sbg, const void* Bu, const uint8_t* sbu,
+                                  int sb_stride, int N, int K, void* h, uint8_t* hsc, int hs_stride,
+                                  const MTile* sb, const int32_t* cb, int mb, const MTile* ss,
+                                  const int32_t* cs, int ms, uint32_t* flags, hipStream_t st);
+hipError_t launch_gemm_down_mx2(const void* A, const uint8_t* hsc, int hs_stride, const void* B,
+                                const uint8_t* sb_w, int sb_stride, int N, int K, float* Y, int ldy,
+                                const MTile* sb, const int32_t* cb, int mb, const MTile* ss,
+                                const int32_t* cs, int ms, hipStream_t st);
 
 // Row-tile height the GEMM launchers use for a dtype and a requested height.
 int gemm_tile_rows(int dtype, int bm_hint);
 
 hipError_t launch_combine(const moe_shape& s, const float* y_perm, const int32_t* row_of_slot,
-                          const float* gates, const float* y_shared, void* out, hipStream_t st);
+                          const float* gates, const float* y_shared, void* out, hipStream_t st,
+                          int parts = 1, long long part_stride = 0);
 
 }  // namespace moe
