@@ -44,8 +44,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (b + (((b >> 16) & 1u) + 0x7FFFu)) >> 16;
 }
 
+// silu(g) * u with silu(g) = g / (1 + e^-g).  The reciprocal is the
+// hardware's v_rcp_f32 (about 1 ulp) rather than an IEEE division: the
+// correctly rounded divide expands to a dozen instructions per element and
+// cost a tenth of the gate/up kernel's time in its epilogue, while h is
+// rounded to fp16 or E4M3 right after.  For e^-g = inf (g < -88) the
+// reciprocal is 0 and the result a signed zero, as with the division.
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  return g / (1.0f + __expf(-g)) * u;
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 // Row tile m and column tile n of logical tile L of a class with mtiles x
@@ -131,6 +137,10 @@ struct MxArgs {
   const uint8_t* sb1;
   uint8_t* sout;
   int sa_stride, sb_stride, sout_stride;
+  // 1: the token scales are already in tile-row order (word row0 + r) even
+  // when the codes are gathered through a_rows, so a wavefront's scale words
+  // are contiguous instead of one cache line per lane
+  int sa_direct;
 };
 
 // E8M0 byte of a block with maximum magnitude amax (finite, >= 0):
@@ -387,6 +397,10 @@ __device__ __forceinline__ void gemm_tile(
     constexpr int NA = MX ? (BM + 8 * NW - 1) / (8 * NW) : NI;  // chunks that may hold token rows
       static_assert(!MX || NI <= 16, "scale words: at most two per lane and stage");
     uint32_t* const sc_lds = reinterpret_cast<uint32_t*>(smem + 2 * PSTAGE);  // [2][ROWS] (MX)
+    // scale word of tile row r sits at r ^ (((r >> 6) & 7) << 3): the eight
+    // 8-row chunks a wavefront stores (rows 64 apart) then fall in distinct
+    // banks, and 32 consecutive fragment rows stay in distinct banks
+    auto sc_idx = [](int r) { return r ^ (((r >> 6) & 7) << 3); };
 #define MOE_READ_FRAGS_P(set_, step_, ks_)                                              \
   do {                                                                                  \
     const uint16_t* sA_ = smem + (((step_) >> 1) & 1) * PSTAGE;                         \
@@ -431,10 +445,10 @@ __device__ __forceinline__ void gemm_tile(
     }                                                                                   \
     if (((step_) & 1) == 0) {                                                           \
       const uint32_t* sc_ = sc_lds + (((step_) >> 1) & 1) * ROWS;                       \
-      _Pragma("unroll") for (int b = 0; b < FM; ++b) scc[b] = sc_[wm * WM + b * 32 + fr]; \
+      _Pragma("unroll") for (int b = 0; b < FM; ++b) scc[b] = sc_[sc_idx(wm * WM + b * 32 + fr)]; \
       _Pragma("unroll") for (int a = 0; a < FN; ++a) {                                  \
-        scc[FM + a] = sc_[BM + wn * WN + a * 32 + fr];                                  \
-        if constexpr (DUAL) scc[FM + FN + a] = sc_[BM + BNB + wn * WN + a * 32 + fr];   \
+        scc[FM + a] = sc_[sc_idx(BM + wn * WN + a * 32 + fr)];                          \
+        if constexpr (DUAL) scc[FM + FN + a] = sc_[sc_idx(BM + BNB + wn * WN + a * 32 + fr)]; \
       }                                                                                 \
     }                                                                                   \
   } while (0)
@@ -465,7 +479,7 @@ __device__ __forceinline__ void gemm_tile(
         if (rho < BM) {
           const int r = min(rho, rows - 1);
           base = reinterpret_cast<const uint32_t*>(mx.sa);
-          row = a_rows ? a_rows[row0 + r] : row0 + r;
+          row = (a_rows && !mx.sa_direct) ? a_rows[row0 + r] : row0 + r;
           strd = mx.sa_stride;
         } else if (rho < BM + NB * BNB) {
           base = reinterpret_cast<const uint32_t*>(rho < BM + BNB ? mx.sb0 : mx.sb1);
@@ -494,7 +508,7 @@ __device__ __forceinline__ void gemm_tile(
     if constexpr (MX) {                                                                 \
       _Pragma("unroll") for (int q = 0; q < NSL; ++q) {                                 \
         if (8 * q + (lane >> 3) < NI)                                                   \
-          sc_lds[((stage_) & 1) * ROWS + 8 * (wave + NW * (8 * q + (lane >> 3))) + (lane & 7)] = scl[q]; \
+          sc_lds[((stage_) & 1) * ROWS + sc_idx(8 * (wave + NW * (8 * q + (lane >> 3))) + (lane & 7))] = scl[q]; \
       }                                                                                 \
     }                                                                                   \
   } while (0)
@@ -694,10 +708,16 @@ __device__ __forceinline__ void gemm_tile(
   // epilogue: accumulator q of fragment (a, b) is output column
   // n = a*32 + 8*(q/4) + 4*(lane/32) + q%4 of token row m = b*32 + lane%32
   bool overflow = false;
+  // Gate/up outputs: the 32 columns of fragment (a, b) in token row m sit in
+  // lanes l (columns 8q + 0..3) and l ^ 32 (8q + 4..7), q = 0..3.  One
+  // v_permlane32_swap per pair of words gives lane l the columns 0..15 and
+  // lane l ^ 32 the columns 16..31 of the row, each stored as whole 16-byte
+  // chunks (one per lane for E4M3 codes, two for fp16) instead of four
+  // scattered 4- or 8-byte stores.  Cross-lane steps run on every lane; the
+  // row and column bounds only gate the stores.
   if constexpr (MODE == kGateUpMX) {
-    // h of one 32-column block of a token row sits in lanes l and l^32 (16
-    // each): its maximum magnitude sets the block's E8M0 scale, and each lane
-    // writes its 16 codes (4 words) and lane l < 32 the scale byte
+    // the block's maximum magnitude (both lane halves) sets its E8M0 scale;
+    // lane l < 32 also writes the scale byte
 #pragma unroll
     for (int b = 0; b < FM; ++b) {
       const int m = wm * WM + b * 32 + fr;
@@ -711,20 +731,58 @@ __device__ __forceinline__ void gemm_tile(
           hv[q] = silu_mul(acc0[a][b][q], acc1[a][b][q]);
           amax = fmaxf(amax, fabsf(hv[q]));
         }
-        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-        if (m >= rows || nb >= N) continue;
-        overflow |= !(amax <= 3.402823466e38f);
+        const auto am = __builtin_amdgcn_permlane32_swap(__float_as_uint(amax), __float_as_uint(amax),
+                                                         false, false);
+        amax = fmaxf(amax, __uint_as_float(fk ? am[0] : am[1]));
         const uint32_t sb = mx_scale_byte(amax);
         const int sh = 127 - (int)sb;
-        uint8_t* dst = static_cast<uint8_t*>(Out) + (size_t)(row0 + m) * ldo + nb + 4 * fk;
+        uint32_t w[4];
 #pragma unroll
         for (int qi = 0; qi < 4; ++qi)
-          *reinterpret_cast<uint32_t*>(dst + 8 * qi) =
-              e4m3x4(ldexpf(hv[4 * qi], sh), ldexpf(hv[4 * qi + 1], sh),
-                     ldexpf(hv[4 * qi + 2], sh), ldexpf(hv[4 * qi + 3], sh));
+          w[qi] = e4m3x4(ldexpf(hv[4 * qi], sh), ldexpf(hv[4 * qi + 1], sh), ldexpf(hv[4 * qi + 2], sh),
+                         ldexpf(hv[4 * qi + 3], sh));
+        const auto s02 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+        const auto s13 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+        if (m >= rows || nb >= N) continue;
+        overflow |= !(amax <= 3.402823466e38f);
+        *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(Out) + (size_t)(row0 + m) * ldo + nb + 16 * fk) =
+            u32x4{s02[0], s02[1], s13[0], s13[1]};
         if (fk == 0)
           mx.sout[((size_t)(nb >> 7) * mx.sout_stride + row0 + m) * 4 + ((nb >> 5) & 3)] =
               (uint8_t)sb;
+      }
+    }
+  } else if constexpr (MODE == kGateUp) {
+    // fp16 h (N is a multiple of 64, so a 32-column block is all in or out)
+#pragma unroll
+    for (int b = 0; b < FM; ++b) {
+      const int m = wm * WM + b * 32 + fr;
+#pragma unroll
+      for (int a = 0; a < FN; ++a) {
+        const int nb = n0 + wn * WN + a * 32;
+        const f32x16 g = acc0[a][b], u = acc1[a][b];
+        uint32_t px[4], py[4];
+        bool ovf = false;
+#pragma unroll
+        for (int qi = 0; qi < 4; ++qi) {
+          const float h0 = silu_mul(g[4 * qi], u[4 * qi]);
+          const float h1 = silu_mul(g[4 * qi + 1], u[4 * qi + 1]);
+          const float h2 = silu_mul(g[4 * qi + 2], u[4 * qi + 2]);
+          const float h3 = silu_mul(g[4 * qi + 3], u[4 * qi + 3]);
+          ovf |= !(fabsf(h0) <= 65504.f && fabsf(h1) <= 65504.f && fabsf(h2) <= 65504.f &&
+                   fabsf(h3) <= 65504.f);
+          px[qi] = f32_to_f16_bits(h0) | (f32_to_f16_bits(h1) << 16);
+          py[qi] = f32_to_f16_bits(h2) | (f32_to_f16_bits(h3) << 16);
+        }
+        const auto x02 = __builtin_amdgcn_permlane32_swap(px[0], px[2], false, false);
+        const auto y02 = __builtin_amdgcn_permlane32_swap(py[0], py[2], false, false);
+        const auto x13 = __builtin_amdgcn_permlane32_swap(px[1], px[3], false, false);
+        const auto y13 = __builtin_amdgcn_permlane32_swap(py[1], py[3], false, false);
+        if (m >= rows || nb >= N) continue;
+        overflow |= ovf;
+        uint16_t* dst = static_cast<uint16_t*>(Out) + (size_t)(row0 + m) * ldo + nb + 16 * fk;
+        *reinterpret_cast<u32x4*>(dst) = u32x4{x02[0], y02[0], x02[1], y02[1]};
+        *reinterpret_cast<u32x4*>(dst + 8) = u32x4{x13[0], y13[0], x13[1], y13[1]};
       }
     }
   } else {
@@ -738,21 +796,7 @@ __device__ __forceinline__ void gemm_tile(
       for (int qi = 0; qi < 4; ++qi) {
         const int n = n0 + wn * WN + a * 32 + 8 * qi + 4 * fk;
         const size_t o = (size_t)(row0 + m) * ldo + n;
-        if constexpr (DUAL) {
-          if (n + 3 < N) {
-            const f32x16 g = acc0[a][b], u = acc1[a][b];
-            const float h0 = silu_mul(g[4 * qi], u[4 * qi]);
-            const float h1 = silu_mul(g[4 * qi + 1], u[4 * qi + 1]);
-            const float h2 = silu_mul(g[4 * qi + 2], u[4 * qi + 2]);
-            const float h3 = silu_mul(g[4 * qi + 3], u[4 * qi + 3]);
-            overflow |= !(fabsf(h0) <= 65504.f && fabsf(h1) <= 65504.f &&
-                          fabsf(h2) <= 65504.f && fabsf(h3) <= 65504.f);
-            u32x2 pk;
-            pk[0] = f32_to_f16_bits(h0) | (f32_to_f16_bits(h1) << 16);
-            pk[1] = f32_to_f16_bits(h2) | (f32_to_f16_bits(h3) << 16);
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Out) + o) = pk;
-          }
-        } else {
+        {
           const f32x16 acc = acc0[a][b];
           f32x4 v = {acc[4 * qi], acc[4 * qi + 1], acc[4 * qi + 2], acc[4 * qi + 3]};
           float* dst = static_cast<float*>(Out) + o;
@@ -1079,10 +1123,10 @@ hipError_t launch_gemm_gateup_mx(int bm, const void* A, const int32_t* a_rows, c
                                  const uint8_t* sbu, int sb_stride, int N, int K, void* h,
                                  uint8_t* hsc, int hs_stride, const MTile* sched,
                                  const int32_t* count, int max_tiles, int static_rows,
-                                 uint32_t* flags, hipStream_t st) {
+                                 uint32_t* flags, hipStream_t st, bool sa_direct) {
   const int mslots = sched ? max_tiles : (static_rows + bm - 1) / bm;
   if (mslots == 0) return hipSuccess;
-  const MxArgs mx{sa, sbg, sbu, hsc, sa_stride, sb_stride, hs_stride};
+  const MxArgs mx{sa, sbg, sbu, hsc, sa_stride, sb_stride, hs_stride, sa_direct ? 1 : 0};
   const int K2 = K / 2;  // 16-bit units
   if (bm == 256)
     return launch_mfma<256, 128, kGateUpMX, 2, 8>(A, a_rows, K2, Bg, Bu, N, K2, h, N, nullptr, sched,
@@ -1138,8 +1182,9 @@ hipError_t launch_gemm_gateup_mx2(const void* A, const int32_t* a_rows, const ui
                                   const void* Bg, const uint8_t* sbg, const void* Bu, const uint8_t* sbu,
                                   int sb_stride, int N, int K, void* h, uint8_t* hsc, int hs_stride,
                                   const MTile* sb, const int32_t* cb, int mb, const MTile* ss,
-                                  const int32_t* cs, int ms, uint32_t* flags, hipStream_t st) {
-  const MxArgs mx{sa, sbg, sbu, hsc, sa_stride, sb_stride, hs_stride};
+                                  const int32_t* cs, int ms, uint32_t* flags, hipStream_t st,
+                                  bool sa_direct) {
+  const MxArgs mx{sa, sbg, sbu, hsc, sa_stride, sb_stride, hs_stride, sa_direct ? 1 : 0};
   return launch_mfma2<256, 128, 32, 256, kGateUpMX>(A, a_rows, K / 2, Bg, Bu, N, K / 2, h, N, flags, sb, cb,
                                                     mb, ss, cs, ms, st, mx);
 }

@@ -199,6 +199,7 @@ WsLayout plan_workspace(const moe_shape& s, bool mx) {
   if (mx) {
     w.xq = take(T * H);
     w.xsc = take(T * H / 32);
+    w.xscp = take(slots * H / 32);
     w.hsc = take(slots * I / 32);
     w.hssc = take(T * Is / 32);
   }
@@ -278,7 +279,8 @@ moe_status run_ffn(const moe_shape& s, const void* x_perm, const int32_t* a_rows
 moe_status run_ffn_mx(const moe_shape& s, const void* xq, const int32_t* a_rows,
                       const uint8_t* xsc, int xs_stride, const int32_t* offsets,
                       const moe_mxfp8_ffn& w, float* y, void* ws, const WsLayout& L,
-                      hipStream_t st, const moe_debug* dbg = nullptr, int ksplit = 1) {
+                      hipStream_t st, const moe_debug* dbg = nullptr, int ksplit = 1,
+                      bool sa_direct = false) {
   const GemmPlan gp = choose_gemm_plan(s);
   const int E = s.num_experts, H = s.hidden, I = s.intermediate;
   const int slots = s.num_tokens * s.top_k;
@@ -296,16 +298,16 @@ moe_status run_ffn_mx(const moe_shape& s, const void* xq, const int32_t* a_rows,
   if (merged) {
     MOE_HIP(launch_gemm_gateup_mx2(xq, a_rows, xsc, xs_stride, w.gate, gsc, w.up, usc, E * I, I, H, h, hsc,
                                    slots, sb, cnt, L.max_tiles_big, ss, cnt + 1, L.max_tiles_small, flags,
-                                   st));
+                                   st, sa_direct));
   } else {
     if (gp.has_big())
       MOE_HIP(launch_gemm_gateup_mx(gp.bm_big, xq, a_rows, xsc, xs_stride, w.gate, gsc, w.up, usc,
                                     E * I, I, H, h, hsc, slots, sb, cnt, L.max_tiles_big, 0, flags,
-                                    st));
+                                    st, sa_direct));
     if (gp.has_small())
       MOE_HIP(launch_gemm_gateup_mx(gp.bm_small, xq, a_rows, xsc, xs_stride, w.gate, gsc, w.up, usc,
                                     E * I, I, H, h, hsc, slots, ss, cnt + 1, L.max_tiles_small, 0,
-                                    flags, st));
+                                    flags, st, sa_direct));
   }
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATE_UP, false, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_DOWN, true, st));
@@ -674,11 +676,15 @@ moe_status moe_layer_forward_mxfp8(const moe_shape* shape, const void* x, const 
                           at<int32_t>(ws, L.tile_counts), L.n_dispatch_tiles, flags, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_DISPATCH, false, st));
   // S6: the dispatch payload is x quantised once per token; the row gather
-  // itself is fused into the gate/up GEMM's tile loads
+  // itself is fused into the gate/up GEMM's tile loads, and the scale words
+  // are also written in dispatch-row order for it
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATHER, true, st));
-  MOE_HIP(launch_quant_mxfp8(MOE_BF16, x, T, s.hidden, T, xq, xsc, flags, st));
+  uint8_t* xscp = at<uint8_t>(ws, L.xscp);
+  MOE_HIP(launch_quant_mxfp8(MOE_BF16, x, T, s.hidden, T, xq, xsc, flags, st, ros, s.top_k, xscp,
+                             T * s.top_k));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATHER, false, st));
-  MOE_TRY(run_ffn_mx(s, xq, row_token, xsc, T, offsets, *experts, y, ws, L, st, dbg, L.ksplit));
+  MOE_TRY(run_ffn_mx(s, xq, row_token, xscp, T * s.top_k, offsets, *experts, y, ws, L, st, dbg, L.ksplit,
+                     true));
   const float* ys = nullptr;
   MOE_HIP(stage_mark(dbg, MOE_STAGE_SHARED, true, st));
   if (s.shared_intermediate > 0) {

@@ -23,12 +23,13 @@ struct MTile {
 };
 
 // Byte offsets of every region inside the caller's workspace.
-// MXFP8 layers add the quantised x (xq, scales xsc with stride T) and the
-// scales of h (hsc, stride T*top_k) and of the shared expert's h (hssc,
-// stride T); h and hs then hold one-byte codes.
+// MXFP8 layers add the quantised x (xq, scales xsc with stride T, and the
+// same scales in dispatch-row order, xscp with stride T*top_k) and the scales
+// of h (hsc, stride T*top_k) and of the shared expert's h (hssc, stride T);
+// h and hs then hold one-byte codes.
 struct WsLayout {
   size_t flags, logits, ids, gates, counts, offsets, tile_counts, row_of_slot, row_token,
-      num_dropped, sched_big, sched_small, sched_count, h, y, hs, ys, xq, xsc, hsc, hssc, total;
+      num_dropped, sched_big, sched_small, sched_count, h, y, hs, ys, xq, xsc, xscp, hsc, hssc, total;
   int n_dispatch_tiles;
   // K-split of the layer's down projection: y holds ksplit partial sums,
   // part p at y + p * slots * H floats (1: no split)
@@ -108,15 +109,19 @@ hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int 
 // MXFP8 path (codes + E8M0 scales; scale words group-major, see mxfp8.hip).
 // Quantises rows x cols (cols a multiple of 128) of bf16 / fp32 src; inf/NaN
 // inputs set MOE_FLAG_H_RANGE when flags is given.
+// row_of_slot (nullable, [rows][k]): also write each scale byte at the
+// dispatch rows of the row's kept slots in perm_scales (stride perm_stride).
 hipError_t launch_quant_mxfp8(int src_dtype, const void* src, int rows, int cols, int stride,
-                              uint8_t* codes, uint8_t* scales, uint32_t* flags, hipStream_t st);
+                              uint8_t* codes, uint8_t* scales, uint32_t* flags, hipStream_t st,
+                              const int32_t* row_of_slot = nullptr, int k = 0,
+                              uint8_t* perm_scales = nullptr, int perm_stride = 0);
 // gate/up + SwiGLU with h re-quantised to MXFP8; bm 256 / 128 / 32
 hipError_t launch_gemm_gateup_mx(int bm, const void* A, const int32_t* a_rows, const uint8_t* sa,
                                  int sa_stride, const void* Bg, const uint8_t* sbg, const void* Bu,
                                  const uint8_t* sbu, int sb_stride, int N, int K, void* h,
                                  uint8_t* hsc, int hs_stride, const MTile* sched,
                                  const int32_t* count, int max_tiles, int static_rows,
-                                 uint32_t* flags, hipStream_t st);
+                                 uint32_t* flags, hipStream_t st, bool sa_direct = false);
 hipError_t launch_gemm_down_mx(int bm, const void* A, const uint8_t* hsc, int hs_stride,
                                const void* B, const uint8_t* sb, int sb_stride, int N, int K,
                                float* Y, int ldy, const MTile* sched, const int32_t* count,
@@ -136,7 +141,8 @@ hipError_t launch_gemm_gateup_mx2(const void* A, const int32_t* a_rows, const ui
                                   const void* Bg, const uint8_t* sbg, const void* Bu, const uint8_t* sbu,
                                   int sb_stride, int N, int K, void* h, uint8_t* hsc, int hs_stride,
                                   const MTile* sb, const int32_t* cb, int mb, const MTile* ss,
-                                  const int32_t* cs, int ms, uint32_t* flags, hipStream_t st);
+                                  const int32_t* cs, int ms, uint32_t* flags, hipStream_t st,
+                                  bool sa_direct = false);
 hipError_t launch_gemm_down_mx2(const void* A, const uint8_t* hsc, int hs_stride, const void* B,
                                 const uint8_t* sb_w, int sb_stride, int N, int K, float* Y, int ldy,
                                 const MTile* sb, const int32_t* cb, int mb, const MTile* ss,

@@ -50,12 +50,19 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   return (uint32_t)p;
 }
 
+// When row_of_slot is given, each scale byte is also written for every kept
+// slot of the row (row r = token r, slots r * k .. r * k + k - 1) at its
+// dispatch row in perm_scales (stride perm_stride): the grouped GEMM then
+// reads the token scales of a row tile as consecutive words.
 template <bool BF16>
 __global__ __launch_bounds__(kQuantThreads) void k_quant_mxfp8(const void* __restrict__ src,
                                                                int rows, int cols, int stride,
                                                                uint8_t* __restrict__ codes,
                                                                uint8_t* __restrict__ scales,
-                                                               uint32_t* __restrict__ flags) {
+                                                               uint32_t* __restrict__ flags,
+                                                               const int32_t* __restrict__ row_of_slot,
+                                                               int k, uint8_t* __restrict__ perm_scales,
+                                                               int perm_stride) {
   const int lane = threadIdx.x & 63;
   const long long seg = (long long)blockIdx.x * (kQuantThreads / 64) + (threadIdx.x >> 6);
   const int segs_per_row = (cols + 511) / 512;
@@ -103,22 +110,32 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_mxfp8(const void* __res
   if ((lane & 3) == 0) {
     const int b = c >> 5;
     scales[((size_t)(b >> 2) * stride + r) * 4 + (b & 3)] = (uint8_t)sb;
+    if (row_of_slot) {
+      for (int j = 0; j < k; ++j) {
+        const int rr = row_of_slot[(size_t)r * k + j];
+        if (rr >= 0) perm_scales[((size_t)(b >> 2) * perm_stride + rr) * 4 + (b & 3)] = (uint8_t)sb;
+      }
+    }
   }
 }
 
 }  // namespace
 
 hipError_t launch_quant_mxfp8(int src_dtype, const void* src, int rows, int cols, int stride,
-                              uint8_t* codes, uint8_t* scales, uint32_t* flags, hipStream_t st) {
+                              uint8_t* codes, uint8_t* scales, uint32_t* flags, hipStream_t st,
+                              const int32_t* row_of_slot, int k, uint8_t* perm_scales,
+                              int perm_stride) {
   const long long segs = (long long)rows * ((cols + 511) / 512);
   const long long blocks = (segs + kQuantThreads / 64 - 1) / (kQuantThreads / 64);
   if (blocks == 0) return hipSuccess;
   if (src_dtype == MOE_BF16)
     hipLaunchKernelGGL(k_quant_mxfp8<true>, dim3((unsigned)blocks), dim3(kQuantThreads), 0, st, src,
-                       rows, cols, stride, codes, scales, flags);
+                       rows, cols, stride, codes, scales, flags, row_of_slot, k, perm_scales,
+                       perm_stride);
   else
     hipLaunchKernelGGL(k_quant_mxfp8<false>, dim3((unsigned)blocks), dim3(kQuantThreads), 0, st, src,
-                       rows, cols, stride, codes, scales, flags);
+                       rows, cols, stride, codes, scales, flags, row_of_slot, k, perm_scales,
+                       perm_stride);
   return hipGetLastError();
 }
 
