@@ -1,0 +1,108 @@
+"""Edge cases of the layer through the C ABI, bf16 and MXFP8 experts: an empty
+batch, a single token, one expert (the layer is then a dense SwiGLU FFN),
+every expert selected (k = E, no renormalisation: the dense softmax
+mixture), a capacity of one row per expert, and graph capture of the MXFP8
+layer.  Comparisons as in test_gpu_layer.py (bf16) and test_gpu_mxfp8.py
+(MXFP8)."""
+
+import pytest
+import torch
+
+import workloads as W
+from expert_serving_amd import abi
+
+from gpu_util import dev, say
+from test_gpu_layer import compare_layer
+from test_gpu_mxfp8 import compare_layer_mx
+
+pytestmark = pytest.mark.gpu
+
+EDGE = {
+    # one expert, k = 1: the layer is one dense SwiGLU FFN with gate 1
+    "one_expert": W.LayerConfig("one_expert", 300, 512, 1, 256, 1),
+    # every expert selected without renormalisation: the dense softmax mixture
+    "all_experts": W.LayerConfig("all_experts", 200, 512, 4, 256, 4, renormalize=0),
+    # capacity ceil(1e-4 * 512 / 8) = 1: each expert keeps its first slot
+    "capacity_one": W.LayerConfig("capacity_one", 256, 512, 8, 256, 2, capacity_factor=1e-4),
+}
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("name", list(EDGE))
+def test_layer_edge_shapes(name, fmt):
+    cfg = EDGE[name]
+    say(f"edge {name} {fmt}")
+    inp = W.make_layer_inputs(cfg, dev(), salt=7)
+    (compare_layer if fmt == "bf16" else compare_layer_mx)(cfg, inp)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("name", ["mixtral_prefill", "deepseek_v3"])
+def test_layer_single_token(name, fmt):
+    cfg = W.CONFIGS[name].with_tokens(1)
+    say(f"single token {name} {fmt}")
+    inp = W.make_layer_inputs(cfg, dev(), salt=8)
+    (compare_layer if fmt == "bf16" else compare_layer_mx)(cfg, inp)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp8"])
+def test_layer_empty_batch(fmt):
+    """T = 0: the call succeeds, launches nothing and writes nothing."""
+    cfg = W.CONFIGS["deepseek_v3"].with_tokens(0)
+    shape = abi.make_shape(cfg)
+    H = cfg.hidden
+    say(f"empty batch {fmt}")
+    dummy = torch.zeros(64, dtype=torch.float32, device=dev())  # any valid aligned pointer
+    out = torch.full((4, H), 7.0, dtype=torch.float32, device=dev())
+    if fmt == "bf16":
+        ws = torch.empty(max(abi.moe_workspace_size(shape), 256), dtype=torch.uint8, device=dev())
+        abi.moe_layer_forward(shape, dummy, dummy, dummy, None, dummy, dummy, dummy, dummy, dummy, dummy, out,
+                              None, ws)
+    else:
+        ws = torch.empty(max(abi.moe_workspace_size_mxfp8(shape), 256), dtype=torch.uint8, device=dev())
+        ffn = abi.MoeMxfp8Ffn(*([dummy.data_ptr()] * 6))
+        abi.moe_layer_forward_mxfp8(shape, dummy, dummy, dummy, None, ffn, ffn, out, None, ws)
+    torch.cuda.synchronize()
+    assert (out == 7.0).all()
+
+
+@pytest.mark.parametrize("name,T", [("mixtral_decode", 64), ("qwen3_skewed", 1024)])
+def test_mxfp8_layer_graph_replay_matches_eager(name, T):
+    """The MXFP8 layer call captured once and replayed, with eager calls and
+    synchronisations between replays, reproduces the eager result bit for bit."""
+    cfg = W.CONFIGS[name].with_tokens(T)
+    say(f"mxfp8 graph capture {name} T={T}")
+    inp = W.make_layer_inputs(cfg, dev(), salt=9)
+    mw = abi.mxfp8_ffn(inp["w_gate"], inp["w_up"], inp["w_down"])
+    mws = abi.mxfp8_ffn(inp["ws_gate"], inp["ws_up"], inp["ws_down"]) if cfg.shared_inter else None
+    shape = abi.make_shape(cfg)
+    ws = torch.empty(abi.moe_workspace_size_mxfp8(shape), dtype=torch.uint8, device=dev())
+    out = torch.empty(cfg.tokens, cfg.hidden, dtype=torch.float32, device=dev())
+
+    def call():
+        abi.moe_layer_forward_mxfp8(shape, inp["x"], inp["w_router"], inp["bias"], inp["k_per_token"], mw, mws,
+                                    out, None, ws)
+
+    call()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for i in range(3):
+        out.fill_(float("nan"))
+        ws.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {i} differs from the eager result"
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+    assert abi.moe_read_device_flags(ws) == 0
