@@ -299,17 +299,38 @@ __global__ __launch_bounds__(256) void k_gather(const uint4* __restrict__ x,
 // list in tiles of bm_small rows.
 __global__ __launch_bounds__(512) void k_build_sched(const int32_t* __restrict__ offsets, int E,
                                                      int bm_big, int bm_small, int split_rows,
+                                                     int tail_rows,
                                                      MTile* __restrict__ sched_big, int max_big,
                                                      MTile* __restrict__ sched_small, int max_small,
                                                      int32_t* __restrict__ count) {
   __shared__ int s_big[512], s_small[512];
   const int tid = threadIdx.x;
-  int r0 = 0, kept = 0, nb = 0, ns = 0;
+  // an expert with at least split_rows rows takes big tiles; smaller experts
+  // take small tiles only.  When no expert is small (an even load), a
+  // remainder of at most tail_rows rows past a big expert's last full tile
+  // goes to small tiles too: a big tile would cost its full height for a
+  // few rows, and the small tiles stream the weights beside the big tiles.
+  // With small experts present their streams already load the memory system
+  // (measured slower with tails on the skewed layers), so there are none.
+  int r0 = 0, kept = 0, nb = 0, ns = 0, sbeg = 0;
   if (tid < E) {
     r0 = offsets[tid];
     kept = offsets[tid + 1] - r0;
-    if (kept >= split_rows) nb = (kept + bm_big - 1) / bm_big;
-    else ns = (kept + bm_small - 1) / bm_small;
+  }
+  if (__syncthreads_or(tid < E && kept > 0 && kept < split_rows)) tail_rows = 0;
+  if (tid < E) {
+    if (kept >= split_rows) {
+      nb = kept / bm_big;
+      const int rem = kept - nb * bm_big;
+      if (rem > 0 && rem <= tail_rows) {
+        sbeg = nb * bm_big;
+        ns = (rem + bm_small - 1) / bm_small;
+      } else if (rem > 0) {
+        nb += 1;
+      }
+    } else {
+      ns = (kept + bm_small - 1) / bm_small;
+    }
   }
   s_big[tid] = nb;
   s_small[tid] = ns;
@@ -322,20 +343,26 @@ __global__ __launch_bounds__(512) void k_build_sched(const int32_t* __restrict__
     s_small[tid] += as;
     __syncthreads();
   }
-  const int bm = nb ? bm_big : bm_small;
-  const int nt = nb ? nb : ns;
-  const int base = nb ? s_big[tid] - nb : s_small[tid] - ns;
-  MTile* out = nb ? sched_big : sched_small;
-  const int cap = nb ? max_big : max_small;
-  for (int i = 0; i < nt; ++i) {
-    const int slot = base + i;
-    if (slot < cap) {
+  for (int i = 0; i < nb; ++i) {
+    const int slot = s_big[tid] - nb + i;
+    if (slot < max_big) {
       MTile m;
       m.expert = tid;
-      m.row0 = r0 + i * bm;
-      m.rows = min(bm, kept - i * bm);
+      m.row0 = r0 + i * bm_big;
+      m.rows = min(bm_big, kept - i * bm_big);
       m.pad = 0;
-      out[slot] = m;
+      sched_big[slot] = m;
+    }
+  }
+  for (int i = 0; i < ns; ++i) {
+    const int slot = s_small[tid] - ns + i;
+    if (slot < max_small) {
+      MTile m;
+      m.expert = tid;
+      m.row0 = r0 + sbeg + i * bm_small;
+      m.rows = min(bm_small, kept - sbeg - i * bm_small);
+      m.pad = 0;
+      sched_small[slot] = m;
     }
   }
   if (tid == 511) {
@@ -433,8 +460,8 @@ hipError_t launch_build_schedule(const int32_t* offsets, int E, const GemmPlan& 
                                  MTile* sched_big, int max_big, MTile* sched_small, int max_small,
                                  int32_t* count, hipStream_t st) {
   hipLaunchKernelGGL(k_build_sched, dim3(1), dim3(512), 0, st, offsets, E, plan.bm_big,
-                     plan.bm_small, plan.split_rows, sched_big, max_big, sched_small, max_small,
-                     count);
+                     plan.bm_small, plan.split_rows, plan.tail_rows, sched_big, max_big, sched_small,
+                     max_small, count);
   return hipGetLastError();
 }
 

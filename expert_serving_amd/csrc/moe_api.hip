@@ -118,6 +118,11 @@ T* at(void* ws, size_t off) {
 
 }  // namespace
 
+#ifndef MOE_TAIL_ROWS
+#define MOE_TAIL_ROWS 64
+#endif
+constexpr int kTailRows = MOE_TAIL_ROWS;
+
 GemmPlan choose_gemm_plan(const moe_shape& s) {
   GemmPlan p;
   const long long slots = (long long)s.num_tokens * s.top_k;
@@ -137,6 +142,10 @@ GemmPlan choose_gemm_plan(const moe_shape& s) {
     // many experts with a few rows (Qwen3-shaped layer: 87 of 120), and an
     // empty small class costs only a few idle blocks.
     p.split_rows = 128;
+    // a big expert's last rows, when few, ride on small tiles: a 256-row
+    // tile costs its full height in MFMA time, while the small tiles stream
+    // the expert's weights beside the big tiles of the same launch
+    p.tail_rows = kTailRows;
   }
   return p;
 }
@@ -152,8 +161,10 @@ WsLayout plan_workspace(const moe_shape& s, bool mx) {
   w.max_tiles_big = gp.has_big() ? (int)(slots / (size_t)gp.bm_big + E + 1) : 0;
   {
     // a small expert has fewer than split_rows rows
-    const size_t per_expert = gp.has_big() ? ((size_t)gp.split_rows + gp.bm_small - 1) / gp.bm_small
-                                           : (size_t)-1;
+    // (small experts: under split_rows rows; big ones: a tail of at most tail_rows)
+    const size_t per_expert =
+        gp.has_big() ? ((size_t)std::max(gp.split_rows - 1, gp.tail_rows) + gp.bm_small - 1) / gp.bm_small
+                     : (size_t)-1;
     const size_t bound = slots / (size_t)gp.bm_small + E + 1;
     w.max_tiles_small = gp.has_small() ? (int)std::min(bound, per_expert == (size_t)-1 ? bound
                                                                                       : per_expert * E)

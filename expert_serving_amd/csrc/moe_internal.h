@@ -44,6 +44,7 @@ struct WsLayout {
 // INT_MAX: all small).
 struct GemmPlan {
   int bm_big, bm_small, split_rows;
+  int tail_rows = 0;  // remainder rows of a big expert placed on small tiles (0: none)
   bool has_big() const { return split_rows != 0x7fffffff; }
   bool has_small() const { return split_rows != 0; }
 };
