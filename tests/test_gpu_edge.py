@@ -5,6 +5,7 @@ mixture), a capacity of one row per expert, and graph capture of the MXFP8
 layer.  Comparisons as in test_gpu_layer.py (bf16) and test_gpu_mxfp8.py
 (MXFP8)."""
 
+import numpy as np
 import pytest
 import torch
 
@@ -43,6 +44,19 @@ def test_layer_single_token(name, fmt):
     say(f"single token {name} {fmt}")
     inp = W.make_layer_inputs(cfg, dev(), salt=8)
     (compare_layer if fmt == "bf16" else compare_layer_mx)(cfg, inp)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp8"])
+def test_layer_interleaved_classes_with_shared_expert(fmt):
+    """DeepSeek-V3-shaped with 2048 tokens (average load 64 rows, the
+    smallest batch that interleaves both tile classes in one launch per
+    projection), with the shared expert on 256-row tiles."""
+    cfg = W.CONFIGS["deepseek_v3"].with_tokens(2048)
+    say(f"interleaved classes with shared expert {fmt}")
+    inp = W.make_layer_inputs(cfg, dev(), salt=10)
+    rng = np.random.default_rng(3)
+    sample = np.array(sorted(set([0, 2047]) | set(rng.choice(2048, 14, replace=False).tolist())), np.int32)
+    (compare_layer if fmt == "bf16" else compare_layer_mx)(cfg, inp, sample=sample)
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "mxfp8"])
