@@ -179,7 +179,10 @@ WsLayout plan_workspace(const moe_shape& s, bool mx) {
     const long long blocks = (long long)w.max_tiles_small * ((H + bnb - 1) / bnb);
     w.ksplit = 1;
     if (!gp.has_big() && gp.has_small() && s.act_dtype == MOE_BF16 && blocks > 0 && blocks < 512) {
-      const int want = (int)std::min<long long>(4, 1024 / blocks);
+      // two parts measured best for both formats on the Mixtral-shaped decode
+      // layer (four or eight: the combine's extra reads cost more than the
+      // down projection gains)
+      const int want = (int)std::min<long long>(2, 1024 / blocks);
       const int stages = (int)(I / 64);
       w.ksplit = std::max(1, std::min(want, stages / 4));
     }
