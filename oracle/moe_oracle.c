@@ -458,8 +458,9 @@ double oracle_e4m3_value(int code) {
 
 /* Nearest E4M3 value to q (|q| < 512 here), ties to the even code; values at
  * or beyond 448 in magnitude saturate to 448.  The sign is kept, so a
- * negative value that rounds to zero gives 0x80. */
-static uint8_t e4m3_encode(double q) {
+ * negative value that rounds to zero gives 0x80.  pos[c] is the value of
+ * code c for c = 0 .. 0x7E (increasing), searched by bisection. */
+static uint8_t e4m3_encode(double q, const double* pos) {
   const int neg = signbit(q) != 0;
   double a = fabs(q);
   uint8_t mag;
@@ -474,13 +475,15 @@ static uint8_t e4m3_encode(double q) {
     if (e < -6) e = -6;
     const double ulp = ldexp(1.0, e - 3);
     const double r = rint(a / ulp) * ulp; /* default rounding: to nearest, ties to even */
-    /* the code whose value is r (r is representable) */
-    mag = 0;
-    for (int c = 0; c <= 0x7E; ++c)
-      if (oracle_e4m3_value(c) == r) {
-        mag = (uint8_t)c;
-        break;
-      }
+    /* the code whose value is r (r is representable; the positive codes
+     * are increasing in value) */
+    int lo = 0, hi = 0x7E;
+    while (lo < hi) {
+      const int mid = (lo + hi) / 2;
+      if (pos[mid] < r) lo = mid + 1;
+      else hi = mid;
+    }
+    mag = (uint8_t)lo;
   }
   return (uint8_t)(mag | (neg ? 0x80 : 0));
 }
@@ -494,6 +497,8 @@ static uint8_t e4m3_encode(double q) {
 void oracle_mxfp8_quantize(int rows, int cols, int dtype, const void* src, uint8_t* codes,
                            uint8_t* scales) {
   const int nb = cols / 32;
+  double pos[0x7F];
+  for (int c = 0; c <= 0x7E; ++c) pos[c] = oracle_e4m3_value(c);
 #pragma omp parallel for schedule(static)
   for (int r = 0; r < rows; ++r) {
     for (int b = 0; b < nb; ++b) {
@@ -512,7 +517,7 @@ void oracle_mxfp8_quantize(int rows, int cols, int dtype, const void* src, uint8
         if (s > 127) s = 127;
       }
       scales[(size_t)r * nb + b] = (uint8_t)(s + 127);
-      for (int i = 0; i < 32; ++i) codes[o + i] = e4m3_encode(ldexp(elem(src, dtype, o + i), -s));
+      for (int i = 0; i < 32; ++i) codes[o + i] = e4m3_encode(ldexp(elem(src, dtype, o + i), -s), pos);
     }
   }
 }
