@@ -95,6 +95,35 @@ __global__ __launch_bounds__(256) void k_mfma32_rand(float* out, int iters) {
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// 32x32x16 f16 with random operands (the down projection's form: fp16 h
+// times bf16 weights widened to fp16, whose three low mantissa bits are zero
+// when BF16W)
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+template <bool BF16W>
+__global__ __launch_bounds__(256) void k_mfma32_f16_rand(float* out, int iters) {
+  constexpr int CH = 4;
+  f16x8 a[CH], b[CH];
+  for (int j = 0; j < CH; ++j)
+    for (int i = 0; i < 8; ++i) {
+      const unsigned ha = hash32((blockIdx.x * 256 + threadIdx.x) * 64 + j * 8 + i);
+      const unsigned hb = hash32(ha ^ 0x9e3779b9u);
+      a[j][i] = (_Float16)(((int)(ha & 0xFFFF) - 32768) / 16384.0f);
+      float bw = ((int)(hb & 0xFFFF) - 32768) / 16384.0f;
+      if (BF16W) bw = __uint_as_float(__float_as_uint(bw) & 0xFFFF0000u);
+      b[j][i] = (_Float16)bw;
+    }
+  f32x16 c[CH];
+  for (int j = 0; j < CH; ++j)
+    for (int q = 0; q < 16; ++q) c[j][q] = 0;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[j], b[j], c[j], 0, 0, 0);
+  }
+  float s = 0;
+  for (int j = 0; j < CH; ++j) s += c[j][0] + c[j][5] + c[j][10] + c[j][15];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 // v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands and E8M0 block scales
 // (the MXFP8 GEMM's instruction), CH independent chains; RAND: random codes
 // (exponent field kept below 8, so no NaN) and random scales near 2^0, a
@@ -297,6 +326,12 @@ int main() {
     ms = time_ms([&] { hipLaunchKernelGGL(k_mfma32_rand, dim3(grid), dim3(256), 0, 0, o, iters); });
     printf("mfma bf16 32x32x16, %d wave(s)/SIMD,  4 chains, random operands: %.1f TFLOP/s\n", bpc,
            (double)grid * 4 * iters * 4 * 32768.0 / ms / 1e9);
+    ms = time_ms([&] { hipLaunchKernelGGL(k_mfma32_f16_rand<false>, dim3(grid), dim3(256), 0, 0, o, iters); });
+    printf("mfma f16 32x32x16, %d wave(s)/SIMD,  4 chains, random operands: %.1f TFLOP/s\n", bpc,
+           (double)grid * 4 * iters * 4 * 32768.0 / ms / 1e9);
+    ms = time_ms([&] { hipLaunchKernelGGL(k_mfma32_f16_rand<true>, dim3(grid), dim3(256), 0, 0, o, iters); });
+    printf("mfma f16 32x32x16, %d wave(s)/SIMD,  4 chains, random fp16 x bf16-valued operands: %.1f TFLOP/s\n",
+           bpc, (double)grid * 4 * iters * 4 * 32768.0 / ms / 1e9);
     ms = time_ms([&] { hipLaunchKernelGGL(k_mfma_fp8<false>, dim3(grid), dim3(256), 0, 0, o, iters / 2); });
     printf("mfma scaled fp8 32x32x64, %d wave(s)/SIMD,  4 chains: %.1f TFLOP/s\n", bpc,
            (double)grid * 4 * (iters / 2) * 4 * 131072.0 / ms / 1e9);
