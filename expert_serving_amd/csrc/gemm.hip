@@ -852,6 +852,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
 // rows, weight-streaming, HBM-bound) are interleaved through the grid
 // (block_tile2), so at any time some compute units stream weights while the
 // others run MFMAs, instead of the two classes running one after the other.
+// ksplit > 1 (fp32 outputs only) splits K of every tile of both classes as
+// in k_gemm_mfma: part p of a tile writes its partial sums at Out + p *
+// part_elems.
 template <int BM1, int BNB1, int BM2, int BNB2, int MODE>
 __global__ __launch_bounds__(512) void k_gemm_mfma2(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int lda,
@@ -859,19 +862,23 @@ __global__ __launch_bounds__(512) void k_gemm_mfma2(
     int K, void* __restrict__ Out, int ldo, uint32_t* __restrict__ flags, const MxArgs mx,
     const MTile* __restrict__ sched1, const int32_t* __restrict__ count1, int mslots1,
     int ntiles1, const MTile* __restrict__ sched2, const int32_t* __restrict__ count2,
-    int mslots2, int ntiles2) {
+    int mslots2, int ntiles2, int ksplit, long long part_elems) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const int m1 = min(*count1, mslots1), m2 = min(*count2, mslots2);
-  int cls, idx, mi, ni;
-  if (!block_tile2(m1 * ntiles1, m2 * ntiles2, cls, idx)) return;
+  int cls, idx, mi, nn;
+  if (!block_tile2(m1 * ntiles1 * ksplit, m2 * ntiles2 * ksplit, cls, idx)) return;
+  if (cls == 0) tile_of(idx, m1, ntiles1 * ksplit, mi, nn);
+  else tile_of(idx, m2, ntiles2 * ksplit, mi, nn);
+  const int part = nn % ksplit, ni = nn / ksplit;
+  const int stages = K / kPingRowElems;
+  const int kst0 = part * stages / ksplit, kst1 = (part + 1) * stages / ksplit;
+  if (part) Out = static_cast<float*>(Out) + part * part_elems;
   if (cls == 0) {
-    tile_of(idx, m1, ntiles1, mi, ni);
     gemm_tile<BM1, BNB1, MODE, 2, 8>(smem, A, a_rows, lda, B0, B1, strideB, N, K, Out, ldo, nullptr,
-                                     sched1, 0, flags, mx, mi, ni, 0, K / kPingRowElems);
+                                     sched1, 0, flags, mx, mi, ni, kst0, kst1 - kst0);
   } else {
-    tile_of(idx, m2, ntiles2, mi, ni);
     gemm_tile<BM2, BNB2, MODE, 2, 8>(smem, A, a_rows, lda, B0, B1, strideB, N, K, Out, ldo, nullptr,
-                                     sched2, 0, flags, mx, mi, ni, 0, K / kPingRowElems);
+                                     sched2, 0, flags, mx, mi, ni, kst0, kst1 - kst0);
   }
 }
 
@@ -1019,7 +1026,8 @@ template <int BM1, int BNB1, int BM2, int BNB2, int MODE>
 hipError_t launch_mfma2(const void* A, const int32_t* a_rows, int lda, const void* B0, const void* B1,
                         int N, int K, void* out, int ldo, uint32_t* flags, const MTile* s1,
                         const int32_t* c1, int ms1, const MTile* s2, const int32_t* c2, int ms2,
-                        hipStream_t st, const MxArgs mx = MxArgs{}) {
+                        hipStream_t st, const MxArgs mx = MxArgs{}, int ksplit = 1,
+                        long long part_elems = 0) {
   constexpr int l1 = gemm_lds_bytes(BM1, BNB1, MODE, 2, 8), l2 = gemm_lds_bytes(BM2, BNB2, MODE, 2, 8);
   constexpr int lds = l1 > l2 ? l1 : l2;
   static_assert(lds <= 160 * 1024, "LDS");
@@ -1027,12 +1035,12 @@ hipError_t launch_mfma2(const void* A, const int32_t* a_rows, int lda, const voi
   hipError_t e = raise_lds_limit<mfma2_kernel<BM1, BNB1, BM2, BNB2, MODE>>(lds, set_on);
   if (e != hipSuccess) return e;
   const int nt1 = (N + BNB1 - 1) / BNB1, nt2 = (N + BNB2 - 1) / BNB2;
-  const dim3 grid(grid_for(ms1, nt1) + grid_for(ms2, nt2));
+  const dim3 grid(grid_for(ms1, nt1 * ksplit) + grid_for(ms2, nt2 * ksplit));
   if (grid.x == 0) return hipSuccess;
   hipLaunchKernelGGL((k_gemm_mfma2<BM1, BNB1, BM2, BNB2, MODE>), grid, dim3(512), lds, st,
                      static_cast<const uint16_t*>(A), a_rows, lda, static_cast<const uint16_t*>(B0),
                      static_cast<const uint16_t*>(B1), (long long)N * K, N, K, out, ldo, flags, mx, s1, c1,
-                     ms1, nt1, s2, c2, ms2, nt2);
+                     ms1, nt1, s2, c2, ms2, nt2, ksplit, part_elems);
   return hipGetLastError();
 }
 
@@ -1173,9 +1181,10 @@ hipError_t launch_gemm_gateup2(const void* A, const int32_t* a_rows, int lda, co
 
 hipError_t launch_gemm_down2(const void* A, int lda, const void* B, int N, int K, float* Y, int ldy,
                              const MTile* sb, const int32_t* cb, int mb, const MTile* ss,
-                             const int32_t* cs, int ms, hipStream_t st) {
+                             const int32_t* cs, int ms, hipStream_t st, int ksplit,
+                             long long part_elems) {
   return launch_mfma2<256, 256, 32, 256, kDown>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sb, cb,
-                                                mb, ss, cs, ms, st);
+                                                mb, ss, cs, ms, st, MxArgs{}, ksplit, part_elems);
 }
 
 hipError_t launch_gemm_gateup_mx2(const void* A, const int32_t* a_rows, const uint8_t* sa, int sa_stride,
@@ -1192,10 +1201,11 @@ hipError_t launch_gemm_gateup_mx2(const void* A, const int32_t* a_rows, const ui
 hipError_t launch_gemm_down_mx2(const void* A, const uint8_t* hsc, int hs_stride, const void* B,
                                 const uint8_t* sb_w, int sb_stride, int N, int K, float* Y, int ldy,
                                 const MTile* sb, const int32_t* cb, int mb, const MTile* ss,
-                                const int32_t* cs, int ms, hipStream_t st) {
+                                const int32_t* cs, int ms, hipStream_t st, int ksplit,
+                                long long part_elems) {
   const MxArgs mx{hsc, sb_w, nullptr, nullptr, hs_stride, sb_stride, 0};
   return launch_mfma2<256, 256, 32, 256, kDownMX>(A, nullptr, K / 2, B, nullptr, N, K / 2, Y, ldy, nullptr, sb,
-                                                  cb, mb, ss, cs, ms, st, mx);
+                                                  cb, mb, ss, cs, ms, st, mx, ksplit, part_elems);
 }
 
 }  // namespace moe

@@ -31,7 +31,8 @@ struct WsLayout {
   size_t flags, logits, ids, gates, counts, offsets, tile_counts, row_of_slot, row_token,
       num_dropped, sched_big, sched_small, sched_count, h, y, hs, ys, xq, xsc, xscp, hsc, hssc, total;
   int n_dispatch_tiles;
-  // K-split of the layer's down projection: y holds ksplit partial sums,
+  // K-split of the layer's down projection (decode-sized layers, and layers
+  // with few 256-row tiles): y holds ksplit partial sums,
   // part p at y + p * slots * H floats (1: no split)
   int ksplit;
   int max_tiles_big, max_tiles_small;
@@ -137,7 +138,8 @@ hipError_t launch_gemm_gateup2(const void* A, const int32_t* a_rows, int lda, co
                                uint32_t* flags, hipStream_t st);
 hipError_t launch_gemm_down2(const void* A, int lda, const void* B, int N, int K, float* Y, int ldy,
                              const MTile* sb, const int32_t* cb, int mb, const MTile* ss,
-                             const int32_t* cs, int ms, hipStream_t st);
+                             const int32_t* cs, int ms, hipStream_t st, int ksplit = 1,
+                             long long part_elems = 0);
 hipError_t launch_gemm_gateup_mx2(const void* A, const int32_t* a_rows, const uint8_t* sa, int sa_stride,
                                   const void* Bg, const uint8_t* sbg, const void* Bu, const uint8_t* sbu,
                                   int sb_stride, int N, int K, void* h, uint8_t* hsc, int hs_stride,
@@ -147,7 +149,8 @@ hipError_t launch_gemm_gateup_mx2(const void* A, const int32_t* a_rows, const ui
 hipError_t launch_gemm_down_mx2(const void* A, const uint8_t* hsc, int hs_stride, const void* B,
                                 const uint8_t* sb_w, int sb_stride, int N, int K, float* Y, int ldy,
                                 const MTile* sb, const int32_t* cb, int mb, const MTile* ss,
-                                const int32_t* cs, int ms, hipStream_t st);
+                                const int32_t* cs, int ms, hipStream_t st, int ksplit = 1,
+                                long long part_elems = 0);
 
 // Row-tile height the GEMM launchers use for a dtype and a requested height.
 int gemm_tile_rows(int dtype, int bm_hint);

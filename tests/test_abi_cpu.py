@@ -89,6 +89,17 @@ def test_workspace_size_grows_with_tokens():
     assert b >= s.tokens * s.top_k * (s.inter * 2 + s.hidden * 4)
 
 
+def test_workspace_holds_down_projection_parts():
+    """A Mixtral-shaped layer of 256 or 512 tokens has at most 64 down tiles of
+    256 rows at an even load, so its down projection splits K = 14336 in
+    three and y holds three partial sums; at 1024 tokens and more, one."""
+    for T, parts in ((256, 3), (512, 3), (1024, 1), (4096, 1)):
+        c = W.CONFIGS["mixtral_prefill"].with_tokens(T)
+        slots = T * c.top_k
+        ws = abi.moe_workspace_size(abi.make_shape(c))
+        assert slots * (2 * c.inter + parts * 4 * c.hidden) <= ws < slots * (2 * c.inter + (parts + 1) * 4 * c.hidden)
+
+
 def test_null_and_misaligned_pointers_rejected_before_launch():
     L = abi.lib()
     s = base_shape(num_tokens=16)

@@ -60,6 +60,19 @@ def test_layer_interleaved_classes_with_shared_expert(fmt):
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "mxfp8"])
+def test_layer_big_tiles_k_split_three(fmt):
+    """Mixtral-shaped with 256 tokens: 32 down tiles of 256 rows (at an even
+    load) would leave most compute units idle, so the down projection splits
+    K = 14336 into three parts, which the combine adds."""
+    cfg = W.CONFIGS["mixtral_prefill"].with_tokens(256)
+    say(f"big tiles, K split in three {fmt}")
+    inp = W.make_layer_inputs(cfg, dev(), salt=11)
+    rng = np.random.default_rng(4)
+    sample = np.array(sorted(set([0, 255]) | set(rng.choice(256, 14, replace=False).tolist())), np.int32)
+    (compare_layer if fmt == "bf16" else compare_layer_mx)(cfg, inp, sample=sample)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp8"])
 def test_layer_empty_batch(fmt):
     """T = 0: the call succeeds, launches nothing and writes nothing."""
     cfg = W.CONFIGS["deepseek_v3"].with_tokens(0)
