@@ -51,6 +51,9 @@ __global__ __launch_bounds__(256) void k_tile_hist(const int32_t* __restrict__ i
 
 // One block of 1024 threads.  Turns tile_counts into per-tile bases (in place),
 // writes counts, capacity-limited offsets, the drop count and the capacity.
+// Each expert's column of tile counts is cut into P = 1024 / ep contiguous
+// ranges (ep = E rounded up to a power of two), one thread each: a first pass
+// sums the ranges, a second rewrites each range from its exclusive base.
 __global__ __launch_bounds__(1024) void k_scan_capacity(int32_t* __restrict__ tile_counts,
                                                         int n_tiles, int E, float cf,
                                                         int32_t* __restrict__ counts,
@@ -59,21 +62,44 @@ __global__ __launch_bounds__(1024) void k_scan_capacity(int32_t* __restrict__ ti
                                                         int32_t* __restrict__ cap_out) {
   __shared__ long long s_total[1024];
   __shared__ int s_scan[1024];
+  __shared__ int s_part[1024];
   const int tid = threadIdx.x;
-  int run = 0;
-  if (tid < E) {
+  int ep = 1;
+  while (ep < E) ep <<= 1;
+  const int P = 1024 / ep, e = tid % ep, g = tid / ep;
+  const int per = (n_tiles + P - 1) / P;
+  const int b_lo = min(g * per, n_tiles), b_hi = min(b_lo + per, n_tiles);
+  int part = 0;
+  if (e < E) {
     // eight tiles per round, so eight loads are in flight at once
-    for (int b0 = 0; b0 < n_tiles; b0 += 8) {
+    for (int b0 = b_lo; b0 < b_hi; b0 += 8) {
       int c[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        c[i] = b0 + i < n_tiles ? tile_counts[(size_t)(b0 + i) * E + tid] : 0;
+      for (int i = 0; i < 8; ++i) c[i] = b0 + i < b_hi ? tile_counts[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) part += c[i];
+    }
+  }
+  s_part[tid] = part;
+  __syncthreads();
+  if (e < E) {
+    int base = 0;
+    for (int q = 0; q < g; ++q) base += s_part[q * ep + e];
+    for (int b0 = b_lo; b0 < b_hi; b0 += 8) {
+      int c[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = b0 + i < b_hi ? tile_counts[(size_t)(b0 + i) * E + e] : 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        if (b0 + i < n_tiles) tile_counts[(size_t)(b0 + i) * E + tid] = run;
-        run += c[i];
+        if (b0 + i < b_hi) tile_counts[(size_t)(b0 + i) * E + e] = base;
+        base += c[i];
       }
     }
+  }
+  // expert tid's total (tid < ep: the thread of its first range)
+  int run = 0;
+  if (tid < E) {
+    for (int q = 0; q < P; ++q) run += s_part[q * ep + tid];
     counts[tid] = run;
   }
   s_total[tid] = tid < E ? run : 0;
@@ -121,27 +147,35 @@ __device__ __forceinline__ void load_wave_ids(const int32_t* __restrict__ ids, i
   }
 }
 
+// Bits that tell the ids of a chunk apart: the ids are -1 or in [0, E), so
+// ceil(log2 E) bits plus one (where -1 has a 1 and every valid id a 0).
+__device__ __forceinline__ int id_bits(int E) { return (E <= 1 ? 0 : 32 - __clz(E - 1)) + 1; }
+
 // Walks the wave's slots in order, 64 at a time: a slot's rank in its expert
 // is the wave's running base (wcnt_wave[e], advanced by the last lane holding
 // e) plus the equal experts in earlier lanes of the chunk; ranks at or beyond
-// the capacity drop the slot.
+// the capacity drop the slot.  The lanes holding a lane's id are the AND, over
+// the id's bits, of the ballot of lanes sharing that bit.
 __device__ __forceinline__ void scatter_wave(const int (&ev)[kRankChunks], int wbase,
-                                             int total_slots, int k_max, int lane,
+                                             int total_slots, int k_max, int lane, int ebits,
                                              int* __restrict__ wcnt_wave,
                                              const int* __restrict__ s_off, int cap,
                                              int32_t* __restrict__ row_of_slot,
                                              int32_t* __restrict__ row_token) {
+  const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
   for (int i = 0; i < kRankChunks; ++i) {
     if (wbase + 64 * i >= total_slots) break;
     const int s = wbase + 64 * i + lane;
     const int e = ev[i];
-    int before = 0, after = 0;
-    for (int j = 0; j < 64; ++j) {
-      const int ej = __builtin_amdgcn_readlane(e, j);
-      before += (ej == e && j < lane) ? 1 : 0;
-      after += (ej == e && j > lane) ? 1 : 0;
+    uint64_t same = ~0ull;
+    for (int b = 0; b < ebits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t on = __ballot(bit);
+      same &= bit ? on : ~on;
     }
+    const int before = __popcll(same & below);
+    const int after = __popcll(same & ~below) - 1;
     if (e >= 0) {
       const int rank = wcnt_wave[e] + before;
       const int row = rank < cap ? s_off[e] + rank : -1;
@@ -191,7 +225,7 @@ __global__ __launch_bounds__(256) void k_rank_scatter(const int32_t* __restrict_
     }
   }
   __syncthreads();
-  scatter_wave(ev, wbase, total_slots, k_max, lane, wcnt[wave], s_off, cap, row_of_slot,
+  scatter_wave(ev, wbase, total_slots, k_max, lane, id_bits(E), wcnt[wave], s_off, cap, row_of_slot,
                row_token);
 }
 
@@ -277,7 +311,7 @@ __global__ __launch_bounds__(256) void k_dispatch_single(const int32_t* __restri
   __syncthreads();
   if (tid == 0 && s_bad) atomicOr(flags, (uint32_t)MOE_FLAG_BAD_EXPERT);
   const int cap = C > INT_MAX ? INT_MAX : (int)C;
-  scatter_wave(ev, wbase, total_slots, k_max, lane, wcnt[wave], s_off, cap, row_of_slot,
+  scatter_wave(ev, wbase, total_slots, k_max, lane, id_bits(E), wcnt[wave], s_off, cap, row_of_slot,
                row_token);
 }
 

@@ -239,12 +239,14 @@ WsLayout plan_workspace(const moe_shape& s, bool mx) {
 // ---- shared launch sequences --------------------------------------------------
 namespace {
 
+// S1; also clears the device flag word (inside the skinny router's launch)
 moe_status run_router(const moe_shape& s, const void* x, const void* w_router, const float* bias,
-                      float* logits, hipStream_t st) {
+                      float* logits, uint32_t* flags, hipStream_t st) {
   if (router_skinny_supported(s)) {
-    MOE_HIP(launch_router_skinny(s, x, w_router, bias, logits, st));
+    MOE_HIP(launch_router_skinny(s, x, w_router, bias, logits, flags, st));
     return MOE_OK;
   }
+  MOE_HIP(launch_clear_flags(flags, st));
   // 128-row tiles (8-wave blocks) once there are enough of them to spread
   // over the chip; 32-row tiles for few tokens
   const int tiles128 = (s.num_tokens + 127) / 128 * ((s.num_experts + 127) / 128);
@@ -422,12 +424,13 @@ moe_status moe_route_topk(const moe_shape* shape, const void* x, const void* w_r
   if (s.num_tokens == 0) return MOE_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint32_t* flags = at<uint32_t>(ws, L.flags);
-  MOE_HIP(launch_clear_flags(flags, st));
   const float* logits = logits_in;
   if (!logits) {
     float* lo = logits_out ? logits_out : at<float>(ws, L.logits);
-    MOE_TRY(run_router(s, x, w_router, router_bias, lo, st));
+    MOE_TRY(run_router(s, x, w_router, router_bias, lo, flags, st));
     logits = lo;
+  } else {
+    MOE_HIP(launch_clear_flags(flags, st));
   }
   MOE_HIP(launch_route_topk(s, logits, k_per_token, topk_ids, topk_gates, flags, st));
   return MOE_OK;
@@ -578,9 +581,8 @@ moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* 
   int32_t* row_token = at<int32_t>(ws, L.row_token);
   float* y = at<float>(ws, L.y);
 
-  MOE_HIP(launch_clear_flags(flags, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTER, true, st));
-  MOE_TRY(run_router(s, x, w_router, router_bias, logits, st));
+  MOE_TRY(run_router(s, x, w_router, router_bias, logits, flags, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTER, false, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTE, true, st));
   MOE_HIP(launch_route_topk(s, logits, k_per_token, ids, gates, flags, st));
@@ -693,9 +695,8 @@ moe_status moe_layer_forward_mxfp8(const moe_shape* shape, const void* x, const 
   uint8_t* xq = at<uint8_t>(ws, L.xq);
   uint8_t* xsc = at<uint8_t>(ws, L.xsc);
 
-  MOE_HIP(launch_clear_flags(flags, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTER, true, st));
-  MOE_TRY(run_router(s, x, w_router, router_bias, logits, st));
+  MOE_TRY(run_router(s, x, w_router, router_bias, logits, flags, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTER, false, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTE, true, st));
   MOE_HIP(launch_route_topk(s, logits, k_per_token, ids, gates, flags, st));

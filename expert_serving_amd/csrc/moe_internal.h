@@ -66,8 +66,9 @@ hipError_t launch_logistic(const float* x, float* y, long long n, hipStream_t st
 // S1 without MFMA for bf16 layers with at most kRouterSkinnyMaxExperts experts
 constexpr int kRouterSkinnyMaxExperts = 32;
 bool router_skinny_supported(const moe_shape& s);
+// (flags, nullable: cleared to 0 by the launch)
 hipError_t launch_router_skinny(const moe_shape& s, const void* x, const void* w_router,
-                                const float* bias, float* logits, hipStream_t st);
+                                const float* bias, float* logits, uint32_t* flags, hipStream_t st);
 
 hipError_t launch_dispatch(const moe_shape& s, const int32_t* ids, int32_t* counts,
                            int32_t* offsets, int32_t* row_of_slot, int32_t* row_token,

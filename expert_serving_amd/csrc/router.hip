@@ -31,10 +31,14 @@ __device__ __forceinline__ void bf16x8_to_f32(const u32x4 v, float* f) {
 
 constexpr int ilog2(int n) { return n <= 1 ? 0 : 1 + ilog2(n / 2); }
 
+// The first kernel of a layer call also clears its device flag word (when
+// given), which saves a launch of its own.
 template <int EMAX, int TPB>
 __global__ __launch_bounds__(kRouterThreads) void k_router_skinny(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-    const float* __restrict__ bias, int T, int H, int E, float* __restrict__ logits) {
+    const float* __restrict__ bias, int T, int H, int E, float* __restrict__ logits,
+    uint32_t* __restrict__ flags) {
+  if (flags && blockIdx.x == 0 && threadIdx.x == 0) *flags = 0u;
   constexpr int N = EMAX * TPB;  // values per thread, index tok*EMAX + e
   constexpr int L = ilog2(N);
   static_assert((1 << L) == N && N <= 64, "N must be a power of two <= 64");
@@ -108,10 +112,10 @@ __global__ __launch_bounds__(kRouterThreads) void k_router_skinny(
 
 template <int EMAX, int TPB>
 hipError_t launch_skinny(const void* x, const void* wr, const float* bias, int T, int H, int E,
-                         float* logits, hipStream_t st) {
+                         float* logits, uint32_t* flags, hipStream_t st) {
   hipLaunchKernelGGL((k_router_skinny<EMAX, TPB>), dim3((T + TPB - 1) / TPB),
                      dim3(kRouterThreads), 0, st, static_cast<const uint16_t*>(x),
-                     static_cast<const uint16_t*>(wr), bias, T, H, E, logits);
+                     static_cast<const uint16_t*>(wr), bias, T, H, E, logits, flags);
   return hipGetLastError();
 }
 
@@ -122,19 +126,19 @@ bool router_skinny_supported(const moe_shape& s) {
 }
 
 hipError_t launch_router_skinny(const moe_shape& s, const void* x, const void* w_router,
-                                const float* bias, float* logits, hipStream_t st) {
+                                const float* bias, float* logits, uint32_t* flags, hipStream_t st) {
   const int T = s.num_tokens, H = s.hidden, E = s.num_experts;
   // several tokens per block share each router-row load; below 1024 tokens
   // one token per block keeps enough blocks in flight
   const bool wide = T >= 1024;
   if (E <= 8)
-    return wide ? launch_skinny<8, 4>(x, w_router, bias, T, H, E, logits, st)
-                : launch_skinny<8, 1>(x, w_router, bias, T, H, E, logits, st);
+    return wide ? launch_skinny<8, 4>(x, w_router, bias, T, H, E, logits, flags, st)
+                : launch_skinny<8, 1>(x, w_router, bias, T, H, E, logits, flags, st);
   if (E <= 16)
-    return wide ? launch_skinny<16, 4>(x, w_router, bias, T, H, E, logits, st)
-                : launch_skinny<16, 1>(x, w_router, bias, T, H, E, logits, st);
-  return wide ? launch_skinny<32, 2>(x, w_router, bias, T, H, E, logits, st)
-              : launch_skinny<32, 1>(x, w_router, bias, T, H, E, logits, st);
+    return wide ? launch_skinny<16, 4>(x, w_router, bias, T, H, E, logits, flags, st)
+                : launch_skinny<16, 1>(x, w_router, bias, T, H, E, logits, flags, st);
+  return wide ? launch_skinny<32, 2>(x, w_router, bias, T, H, E, logits, flags, st)
+              : launch_skinny<32, 1>(x, w_router, bias, T, H, E, logits, flags, st);
 }
 
 }  // namespace moe
