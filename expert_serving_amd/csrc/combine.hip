@@ -17,7 +17,9 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (b + (((b >> 16) & 1u) + 0x7FFFu)) >> 16;
 }
 
-// One block per token; thread i owns 4 consecutive columns per pass.  KM is
+// One block per token (and column slice: a small batch splits the columns
+// over gridDim.y blocks so that more compute units share the reads); thread
+// i owns 4 consecutive columns per pass.  KM is
 // a compile-time bound on k_max (2, 4, 8 or 16), so the loads of all of a
 // token's rows are issued before the first multiply-add waits on them.  y may
 // come in `parts` partial sums (a K-split down projection), each `part_stride`
@@ -38,7 +40,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, in
     s_g[threadIdx.x] = live ? gates[(size_t)t * k_max + threadIdx.x] : 0.f;
   }
   __syncthreads();
-  for (int c = threadIdx.x * 4; c < H; c += blockDim.x * 4) {
+  for (int c = (blockIdx.y * blockDim.x + threadIdx.x) * 4; c < H; c += gridDim.y * blockDim.x * 4) {
     f32x4 v[KM];
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
@@ -79,7 +81,9 @@ template <int KM>
 hipError_t launch_combine_k(const moe_shape& s, const float* y, int parts, long long part_stride,
                             const int32_t* row_of_slot, const float* gates, const float* y_shared,
                             void* out, hipStream_t st) {
-  const dim3 grid(s.num_tokens);
+  // fewer than 512 tokens: up to one block per 1024 columns of a token
+  const int ysplit = s.num_tokens < 512 ? std::max(1, s.hidden / 1024) : 1;
+  const dim3 grid(s.num_tokens, ysplit);
   if (s.out_dtype == MOE_BF16)
     hipLaunchKernelGGL((k_combine<true, KM>), grid, dim3(256), 0, st, y, parts, part_stride, row_of_slot,
                        gates, y_shared, s.hidden, s.top_k, out);

@@ -102,39 +102,82 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
   if (active && kpt) kt = kpt[t];
   const bool bad_k = active && (kt < 1 || kt > k_max);
 
-  // ---- group limit: lane g scores group g, the wave keeps the best groups ----
+  // ---- group limit: lane g ends with group g's score, the wave keeps the best groups ----
   if (G > 1) {
-    if (active) {
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (elig[i]) s_logit[wave][lane * EPL + i] = v[i];
-    }
-    __syncthreads();
     const int gs = E / G;
+    const int gl = gs / EPL;  // lanes of a group, when groups fall on whole lanes
     float gscore = 0.0f;
     int gidx = INT_MAX;
-    if (active && lane < G) {
+    if (gs % EPL == 0 && gl > 0 && (gl & (gl - 1)) == 0) {
+      // Groups on whole, aligned runs of gl lanes: every lane scores its own
+      // experts into a descending top-n list, and a butterfly over the
+      // group's lanes merges the lists (each lane inserts its partner's), so
+      // every lane of the group ends with the group's n largest scores.  The
+      // score is their sum, largest first, as below.
       float top[kMaxGroupTopn];
 #pragma unroll
       for (int q = 0; q < kMaxGroupTopn; ++q) top[q] = -1.0f;  // below any sigmoid value
-      for (int e = lane * gs; e < (lane + 1) * gs; ++e) {
-        float s = logistic_seq(s_logit[wave][e]);
-        // insert into the descending list top[0..topn)
+      auto insert = [&](float sv) {
 #pragma unroll
         for (int q = 0; q < kMaxGroupTopn; ++q) {
-          if (q < topn && s > top[q]) {
+          if (q < topn && sv > top[q]) {
             const float tmp = top[q];
-            top[q] = s;
-            s = tmp;
+            top[q] = sv;
+            sv = tmp;
           }
         }
+      };
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (lane * EPL + i < E) insert(logistic_seq(v[i]));
+      for (int m = 1; m < gl; m <<= 1) {
+        float other[kMaxGroupTopn];
+#pragma unroll
+        for (int q = 0; q < kMaxGroupTopn; ++q) other[q] = __shfl_xor(top[q], m, 64);
+#pragma unroll
+        for (int q = 0; q < kMaxGroupTopn; ++q)
+          if (q < topn) insert(other[q]);
       }
       float sum = top[0];
 #pragma unroll
       for (int q = 1; q < kMaxGroupTopn; ++q)
         if (q < topn) sum = __fadd_rn(sum, top[q]);
-      gscore = sum;
-      gidx = lane;
+      const float at_g = __shfl(sum, (lane < G ? lane : 0) * gl, 64);
+      if (active && lane < G) {
+        gscore = at_g;
+        gidx = lane;
+      }
+    } else {
+      // other group shapes: lane g scores group g serially
+      if (active) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+          if (elig[i]) s_logit[wave][lane * EPL + i] = v[i];
+      }
+      __syncthreads();
+      if (active && lane < G) {
+        float top[kMaxGroupTopn];
+#pragma unroll
+        for (int q = 0; q < kMaxGroupTopn; ++q) top[q] = -1.0f;  // below any sigmoid value
+        for (int e = lane * gs; e < (lane + 1) * gs; ++e) {
+          float s = logistic_seq(s_logit[wave][e]);
+          // insert into the descending list top[0..topn)
+#pragma unroll
+          for (int q = 0; q < kMaxGroupTopn; ++q) {
+            if (q < topn && s > top[q]) {
+              const float tmp = top[q];
+              top[q] = s;
+              s = tmp;
+            }
+          }
+        }
+        float sum = top[0];
+#pragma unroll
+        for (int q = 1; q < kMaxGroupTopn; ++q)
+          if (q < topn) sum = __fadd_rn(sum, top[q]);
+        gscore = sum;
+        gidx = lane;
+      }
     }
     uint64_t kept = 0;
     for (int q = 0; q < topk_groups; ++q) {

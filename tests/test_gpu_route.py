@@ -50,6 +50,10 @@ ROUTE_CASES = [
     ("deepseek_topn1", 2000, 256, 8, dict(score=1, scale=2.5, G=8, keep=4, topn=1, zipf=1.1, tie=0.05)),
     ("grouped_e96_g3", 777, 96, 6, dict(score=1, G=3, keep=2, topn=2, tie=0.1)),
     ("grouped_softmax_e64_g8", 500, 64, 4, dict(G=8, keep=3, topn=2)),
+    # groups on 16 lanes, top-4 group scores (butterfly merge of 4-long lists)
+    ("grouped_e128_g4_topn4", 600, 128, 8, dict(score=1, G=4, keep=2, topn=4, tie=0.1)),
+    # 12 experts per group (not a power-of-two run of lanes): groups scored serially
+    ("grouped_e48_g4_serial", 300, 48, 4, dict(score=1, G=4, keep=2, topn=3, tie=0.1)),
     ("sigmoid_norenorm", 400, 32, 4, dict(score=1, renorm=0)),
     ("qwen_per_token_k", 16384, 128, 8, dict(kpt=(2, 4, 6, 8), zipf=1.2)),
     ("per_token_k_invalid", 999, 16, 8, dict(kpt=(1, 3, 8), bad_k=True)),
