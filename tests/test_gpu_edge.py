@@ -72,6 +72,21 @@ def test_layer_big_tiles_k_split_three(fmt):
     (compare_layer if fmt == "bf16" else compare_layer_mx)(cfg, inp, sample=sample)
 
 
+def test_layer_large_batch_sampled():
+    """32 times the Mixtral-shaped prefill batch: 131072 tokens, 262144 routed
+    rows (h 7.5 GB and y 4.3 GB of workspace).  Routing, counts and
+    permutation are compared on every token (near ties allowed as in
+    test_gpu_layer.py), outputs on a sample: the index arithmetic far past
+    the benchmark's sizes."""
+    cfg = W.CONFIGS["mixtral_prefill"].with_tokens(131072)
+    say(f"large batch: T={cfg.tokens}")
+    inp = W.make_layer_inputs(cfg, dev(), salt=5)
+    rng = np.random.default_rng(6)
+    sample = np.array(sorted(set([0, cfg.tokens - 1]) | set(rng.choice(cfg.tokens, 10, replace=False).tolist())),
+                      np.int32)
+    compare_layer(cfg, inp, sample=sample)
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "mxfp8"])
 def test_layer_empty_batch(fmt):
     """T = 0: the call succeeds, launches nothing and writes nothing."""
