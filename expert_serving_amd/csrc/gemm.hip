@@ -386,10 +386,10 @@ __device__ __forceinline__ void gemm_tile(
     // clamped per chunk and their offsets differ from one chunk to the next
     // only by a uniform term.
     constexpr int RW = kPingRowElems;
-    // 32-row tiles (small experts): each weight row is read by one or two row
-    // tiles only, so its loads are non-temporal and do not displace the L2
-    // lines that the big tiles of an interleaved launch reuse
-    constexpr bool STREAM_W = BM <= 32;
+    // 32- and 64-row tiles (small experts): each weight row is read by one or
+    // two row tiles only, so its loads are non-temporal and do not displace
+    // the L2 lines that the big tiles of an interleaved launch reuse
+    constexpr bool STREAM_W = BM <= 64;
     constexpr int PSTAGE = ROWS * RW;   // elements of one stage
     constexpr int NI = ROWS / (8 * NW); // 8-row loads per wave per stage
     constexpr int NH0 = (NI + 1) / 2;   // ... in the first half stage
@@ -1078,6 +1078,7 @@ hipError_t launch_gemm_gateup(int dtype, int bm, const void* A, const int32_t* a
   // 32-row tiles (small experts, decode): 8-wave blocks of 32 x 256, which
   // stream the weights faster than 4-wave 32 x 128 blocks (measured 0.29 vs
   // 0.35 ms on the Mixtral-shaped decode layer)
+  if (bm != 32) return hipErrorInvalidValue;
   return launch_mfma<32, 256, kGateUp, 2, 8>(A, a_rows, lda, Bg, Bu, N, K, h, ldh, nullptr, sched, count,
                                              mslots, static_rows, flags, st);
 }
@@ -1105,6 +1106,7 @@ hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int 
     if (bm == 128)
       return launch_mfma<128, 128, kDown, 2, 8>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
                                           mslots, static_rows, nullptr, st);
+    if (bm != 32) return hipErrorInvalidValue;
     // few blocks (decode-sized layers): a deeper ring keeps more weight bytes
     // in flight per compute unit
     if ((long long)mslots * ((N + 127) / 128) <= 1024)
@@ -1117,6 +1119,7 @@ hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int 
   if (bm == 128)
     return launch_mfma<128, 128, kPlain, 2, 8>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, bias, sched, count,
                                          mslots, static_rows, nullptr, st);
+  if (bm != 32) return hipErrorInvalidValue;
   return launch_mfma<32, 128, kPlain, 4, 4>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, bias, sched, count,
                                       mslots, static_rows, nullptr, st);
 }
@@ -1142,6 +1145,7 @@ hipError_t launch_gemm_gateup_mx(int bm, const void* A, const int32_t* a_rows, c
   if (bm == 128)
     return launch_mfma<128, 128, kGateUpMX, 2, 8>(A, a_rows, K2, Bg, Bu, N, K2, h, N, nullptr, sched,
                                                   count, mslots, static_rows, flags, st, mx);
+  if (bm != 32) return hipErrorInvalidValue;
   return launch_mfma<32, 256, kGateUpMX, 2, 8>(A, a_rows, K2, Bg, Bu, N, K2, h, N, nullptr, sched,
                                                count, mslots, static_rows, flags, st, mx);
 }
@@ -1164,6 +1168,7 @@ hipError_t launch_gemm_down_mx(int bm, const void* A, const uint8_t* hsc, int hs
   if (bm == 128)
     return launch_mfma<128, 128, kDownMX, 2, 8>(A, nullptr, K2, B, nullptr, N, K2, Y, ldy, nullptr,
                                                 sched, count, mslots, static_rows, nullptr, st, mx);
+  if (bm != 32) return hipErrorInvalidValue;
   return launch_mfma<32, 256, kDownMX, 2, 8>(A, nullptr, K2, B, nullptr, N, K2, Y, ldy, nullptr,
                                              sched, count, mslots, static_rows, nullptr, st, mx, ksplit,
                                              part_elems);
@@ -1175,7 +1180,7 @@ hipError_t launch_gemm_gateup2(const void* A, const int32_t* a_rows, int lda, co
                                const void* Bu, int N, int K, void* h, int ldh, const MTile* sb,
                                const int32_t* cb, int mb, const MTile* ss, const int32_t* cs, int ms,
                                uint32_t* flags, hipStream_t st) {
-  return launch_mfma2<256, 128, 32, 256, kGateUp>(A, a_rows, lda, Bg, Bu, N, K, h, ldh, flags, sb, cb, mb,
+  return launch_mfma2<256, 128, kMergedSmallRows, 256, kGateUp>(A, a_rows, lda, Bg, Bu, N, K, h, ldh, flags, sb, cb, mb,
                                                   ss, cs, ms, st);
 }
 
@@ -1183,7 +1188,7 @@ hipError_t launch_gemm_down2(const void* A, int lda, const void* B, int N, int K
                              const MTile* sb, const int32_t* cb, int mb, const MTile* ss,
                              const int32_t* cs, int ms, hipStream_t st, int ksplit,
                              long long part_elems) {
-  return launch_mfma2<256, 256, 32, 256, kDown>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sb, cb,
+  return launch_mfma2<256, 256, kMergedSmallRows, 256, kDown>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sb, cb,
                                                 mb, ss, cs, ms, st, MxArgs{}, ksplit, part_elems);
 }
 
@@ -1194,7 +1199,7 @@ hipError_t launch_gemm_gateup_mx2(const void* A, const int32_t* a_rows, const ui
                                   const int32_t* cs, int ms, uint32_t* flags, hipStream_t st,
                                   bool sa_direct) {
   const MxArgs mx{sa, sbg, sbu, hsc, sa_stride, sb_stride, hs_stride, sa_direct ? 1 : 0};
-  return launch_mfma2<256, 128, 32, 256, kGateUpMX>(A, a_rows, K / 2, Bg, Bu, N, K / 2, h, N, flags, sb, cb,
+  return launch_mfma2<256, 128, kMergedSmallRows, 256, kGateUpMX>(A, a_rows, K / 2, Bg, Bu, N, K / 2, h, N, flags, sb, cb,
                                                     mb, ss, cs, ms, st, mx);
 }
 
@@ -1204,7 +1209,7 @@ hipError_t launch_gemm_down_mx2(const void* A, const uint8_t* hsc, int hs_stride
                                 const int32_t* cs, int ms, hipStream_t st, int ksplit,
                                 long long part_elems) {
   const MxArgs mx{hsc, sb_w, nullptr, nullptr, hs_stride, sb_stride, 0};
-  return launch_mfma2<256, 256, 32, 256, kDownMX>(A, nullptr, K / 2, B, nullptr, N, K / 2, Y, ldy, nullptr, sb,
+  return launch_mfma2<256, 256, kMergedSmallRows, 256, kDownMX>(A, nullptr, K / 2, B, nullptr, N, K / 2, Y, ldy, nullptr, sb,
                                                   cb, mb, ss, cs, ms, st, mx, ksplit, part_elems);
 }
 

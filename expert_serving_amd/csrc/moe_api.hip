@@ -139,11 +139,12 @@ GemmPlan choose_gemm_plan(const moe_shape& s) {
     p.split_rows = 0x7fffffff;   // every expert small: weight-streaming 32-row tiles
   } else {
     // both classes, in one interleaved launch for bf16 and MXFP8 layers:
-    // experts with >= 128 kept rows on 256-row tiles, the rest on 32-row
+    // experts with >= 128 kept rows on 256-row tiles, the rest on 64-row
     // tiles.  Even with a large average load, skew and capacity drops leave
     // many experts with a few rows (Qwen3-shaped layer: 87 of 120), and an
     // empty small class costs only a few idle blocks.
     p.split_rows = 128;
+    p.bm_small = kMergedSmallRows;
     // a big expert's last rows, when few, ride on small tiles: a 256-row
     // tile costs its full height in MFMA time, while the small tiles stream
     // the expert's weights beside the big tiles of the same launch
@@ -274,7 +275,7 @@ moe_status run_ffn(const moe_shape& s, const void* x_perm, const int32_t* a_rows
   // skewed loads (both tile classes) on bf16: one interleaved launch per
   // projection, so small experts stream weights while big ones run MFMAs
   const bool merged = gp.has_big() && gp.has_small() && s.act_dtype == MOE_BF16 &&
-                      gp.bm_big == 256 && gp.bm_small == 32;
+                      gp.bm_big == 256 && gp.bm_small == kMergedSmallRows;
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATE_UP, true, st));
   if (merged) {
     MOE_HIP(launch_gemm_gateup2(x_perm, a_rows, H, w_gate, w_up, I, H, h, I, sb, cnt, L.max_tiles_big, ss,
@@ -324,7 +325,7 @@ moe_status run_ffn_mx(const moe_shape& s, const void* xq, const int32_t* a_rows,
   void* h = at<void>(ws, L.h);
   uint8_t* hsc = at<uint8_t>(ws, L.hsc);
   const auto gsc = w.gate_scales, usc = w.up_scales, dsc = w.down_scales;
-  const bool merged = gp.has_big() && gp.has_small() && gp.bm_big == 256 && gp.bm_small == 32;
+  const bool merged = gp.has_big() && gp.has_small() && gp.bm_big == 256 && gp.bm_small == kMergedSmallRows;
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATE_UP, true, st));
   if (merged) {
     MOE_HIP(launch_gemm_gateup_mx2(xq, a_rows, xsc, xs_stride, w.gate, gsc, w.up, usc, E * I, I, H, h, hsc,

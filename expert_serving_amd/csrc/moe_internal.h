@@ -38,6 +38,13 @@ struct WsLayout {
   int max_tiles_big, max_tiles_small;
 };
 
+// Row-tile height of the weight-streaming class in the interleaved
+// (big + small) launches: an expert of up to 64 rows (or a big expert's tail
+// of up to 64 rows) streams each weight tile once, where 32-row tiles would
+// stream it once per 32 rows; the extra MFMA work stays hidden behind the
+// weight stream.
+constexpr int kMergedSmallRows = 64;
+
 // GEMM tile configuration chosen by the host for a shape.
 // Row tiling of the grouped GEMMs.  Experts with at least split_rows kept rows
 // are cut into tiles of bm_big rows, the others into tiles of bm_small rows;

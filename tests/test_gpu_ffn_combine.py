@@ -29,7 +29,7 @@ FFN_CASES = [
     # the smallest K (one 64-wide stage), a big and an empty expert
     ("bf16_min_k", W.DT_BF16, 2, 64, 64, [300, 0], 600),
     # no small expert: the remainders past the last full 256-row tile (44, 1
-    # and 40 rows) ride on 32-row tiles beside the big ones
+    # and 40 rows) ride on 64-row tiles beside the big ones
     ("bf16_big_tiles_with_tails", W.DT_BF16, 3, 512, 384, [300, 257, 552], 4096),
     ("f32_tiny", W.DT_F32, 3, 128, 96, [40, 0, 33], 73),
     ("f32_ragged", W.DT_F32, 5, 64, 36, [1, 31, 32, 33, 70], 167),
