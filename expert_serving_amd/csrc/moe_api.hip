@@ -124,6 +124,8 @@ T* at(void* ws, size_t off) {
 constexpr int kTailRows = MOE_TAIL_ROWS;
 // compute units of one MI355X (8 XCDs x 32)
 constexpr int kComputeUnits = 256;
+// K-split parts of the down projection for a batch of a token or two
+constexpr int kFewKsplit = 8;
 
 GemmPlan choose_gemm_plan(const moe_shape& s) {
   GemmPlan p;
@@ -181,12 +183,23 @@ WsLayout plan_workspace(const moe_shape& s, bool mx) {
     const int bnb = mx ? 256 : 128;  // column tile of the 32-row down kernels
     const long long blocks = (long long)w.max_tiles_small * ((H + bnb - 1) / bnb);
     w.ksplit = 1;
+    // at most min(T*k, E) experts hold rows, one 32-row tile each when T*k is small
+    const long long few = std::max<long long>(std::min<long long>((long long)slots, (long long)E),
+                                              ((long long)slots + 31) / 32);
+    const long long few_blocks = std::min<long long>(w.max_tiles_small, few) * ((H + bnb - 1) / bnb);
     if (!gp.has_big() && gp.has_small() && s.act_dtype == MOE_BF16 && blocks > 0 && blocks < 512) {
-      // two parts measured best for both formats on the Mixtral-shaped decode
-      // layer (four or eight: the combine's extra reads cost more than the
-      // down projection gains)
-      const int want = (int)std::min<long long>(2, 1024 / blocks);
       const int stages = (int)(I / 64);
+      int want;
+      if ((long long)slots < E && few_blocks <= kComputeUnits / 2) {
+        // fewer routed slots than experts (a few tokens): up to eight parts,
+        // so most compute units stream a slice of the few weight matrices;
+        // the combine's extra reads are a few KB per part
+        want = (int)std::min<long long>(kFewKsplit, (4LL * kComputeUnits + few_blocks - 1) / few_blocks);
+      } else {
+        // two parts measured best for both formats on the Mixtral-shaped
+        // decode layer (four or eight: slower)
+        want = (int)std::min<long long>(2, 1024 / blocks);
+      }
       w.ksplit = std::max(1, std::min(want, stages / 4));
     } else if (gp.has_big() && gp.bm_big == 256 && s.act_dtype == MOE_BF16) {
       // Few 256-row down tiles with a long K (at an even load, at most a
