@@ -190,7 +190,7 @@ WsLayout plan_workspace(const moe_shape& s, bool mx) {
     if (!gp.has_big() && gp.has_small() && s.act_dtype == MOE_BF16 && blocks > 0 && blocks < 512) {
       const int stages = (int)(I / 64);
       int want;
-      if ((long long)slots < E && few_blocks <= kComputeUnits / 2) {
+      if ((long long)slots < E && few_blocks > 0 && few_blocks <= kComputeUnits / 2) {
         // fewer routed slots than experts (a few tokens): up to eight parts,
         // so most compute units stream a slice of the few weight matrices;
         // the combine's extra reads are a few KB per part
