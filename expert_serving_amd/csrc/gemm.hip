@@ -125,7 +125,12 @@ __device__ __forceinline__ bool block_tile2(int real0, int real1, int& cls, int&
 //   kDownMX: A = MXFP8 h rows, B0 = MXFP8 down weights; out y (fp32)
 // The MX modes take every row length, K and lda in 16-bit units (two E4M3
 // codes), so the byte layout of their tiles is that of the bf16 modes.
-enum GemmMode { kGateUp = 0, kDown = 1, kPlain = 2, kGateUpMX = 3, kDownMX = 4 };
+//   kGateUpPart: as kGateUp on one K range of a split K, without SwiGLU: the
+//            fp32 partial sums A.B0^T at Out and A.B1^T at Out + up_off
+enum GemmMode { kGateUp = 0, kDown = 1, kPlain = 2, kGateUpMX = 3, kDownMX = 4, kGateUpPart = 5 };
+
+// modes that multiply by both the gate and the up weights
+constexpr bool gemm_dual(int MODE) { return MODE == kGateUp || MODE == kGateUpMX || MODE == kGateUpPart; }
 
 // Scales of the MXFP8 operands (E8M0 bytes, four blocks of a 128-column group
 // per 32-bit word, words group-major: the word of group g of row r is
@@ -201,7 +206,7 @@ constexpr int kPingRowElems = 64;  // K elements per LDS row of 8-wave blocks (1
 // Rows of one stage, padded to whole wavefront loads per wave: 16 rows per
 // load for 4-wave blocks, 8 rows per load for 8-wave blocks.
 constexpr int gemm_stage_rows(int BM, int BNB, int MODE, int NW) {
-  return (BM + BNB * ((MODE == kGateUp || MODE == kGateUpMX) ? 2 : 1) + (NW == 8 ? 8 : 16) * NW - 1) /
+  return (BM + BNB * (gemm_dual(MODE) ? 2 : 1) + (NW == 8 ? 8 : 16) * NW - 1) /
          ((NW == 8 ? 8 : 16) * NW) * ((NW == 8 ? 8 : 16) * NW);
 }
 // Bytes of LDS one block of k_gemm_mfma<BM, BNB, MODE, NS, NW> uses: NS
@@ -247,8 +252,8 @@ __device__ __forceinline__ void gemm_tile(
     int lda, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, long long strideB,
     int N, int K, void* __restrict__ Out, int ldo, const float* __restrict__ bias,
     const MTile* __restrict__ sched, int static_rows, uint32_t* __restrict__ flags, const MxArgs mx,
-    int mi, int ni, int kst0, int kstn) {
-  constexpr bool DUAL = MODE == kGateUp || MODE == kGateUpMX;
+    int mi, int ni, int kst0, int kstn, long long up_off = 0) {
+  constexpr bool DUAL = gemm_dual(MODE);
   constexpr bool MX = MODE == kGateUpMX || MODE == kDownMX;
   constexpr int WAVES_M = BM >= 64 ? 2 : 1, WAVES_N = NW / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BNB / WAVES_N;
@@ -796,10 +801,11 @@ __device__ __forceinline__ void gemm_tile(
       for (int qi = 0; qi < 4; ++qi) {
         const int n = n0 + wn * WN + a * 32 + 8 * qi + 4 * fk;
         const size_t o = (size_t)(row0 + m) * ldo + n;
-        {
-          const f32x16 acc = acc0[a][b];
+#pragma unroll
+        for (int ob = 0; ob < (MODE == kGateUpPart ? 2 : 1); ++ob) {
+          const f32x16 acc = ob ? acc1[DUAL ? a : 0][DUAL ? b : 0] : acc0[a][b];
           f32x4 v = {acc[4 * qi], acc[4 * qi + 1], acc[4 * qi + 2], acc[4 * qi + 3]};
-          float* dst = static_cast<float*>(Out) + o;
+          float* dst = static_cast<float*>(Out) + o + (ob ? up_off : 0);
           if (n + 3 < N && (ldo & 3) == 0) {
             if (bias) {
               v[0] += bias[n];
@@ -844,7 +850,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
   const int kst0 = part * stages / ksplit, kst1 = (part + 1) * stages / ksplit;
   if (part) Out = static_cast<float*>(Out) + part * part_elems;
   gemm_tile<BM, BNB, MODE, NS, NW>(smem, A, a_rows, lda, B0, B1, strideB, N, K, Out, ldo, bias, sched,
-                                   static_rows, flags, mx, mi, ni, kst0, kst1 - kst0);
+                                   static_rows, flags, mx, mi, ni, kst0, kst1 - kst0,
+                                   MODE == kGateUpPart ? ksplit * part_elems : 0);
 }
 
 // Both row-tile classes of a skewed layer in one launch (8-wave blocks): the
@@ -954,6 +961,39 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A,
       Out[(size_t)(row0 + m) * ldo + n] = v;
     }
   }
+}
+
+// SwiGLU over split-K partial sums: h[r][c] = silu(sum_p G_p[r][c]) *
+// (sum_p U_p[r][c]) for rows r below *rows_dev (or static_rows), where part
+// p of the gate sums is at parts + p * part_elems and part p of the up sums at
+// parts + (nparts + p) * part_elems, rows of ld floats.  Parts are added in
+// order; h is fp16 as in the fused epilogue (values outside its range set
+// MOE_FLAG_H_RANGE).  One block per row and 1024 columns, four per thread.
+__global__ __launch_bounds__(256) void k_swiglu_parts(const float* __restrict__ parts, int nparts,
+                                                      long long part_elems, int N, int ld,
+                                                      const int32_t* __restrict__ rows_dev,
+                                                      int static_rows, uint16_t* __restrict__ h,
+                                                      int ldh, uint32_t* __restrict__ flags) {
+  const int r = blockIdx.x;
+  const int rows = rows_dev ? *rows_dev : static_rows;
+  if (r >= rows) return;
+  const int c = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
+  if (c >= N) return;
+  const float* g = parts + (size_t)r * ld + c;
+  const float* u = g + (size_t)nparts * part_elems;
+  f32x4 gs = *reinterpret_cast<const f32x4*>(g);
+  f32x4 us = *reinterpret_cast<const f32x4*>(u);
+  for (int p = 1; p < nparts; ++p) {
+    gs += *reinterpret_cast<const f32x4*>(g + p * part_elems);
+    us += *reinterpret_cast<const f32x4*>(u + p * part_elems);
+  }
+  const float h0 = silu_mul(gs[0], us[0]), h1 = silu_mul(gs[1], us[1]);
+  const float h2 = silu_mul(gs[2], us[2]), h3 = silu_mul(gs[3], us[3]);
+  const bool ovf = !(fabsf(h0) <= 65504.f && fabsf(h1) <= 65504.f && fabsf(h2) <= 65504.f &&
+                     fabsf(h3) <= 65504.f);
+  *reinterpret_cast<uint2*>(h + (size_t)r * ldh + c) =
+      uint2{f32_to_f16_bits(h0) | (f32_to_f16_bits(h1) << 16), f32_to_f16_bits(h2) | (f32_to_f16_bits(h3) << 16)};
+  if (ovf && flags) atomicOr(flags, (uint32_t)MOE_FLAG_H_RANGE);
 }
 
 // Worst-case grid: every row-tile slot real; a multiple of 8 (one slot per XCD).
@@ -1081,6 +1121,27 @@ hipError_t launch_gemm_gateup(int dtype, int bm, const void* A, const int32_t* a
   if (bm != 32) return hipErrorInvalidValue;
   return launch_mfma<32, 256, kGateUp, 2, 8>(A, a_rows, lda, Bg, Bu, N, K, h, ldh, nullptr, sched, count,
                                              mslots, static_rows, flags, st);
+}
+
+hipError_t launch_gemm_gateup_parts(const void* A, const int32_t* a_rows, int lda, const void* Bg,
+                                    const void* Bu, int N, int K, float* parts, const MTile* sched,
+                                    const int32_t* count, int max_tiles, int static_rows, int ksplit,
+                                    long long part_elems, hipStream_t st) {
+  const int mslots = sched ? max_tiles : (static_rows + 31) / 32;
+  if (mslots == 0) return hipSuccess;
+  return launch_mfma<32, 256, kGateUpPart, 2, 8>(A, a_rows, lda, Bg, Bu, N, K, parts, N, nullptr, sched, count,
+                                                 mslots, static_rows, nullptr, st, MxArgs{}, ksplit, part_elems);
+}
+
+hipError_t launch_swiglu_parts(const float* parts, int nparts, long long part_elems, int N,
+                               const int32_t* rows_dev, int static_rows, int max_rows, void* h, int ldh,
+                               uint32_t* flags, hipStream_t st) {
+  if (max_rows <= 0) return hipSuccess;
+  if (N % 4) return hipErrorInvalidValue;
+  const dim3 grid(max_rows, (N + 1023) / 1024);
+  hipLaunchKernelGGL(k_swiglu_parts, grid, dim3(256), 0, st, parts, nparts, part_elems, N, N, rows_dev,
+                     static_rows, static_cast<uint16_t*>(h), ldh, flags);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int lda,

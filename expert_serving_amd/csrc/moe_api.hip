@@ -126,6 +126,9 @@ constexpr int kTailRows = MOE_TAIL_ROWS;
 constexpr int kComputeUnits = 256;
 // K-split parts of the down projection for a batch of a token or two
 constexpr int kFewKsplit = 8;
+// most K-split parts of a gate/up projection (16 keeps each part >= 4 stages
+// of 64 for H >= 4096)
+constexpr int kGateUpKsplitMax = 16;
 
 GemmPlan choose_gemm_plan(const moe_shape& s) {
   GemmPlan p;
@@ -216,6 +219,33 @@ WsLayout plan_workspace(const moe_shape& s, bool mx) {
       }
     }
   }
+  // Gate/up of a token or two (routed) and of the shared expert for a few
+  // tokens: when the weight-streaming 32 x 256 tiles would keep at most half
+  // the compute units busy, K is split into about one block per unit (each
+  // streams a slice of its weight rows) and a small kernel adds the parts and
+  // applies SwiGLU.  Measured on the DeepSeek-V3-shaped layer: one token
+  // 0.473 -> 0.289 ms, two 0.546 -> 0.359 ms (the shared expert's gate/up ran
+  // 8 blocks); Mixtral-shaped single token unchanged (0.156 -> 0.155 ms).
+  w.ks_gu = w.ks_gus = 1;
+  if (!mx && s.act_dtype == MOE_BF16) {
+    const int stages = (int)(H / 64);
+    if (!gp.has_big() && gp.has_small()) {
+      const long long few = std::max<long long>(std::min<long long>((long long)slots, (long long)E),
+                                                ((long long)slots + 31) / 32);
+      const long long blocks = std::min<long long>(w.max_tiles_small, few) * (long long)((I + 255) / 256);
+      if (blocks > 0 && blocks <= kComputeUnits / 2)
+        w.ks_gu = std::max(1, std::min<int>((int)std::min<long long>(kGateUpKsplitMax,
+                                                                     (kComputeUnits + blocks - 1) / blocks),
+                                            stages / 4));
+    }
+    if (Is > 0 && T < 128) {
+      const long long blocks = (long long)((T + 31) / 32) * (long long)((Is + 255) / 256);
+      if (blocks > 0 && blocks <= kComputeUnits / 2)
+        w.ks_gus = std::max(1, std::min<int>((int)std::min<long long>(kGateUpKsplitMax,
+                                                                      (kComputeUnits + blocks - 1) / blocks),
+                                             stages / 4));
+    }
+  }
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at_ = o;
@@ -239,6 +269,8 @@ WsLayout plan_workspace(const moe_shape& s, bool mx) {
   w.y = take((size_t)w.ksplit * slots * H * 4);
   w.hs = take(T * Is * eb);
   w.ys = take(Is ? T * H * 4 : 0);
+  w.gu_parts = take(std::max(w.ks_gu > 1 ? 2 * (size_t)w.ks_gu * slots * I * 4 : 0,
+                             w.ks_gus > 1 ? 2 * (size_t)w.ks_gus * T * Is * 4 : 0));
   if (mx) {
     w.xq = take(T * H);
     w.xsc = take(T * H / 32);
@@ -297,9 +329,17 @@ moe_status run_ffn(const moe_shape& s, const void* x_perm, const int32_t* a_rows
     if (gp.has_big())
       MOE_HIP(launch_gemm_gateup(s.act_dtype, gp.bm_big, x_perm, a_rows, H, w_gate, w_up, I, H, h,
                                  I, sb, cnt, L.max_tiles_big, 0, flags, st));
-    if (gp.has_small())
+    if (gp.has_small() && L.ks_gu > 1) {
+      float* parts = at<float>(ws, L.gu_parts);
+      const long long pe = (long long)s.num_tokens * s.top_k * I;
+      MOE_HIP(launch_gemm_gateup_parts(x_perm, a_rows, H, w_gate, w_up, I, H, parts, ss, cnt + 1,
+                                       L.max_tiles_small, 0, L.ks_gu, pe, st));
+      MOE_HIP(launch_swiglu_parts(parts, L.ks_gu, pe, I, offsets + E, 0, s.num_tokens * s.top_k, h, I,
+                                  flags, st));
+    } else if (gp.has_small()) {
       MOE_HIP(launch_gemm_gateup(s.act_dtype, gp.bm_small, x_perm, a_rows, H, w_gate, w_up, I, H,
                                  h, I, ss, cnt + 1, L.max_tiles_small, 0, flags, st));
+    }
   }
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATE_UP, false, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_DOWN, true, st));
@@ -394,8 +434,17 @@ moe_status run_shared(const moe_shape& s, const void* x, const void* wsg, const 
   const int bm = s.act_dtype == MOE_F32 ? 32 : (T >= 2048 ? 256 : (T >= 128 ? 128 : 32));
   void* hs = at<void>(ws, L.hs);
   float* ys = at<float>(ws, L.ys);
-  MOE_HIP(launch_gemm_gateup(s.act_dtype, bm, x, nullptr, H, wsg, wsu, Is, H, hs, Is, nullptr,
-                             nullptr, 0, T, at<uint32_t>(ws, L.flags), st));
+  if (L.ks_gus > 1 && bm == 32) {
+    float* parts = at<float>(ws, L.gu_parts);
+    const long long pe = (long long)T * Is;
+    MOE_HIP(launch_gemm_gateup_parts(x, nullptr, H, wsg, wsu, Is, H, parts, nullptr, nullptr, 0, T,
+                                     L.ks_gus, pe, st));
+    MOE_HIP(launch_swiglu_parts(parts, L.ks_gus, pe, Is, nullptr, T, T, hs, Is, at<uint32_t>(ws, L.flags),
+                                st));
+  } else {
+    MOE_HIP(launch_gemm_gateup(s.act_dtype, bm, x, nullptr, H, wsg, wsu, Is, H, hs, Is, nullptr,
+                               nullptr, 0, T, at<uint32_t>(ws, L.flags), st));
+  }
   MOE_HIP(launch_gemm_plain(s.act_dtype, bm, true, hs, Is, wsd, H, Is, nullptr, ys, H, nullptr,
                             nullptr, 0, T, st));
   return MOE_OK;

@@ -29,12 +29,17 @@ struct MTile {
 // h and hs then hold one-byte codes.
 struct WsLayout {
   size_t flags, logits, ids, gates, counts, offsets, tile_counts, row_of_slot, row_token,
-      num_dropped, sched_big, sched_small, sched_count, h, y, hs, ys, xq, xsc, xscp, hsc, hssc, total;
+      num_dropped, sched_big, sched_small, sched_count, h, y, hs, ys, xq, xsc, xscp, hsc, hssc, gu_parts,
+      total;
   int n_dispatch_tiles;
   // K-split of the layer's down projection (decode-sized layers, and layers
   // with few 256-row tiles): y holds ksplit partial sums,
   // part p at y + p * slots * H floats (1: no split)
   int ksplit;
+  // K-split of the gate/up projection for a token or two (routed experts,
+  // ks_gu) and of the shared expert's for a few tokens (ks_gus): fp32
+  // partial gate and up sums in gu_parts, reduced by launch_swiglu_parts
+  int ks_gu, ks_gus;
   int max_tiles_big, max_tiles_small;
 };
 
@@ -106,6 +111,18 @@ hipError_t launch_gemm_gateup(int dtype, int bm, const void* A, const int32_t* a
                               const void* Bg, const void* Bu, int N, int K, void* h, int ldh,
                               const MTile* sched, const int32_t* count, int max_tiles,
                               int static_rows, uint32_t* flags, hipStream_t st);
+// gate/up on 32-row tiles with K split into ksplit ranges, no SwiGLU: range
+// p's fp32 sums A.Bg^T at parts + p * part_elems and A.Bu^T at parts +
+// (ksplit + p) * part_elems (rows of N floats); bf16 layers.
+hipError_t launch_gemm_gateup_parts(const void* A, const int32_t* a_rows, int lda, const void* Bg,
+                                    const void* Bu, int N, int K, float* parts, const MTile* sched,
+                                    const int32_t* count, int max_tiles, int static_rows, int ksplit,
+                                    long long part_elems, hipStream_t st);
+// h[r] = fp16(silu(sum of gate parts) * sum of up parts) for r below *rows_dev
+// (or static_rows when rows_dev is null); max_rows bounds the grid.
+hipError_t launch_swiglu_parts(const float* parts, int nparts, long long part_elems, int N,
+                               const int32_t* rows_dev, int static_rows, int max_rows, void* h, int ldh,
+                               uint32_t* flags, hipStream_t st);
 // plain: Y[r][n] = A[r].B[e][n] (+ bias[n]), fp32 out.  a_is_h: A is the
 // fp16 h of a bf16 layer (down projection), B is converted to fp16 on load.
 // ksplit > 1 (32-row down tiles): K in ksplit ranges of whole 64-element

@@ -31,6 +31,9 @@ FFN_CASES = [
     # no small expert: the remainders past the last full 256-row tile (44, 1
     # and 40 rows) ride on 64-row tiles beside the big ones
     ("bf16_big_tiles_with_tails", W.DT_BF16, 3, 512, 384, [300, 257, 552], 4096),
+    # a token or two: two one-row experts, so the gate/up K is split into
+    # parts that a separate kernel adds before SwiGLU
+    ("bf16_two_rows_split_gate_up", W.DT_BF16, 8, 1024, 512, [1, 0, 0, 0, 0, 0, 1, 0], 2),
     ("f32_tiny", W.DT_F32, 3, 128, 96, [40, 0, 33], 73),
     ("f32_ragged", W.DT_F32, 5, 64, 36, [1, 31, 32, 33, 70], 167),
 ]
