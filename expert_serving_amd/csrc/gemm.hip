@@ -127,10 +127,19 @@ __device__ __forceinline__ bool block_tile2(int real0, int real1, int& cls, int&
 // codes), so the byte layout of their tiles is that of the bf16 modes.
 //   kGateUpPart: as kGateUp on one K range of a split K, without SwiGLU: the
 //            fp32 partial sums A.B0^T at Out and A.B1^T at Out + up_off
-enum GemmMode { kGateUp = 0, kDown = 1, kPlain = 2, kGateUpMX = 3, kDownMX = 4, kGateUpPart = 5 };
+//   kGateUpMXPart: the same on MXFP8 operands
+enum GemmMode {
+  kGateUp = 0, kDown = 1, kPlain = 2, kGateUpMX = 3, kDownMX = 4, kGateUpPart = 5, kGateUpMXPart = 6
+};
 
 // modes that multiply by both the gate and the up weights
-constexpr bool gemm_dual(int MODE) { return MODE == kGateUp || MODE == kGateUpMX || MODE == kGateUpPart; }
+constexpr bool gemm_dual(int MODE) {
+  return MODE == kGateUp || MODE == kGateUpMX || MODE == kGateUpPart || MODE == kGateUpMXPart;
+}
+// modes on MXFP8 operands
+constexpr bool gemm_mx(int MODE) { return MODE == kGateUpMX || MODE == kDownMX || MODE == kGateUpMXPart; }
+// split-K gate/up modes (fp32 partial gate and up sums out)
+constexpr bool gemm_part(int MODE) { return MODE == kGateUpPart || MODE == kGateUpMXPart; }
 
 // Scales of the MXFP8 operands (E8M0 bytes, four blocks of a 128-column group
 // per 32-bit word, words group-major: the word of group g of row r is
@@ -214,7 +223,7 @@ constexpr int gemm_stage_rows(int BM, int BNB, int MODE, int NW) {
 // and stage.
 constexpr int gemm_lds_bytes(int BM, int BNB, int MODE, int NS, int NW) {
   return NS * gemm_stage_rows(BM, BNB, MODE, NW) *
-         ((NW == 8 ? kPingRowElems : kSK) * 2 + ((MODE == kGateUpMX || MODE == kDownMX) ? 4 : 0));
+         ((NW == 8 ? kPingRowElems : kSK) * 2 + (gemm_mx(MODE) ? 4 : 0));
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -254,7 +263,7 @@ __device__ __forceinline__ void gemm_tile(
     const MTile* __restrict__ sched, int static_rows, uint32_t* __restrict__ flags, const MxArgs mx,
     int mi, int ni, int kst0, int kstn, long long up_off = 0) {
   constexpr bool DUAL = gemm_dual(MODE);
-  constexpr bool MX = MODE == kGateUpMX || MODE == kDownMX;
+  constexpr bool MX = gemm_mx(MODE);
   constexpr int WAVES_M = BM >= 64 ? 2 : 1, WAVES_N = NW / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BNB / WAVES_N;
   constexpr int FM = WM / 32, FN = WN / 32;
@@ -802,7 +811,7 @@ __device__ __forceinline__ void gemm_tile(
         const int n = n0 + wn * WN + a * 32 + 8 * qi + 4 * fk;
         const size_t o = (size_t)(row0 + m) * ldo + n;
 #pragma unroll
-        for (int ob = 0; ob < (MODE == kGateUpPart ? 2 : 1); ++ob) {
+        for (int ob = 0; ob < (gemm_part(MODE) ? 2 : 1); ++ob) {
           const f32x16 acc = ob ? acc1[DUAL ? a : 0][DUAL ? b : 0] : acc0[a][b];
           f32x4 v = {acc[4 * qi], acc[4 * qi + 1], acc[4 * qi + 2], acc[4 * qi + 3]};
           float* dst = static_cast<float*>(Out) + o + (ob ? up_off : 0);
@@ -851,7 +860,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
   if (part) Out = static_cast<float*>(Out) + part * part_elems;
   gemm_tile<BM, BNB, MODE, NS, NW>(smem, A, a_rows, lda, B0, B1, strideB, N, K, Out, ldo, bias, sched,
                                    static_rows, flags, mx, mi, ni, kst0, kst1 - kst0,
-                                   MODE == kGateUpPart ? ksplit * part_elems : 0);
+                                   gemm_part(MODE) ? ksplit * part_elems : 0);
 }
 
 // Both row-tile classes of a skewed layer in one launch (8-wave blocks): the
@@ -994,6 +1003,53 @@ __global__ __launch_bounds__(256) void k_swiglu_parts(const float* __restrict__ 
   *reinterpret_cast<uint2*>(h + (size_t)r * ldh + c) =
       uint2{f32_to_f16_bits(h0) | (f32_to_f16_bits(h1) << 16), f32_to_f16_bits(h2) | (f32_to_f16_bits(h3) << 16)};
   if (ovf && flags) atomicOr(flags, (uint32_t)MOE_FLAG_H_RANGE);
+}
+
+// The MXFP8 form: h re-quantised per 32-column block as in the fused
+// epilogue (block maximum -> E8M0 scale, E4M3 codes), codes [rows][N] and
+// scale bytes at ((c / 128) * hs_stride + r) * 4 + (c / 32) % 4.  Thread t of
+// a block owns columns 4t .. 4t+3, so a 32-column block is 8 consecutive
+// lanes and its maximum takes three shuffles.
+__global__ __launch_bounds__(256) void k_swiglu_parts_mx(const float* __restrict__ parts, int nparts,
+                                                         long long part_elems, int N,
+                                                         const int32_t* __restrict__ rows_dev,
+                                                         int static_rows, uint8_t* __restrict__ h,
+                                                         uint8_t* __restrict__ hsc, int hs_stride,
+                                                         uint32_t* __restrict__ flags) {
+  const int r = blockIdx.x;
+  const int rows = rows_dev ? *rows_dev : static_rows;
+  if (r >= rows) return;  // uniform over the block
+  const int c = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
+  const bool live = c < N;  // N is a multiple of 128: whole 8-lane groups are live or not
+  f32x4 gs = {0.f, 0.f, 0.f, 0.f}, us = {0.f, 0.f, 0.f, 0.f};
+  if (live) {
+    const float* g = parts + (size_t)r * N + c;
+    const float* u = g + (size_t)nparts * part_elems;
+    gs = *reinterpret_cast<const f32x4*>(g);
+    us = *reinterpret_cast<const f32x4*>(u);
+    for (int p = 1; p < nparts; ++p) {
+      gs += *reinterpret_cast<const f32x4*>(g + p * part_elems);
+      us += *reinterpret_cast<const f32x4*>(u + p * part_elems);
+    }
+  }
+  float hv[4];
+  float amax = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    hv[q] = silu_mul(gs[q], us[q]);
+    amax = fmaxf(amax, fabsf(hv[q]));
+  }
+#pragma unroll
+  for (int off = 1; off < 8; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  if (!live) return;
+  const uint32_t sb = mx_scale_byte(amax);
+  const int sh = 127 - (int)sb;
+  *reinterpret_cast<uint32_t*>(h + (size_t)r * N + c) =
+      e4m3x4(ldexpf(hv[0], sh), ldexpf(hv[1], sh), ldexpf(hv[2], sh), ldexpf(hv[3], sh));
+  if ((threadIdx.x & 7) == 0) {
+    hsc[((size_t)(c >> 7) * hs_stride + r) * 4 + ((c >> 5) & 3)] = (uint8_t)sb;
+    if (!(amax <= 3.402823466e38f) && flags) atomicOr(flags, (uint32_t)MOE_FLAG_H_RANGE);
+  }
 }
 
 // Worst-case grid: every row-tile slot real; a multiple of 8 (one slot per XCD).
@@ -1209,6 +1265,32 @@ hipError_t launch_gemm_gateup_mx(int bm, const void* A, const int32_t* a_rows, c
   if (bm != 32) return hipErrorInvalidValue;
   return launch_mfma<32, 256, kGateUpMX, 2, 8>(A, a_rows, K2, Bg, Bu, N, K2, h, N, nullptr, sched,
                                                count, mslots, static_rows, flags, st, mx);
+}
+
+hipError_t launch_gemm_gateup_mx_parts(const void* A, const int32_t* a_rows, const uint8_t* sa,
+                                       int sa_stride, const void* Bg, const uint8_t* sbg, const void* Bu,
+                                       const uint8_t* sbu, int sb_stride, int N, int K, float* parts,
+                                       const MTile* sched, const int32_t* count, int max_tiles,
+                                       int static_rows, int ksplit, long long part_elems, hipStream_t st,
+                                       bool sa_direct) {
+  const int mslots = sched ? max_tiles : (static_rows + 31) / 32;
+  if (mslots == 0) return hipSuccess;
+  const MxArgs mx{sa, sbg, sbu, nullptr, sa_stride, sb_stride, 0, sa_direct ? 1 : 0};
+  const int K2 = K / 2;  // 16-bit units
+  return launch_mfma<32, 256, kGateUpMXPart, 2, 8>(A, a_rows, K2, Bg, Bu, N, K2, parts, N, nullptr, sched,
+                                                   count, mslots, static_rows, nullptr, st, mx, ksplit,
+                                                   part_elems);
+}
+
+hipError_t launch_swiglu_parts_mx(const float* parts, int nparts, long long part_elems, int N,
+                                  const int32_t* rows_dev, int static_rows, int max_rows, void* h,
+                                  uint8_t* hsc, int hs_stride, uint32_t* flags, hipStream_t st) {
+  if (max_rows <= 0) return hipSuccess;
+  if (N % 128) return hipErrorInvalidValue;
+  const dim3 grid(max_rows, (N + 1023) / 1024);
+  hipLaunchKernelGGL(k_swiglu_parts_mx, grid, dim3(256), 0, st, parts, nparts, part_elems, N, rows_dev,
+                     static_rows, static_cast<uint8_t*>(h), hsc, hs_stride, flags);
+  return hipGetLastError();
 }
 
 // MXFP8 down projection: A = MXFP8 h rows [rows][K] (scales hsc, stride

@@ -227,8 +227,8 @@ WsLayout plan_workspace(const moe_shape& s, bool mx) {
   // 0.473 -> 0.289 ms, two 0.546 -> 0.359 ms (the shared expert's gate/up ran
   // 8 blocks); Mixtral-shaped single token unchanged (0.156 -> 0.155 ms).
   w.ks_gu = w.ks_gus = 1;
-  if (!mx && s.act_dtype == MOE_BF16) {
-    const int stages = (int)(H / 64);
+  if (s.act_dtype == MOE_BF16) {
+    const int stages = (int)(H / (mx ? 128 : 64));  // K stages (128 codes, or 64 bf16 elements)
     if (!gp.has_big() && gp.has_small()) {
       const long long few = std::max<long long>(std::min<long long>((long long)slots, (long long)E),
                                                 ((long long)slots + 31) / 32);
@@ -389,10 +389,19 @@ moe_status run_ffn_mx(const moe_shape& s, const void* xq, const int32_t* a_rows,
       MOE_HIP(launch_gemm_gateup_mx(gp.bm_big, xq, a_rows, xsc, xs_stride, w.gate, gsc, w.up, usc,
                                     E * I, I, H, h, hsc, slots, sb, cnt, L.max_tiles_big, 0, flags,
                                     st, sa_direct));
-    if (gp.has_small())
+    if (gp.has_small() && L.ks_gu > 1) {
+      float* parts = at<float>(ws, L.gu_parts);
+      const long long pe = (long long)slots * I;
+      MOE_HIP(launch_gemm_gateup_mx_parts(xq, a_rows, xsc, xs_stride, w.gate, gsc, w.up, usc, E * I, I, H,
+                                          parts, ss, cnt + 1, L.max_tiles_small, 0, L.ks_gu, pe, st,
+                                          sa_direct));
+      MOE_HIP(launch_swiglu_parts_mx(parts, L.ks_gu, pe, I, offsets + E, 0, slots, h, hsc, slots, flags,
+                                     st));
+    } else if (gp.has_small()) {
       MOE_HIP(launch_gemm_gateup_mx(gp.bm_small, xq, a_rows, xsc, xs_stride, w.gate, gsc, w.up, usc,
                                     E * I, I, H, h, hsc, slots, ss, cnt + 1, L.max_tiles_small, 0,
                                     flags, st, sa_direct));
+    }
   }
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATE_UP, false, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_DOWN, true, st));
@@ -420,9 +429,18 @@ moe_status run_shared_mx(const moe_shape& s, const void* xq, const uint8_t* xsc,
   void* hs = at<void>(ws, L.hs);
   uint8_t* hssc = at<uint8_t>(ws, L.hssc);
   float* ys = at<float>(ws, L.ys);
-  MOE_HIP(launch_gemm_gateup_mx(bm, xq, nullptr, xsc, T, w.gate, w.gate_scales, w.up, w.up_scales,
-                                Is, Is, H, hs, hssc, T, nullptr, nullptr, 0, T,
-                                at<uint32_t>(ws, L.flags), st));
+  if (L.ks_gus > 1 && bm == 32) {
+    float* parts = at<float>(ws, L.gu_parts);
+    const long long pe = (long long)T * Is;
+    MOE_HIP(launch_gemm_gateup_mx_parts(xq, nullptr, xsc, T, w.gate, w.gate_scales, w.up, w.up_scales, Is,
+                                        Is, H, parts, nullptr, nullptr, 0, T, L.ks_gus, pe, st, false));
+    MOE_HIP(launch_swiglu_parts_mx(parts, L.ks_gus, pe, Is, nullptr, T, T, hs, hssc, T,
+                                   at<uint32_t>(ws, L.flags), st));
+  } else {
+    MOE_HIP(launch_gemm_gateup_mx(bm, xq, nullptr, xsc, T, w.gate, w.gate_scales, w.up, w.up_scales,
+                                  Is, Is, H, hs, hssc, T, nullptr, nullptr, 0, T,
+                                  at<uint32_t>(ws, L.flags), st));
+  }
   MOE_HIP(launch_gemm_down_mx(bm, hs, hssc, T, w.down, w.down_scales, H, H, Is, ys, H, nullptr,
                               nullptr, 0, T, st));
   return MOE_OK;

@@ -123,6 +123,17 @@ hipError_t launch_gemm_gateup_parts(const void* A, const int32_t* a_rows, int ld
 hipError_t launch_swiglu_parts(const float* parts, int nparts, long long part_elems, int N,
                                const int32_t* rows_dev, int static_rows, int max_rows, void* h, int ldh,
                                uint32_t* flags, hipStream_t st);
+// The same two steps on MXFP8 operands; the reduction re-quantises h (codes
+// [rows][N], scales as the MXFP8 gate/up epilogue writes them).
+hipError_t launch_gemm_gateup_mx_parts(const void* A, const int32_t* a_rows, const uint8_t* sa,
+                                       int sa_stride, const void* Bg, const uint8_t* sbg, const void* Bu,
+                                       const uint8_t* sbu, int sb_stride, int N, int K, float* parts,
+                                       const MTile* sched, const int32_t* count, int max_tiles,
+                                       int static_rows, int ksplit, long long part_elems, hipStream_t st,
+                                       bool sa_direct);
+hipError_t launch_swiglu_parts_mx(const float* parts, int nparts, long long part_elems, int N,
+                                  const int32_t* rows_dev, int static_rows, int max_rows, void* h,
+                                  uint8_t* hsc, int hs_stride, uint32_t* flags, hipStream_t st);
 // plain: Y[r][n] = A[r].B[e][n] (+ bias[n]), fp32 out.  a_is_h: A is the
 // fp16 h of a bf16 layer (down projection), B is converted to fp16 on load.
 // ksplit > 1 (32-row down tiles): K in ksplit ranges of whole 64-element

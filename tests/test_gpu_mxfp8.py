@@ -109,8 +109,11 @@ FFN_CASES = [
     ("both_classes_skew", 16, 256, 256, None, 1600),
     ("one_stage_k", 2, 128, 128, [300, 45], 600),
     ("odd_k_stages", 2, 384, 640, [520, 260], 1024),
-    # remainders past the last full 256-row tile on 32-row tiles (no small expert)
+    # remainders past the last full 256-row tile on 64-row tiles (no small expert)
     ("big_tiles_with_tails", 3, 512, 384, [300, 257, 552], 4096),
+    # two one-row experts: gate/up K split into parts, h re-quantised by the
+    # reduction kernel
+    ("two_rows_split_gate_up", 8, 1024, 512, [1, 0, 0, 0, 0, 0, 1, 0], 2),
 ]
 
 
