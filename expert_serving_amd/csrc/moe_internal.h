@@ -77,6 +77,9 @@ hipError_t launch_logistic(const float* x, float* y, long long n, hipStream_t st
 
 // S1 without MFMA for bf16 layers with at most kRouterSkinnyMaxExperts experts
 constexpr int kRouterSkinnyMaxExperts = 32;
+// ... and for more experts up to this many tokens (slices of 8 experts; the
+// 128-row MFMA router keeps only a few compute units busy below it)
+constexpr int kRouterSlicedMaxTokens = 1024;
 bool router_skinny_supported(const moe_shape& s);
 // (flags, nullable: cleared to 0 by the launch)
 hipError_t launch_router_skinny(const moe_shape& s, const void* x, const void* w_router,

@@ -4,7 +4,10 @@
 // scores every expert for every token).
 //
 // With E <= 32 the product is a handful of dot products per token, far too
-// narrow for 128-wide MFMA tiles, and the cost is reading x once.  One block
+// narrow for 128-wide MFMA tiles, and the cost is reading x once.  Wider
+// routers with few tokens (a 128-row MFMA tile per block would leave most
+// compute units idle) take the same kernel over slices of EMAX experts
+// (blockIdx.y), re-reading the few x rows from L2.  One block
 // of 256 threads takes TPB tokens; thread i reads the 16-byte chunks
 // i, i+256, ... of each token row (coalesced) and the same chunks of every
 // router row (L2-resident), and keeps TPB*EMAX fp32 partial sums.  The
@@ -47,6 +50,7 @@ __global__ __launch_bounds__(kRouterThreads) void k_router_skinny(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * TPB;
+  const int e0 = blockIdx.y * EMAX;  // first expert of this block's slice
   const int chunks = H >> 3;
 
   float v[N];
@@ -63,7 +67,7 @@ __global__ __launch_bounds__(kRouterThreads) void k_router_skinny(
       xr[q] = *reinterpret_cast<const u32x4*>(x + (size_t)min(t0 + q, T - 1) * H + c * 8);
 #pragma unroll
     for (int e = 0; e < EMAX; ++e)
-      wrr[e] = *reinterpret_cast<const u32x4*>(wr + (size_t)min(e, E - 1) * H + c * 8);
+      wrr[e] = *reinterpret_cast<const u32x4*>(wr + (size_t)min(e0 + e, E - 1) * H + c * 8);
     float xf[TPB][8];
 #pragma unroll
     for (int q = 0; q < TPB; ++q) bf16x8_to_f32(xr[q], xf[q]);
@@ -106,14 +110,14 @@ __global__ __launch_bounds__(kRouterThreads) void k_router_skinny(
 #pragma unroll
     for (int w = 1; w < NWAVES; ++w) sum += s_part[w][tid];
     const int q = tid / EMAX, e = tid % EMAX, t = t0 + q;
-    if (t < T && e < E) logits[(size_t)t * E + e] = sum + (bias ? bias[e] : 0.f);
+    if (t < T && e0 + e < E) logits[(size_t)t * E + e0 + e] = sum + (bias ? bias[e0 + e] : 0.f);
   }
 }
 
 template <int EMAX, int TPB>
 hipError_t launch_skinny(const void* x, const void* wr, const float* bias, int T, int H, int E,
                          float* logits, uint32_t* flags, hipStream_t st) {
-  hipLaunchKernelGGL((k_router_skinny<EMAX, TPB>), dim3((T + TPB - 1) / TPB),
+  hipLaunchKernelGGL((k_router_skinny<EMAX, TPB>), dim3((T + TPB - 1) / TPB, (E + EMAX - 1) / EMAX),
                      dim3(kRouterThreads), 0, st, static_cast<const uint16_t*>(x),
                      static_cast<const uint16_t*>(wr), bias, T, H, E, logits, flags);
   return hipGetLastError();
@@ -122,7 +126,8 @@ hipError_t launch_skinny(const void* x, const void* wr, const float* bias, int T
 }  // namespace
 
 bool router_skinny_supported(const moe_shape& s) {
-  return s.act_dtype == MOE_BF16 && s.num_experts <= kRouterSkinnyMaxExperts;
+  return s.act_dtype == MOE_BF16 &&
+         (s.num_experts <= kRouterSkinnyMaxExperts || s.num_tokens <= kRouterSlicedMaxTokens);
 }
 
 hipError_t launch_router_skinny(const moe_shape& s, const void* x, const void* w_router,
@@ -131,6 +136,11 @@ hipError_t launch_router_skinny(const moe_shape& s, const void* x, const void* w
   // several tokens per block share each router-row load; below 1024 tokens
   // one token per block keeps enough blocks in flight
   const bool wide = T >= 1024;
+  // wide routers, few tokens: 8-expert slices, one token per block below 64
+  // tokens, four above
+  if (E > kRouterSkinnyMaxExperts)
+    return T >= 64 ? launch_skinny<8, 4>(x, w_router, bias, T, H, E, logits, flags, st)
+                   : launch_skinny<8, 1>(x, w_router, bias, T, H, E, logits, flags, st);
   if (E <= 8)
     return wide ? launch_skinny<8, 4>(x, w_router, bias, T, H, E, logits, flags, st)
                 : launch_skinny<8, 1>(x, w_router, bias, T, H, E, logits, flags, st);

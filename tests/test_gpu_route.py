@@ -107,6 +107,13 @@ ROUTER_CASES = [
     (W.DT_BF16, 2050, 1024, 32, True),
     (W.DT_BF16, 3, 64, 24, True),
     (W.DT_BF16, 257, 2048, 33, True),
+    # E > 32 with at most 1024 tokens: vector-ALU router over 8-expert
+    # slices (one token per block below 64 tokens, four from 64)
+    (W.DT_BF16, 1, 7168, 256, True),
+    (W.DT_BF16, 63, 2048, 128, False),
+    (W.DT_BF16, 256, 7168, 256, True),
+    (W.DT_BF16, 100, 1024, 37, True),
+    (W.DT_BF16, 5, 512, 512, True),
     (W.DT_BF16, 777, 7168, 256, True),
     (W.DT_BF16, 4096, 2048, 128, True),
     (W.DT_BF16, 16384, 1024, 256, True),      # 128-row tiles (8-wave MFMA kernel)
