@@ -1224,6 +1224,13 @@ hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int 
       return launch_mfma<128, 128, kDown, 2, 8>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
                                           mslots, static_rows, nullptr, st);
     if (bm != 32) return hipErrorInvalidValue;
+    // K of at least 2048: 8-wave 32 x 256 blocks, as for gate/up (Mixtral-
+    // shaped decode down 0.181 -> 0.139 ms); shorter K keeps the 4-wave
+    // 32 x 128 blocks (I = 768: 0.025 against 0.030 ms)
+    if (K >= kDown8MinK)
+      return launch_mfma<32, 256, kDown, 2, 8>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sched,
+                                               count, mslots, static_rows, nullptr, st, MxArgs{}, ksplit,
+                                               part_elems);
     // few blocks (decode-sized layers): a deeper ring keeps more weight bytes
     // in flight per compute unit
     if ((long long)mslots * ((N + 127) / 128) <= 1024)

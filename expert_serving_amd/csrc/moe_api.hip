@@ -183,7 +183,7 @@ WsLayout plan_workspace(const moe_shape& s, bool mx) {
   // into partial sums that the combine adds gives every unit weight rows to
   // stream.
   {
-    const int bnb = mx ? 256 : 128;  // column tile of the 32-row down kernels
+    const int bnb = (mx || I >= (size_t)kDown8MinK) ? 256 : 128;  // column tile of the 32-row down kernels
     const long long blocks = (long long)w.max_tiles_small * ((H + bnb - 1) / bnb);
     w.ksplit = 1;
     // at most min(T*k, E) experts hold rows, one 32-row tile each when T*k is small

@@ -43,6 +43,10 @@ struct WsLayout {
   int max_tiles_big, max_tiles_small;
 };
 
+// K from which the 32-row bf16 down tiles are 8-wave 32 x 256 blocks (else
+// 4-wave 32 x 128)
+constexpr int kDown8MinK = 2048;
+
 // Row-tile height of the weight-streaming class in the interleaved
 // (big + small) launches: an expert of up to 64 rows (or a big expert's tail
 // of up to 64 rows) streams each weight tile once, where 32-row tiles would
