@@ -47,6 +47,18 @@ def test_layer_single_token(name, fmt):
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("name,T", [("mixtral_prefill", 3), ("deepseek_v3", 5), ("deepseek_v3", 2)])
+def test_layer_few_tokens_split_gate_up(name, T, fmt):
+    """A few tokens: the gate/up projection's K is split into parts (their
+    weight-streaming tiles fill one or two rounds of the compute units
+    poorly), the parts added by the SwiGLU reduction kernel."""
+    cfg = W.CONFIGS[name].with_tokens(T)
+    say(f"few tokens {name} T={T} {fmt}")
+    inp = W.make_layer_inputs(cfg, dev(), salt=12)
+    (compare_layer if fmt == "bf16" else compare_layer_mx)(cfg, inp)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp8"])
 def test_layer_interleaved_classes_with_shared_expert(fmt):
     """DeepSeek-V3-shaped with 2048 tokens (average load 64 rows, the
     smallest batch that interleaves both tile classes in one launch per
