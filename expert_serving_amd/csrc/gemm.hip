@@ -857,7 +857,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
   const int part = nn % ksplit, ni = nn / ksplit;
   const int stages = K / kPingRowElems;
   const int kst0 = part * stages / ksplit, kst1 = (part + 1) * stages / ksplit;
-  if (part) Out = static_cast<float*>(Out) + part * part_elems;
+  if (part) {
+    Out = static_cast<float*>(Out) + part * part_elems;
+    bias = nullptr;  // added once, by part 0
+  }
   gemm_tile<BM, BNB, MODE, NS, NW>(smem, A, a_rows, lda, B0, B1, strideB, N, K, Out, ldo, bias, sched,
                                    static_rows, flags, mx, mi, ni, kst0, kst1 - kst0,
                                    gemm_part(MODE) ? ksplit * part_elems : 0);
@@ -1206,6 +1209,7 @@ hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int 
                              int static_rows, hipStream_t st, int ksplit, long long part_elems) {
   const long long strideB = (long long)N * K;
   if (dtype == MOE_F32) {
+    if (ksplit > 1) return hipErrorInvalidValue;  // the fp32 kernel does not split K
     const int mslots = sched ? max_tiles : (static_rows + 31) / 32;
     const int ntiles = (N + 31) / 32;
     if (mslots == 0) return hipSuccess;
@@ -1219,10 +1223,10 @@ hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int 
   if (a_is_h) {
     if (bm == 256)
       return launch_mfma<256, 256, kDown, 2, 8>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
-                                          mslots, static_rows, nullptr, st);
+                                          mslots, static_rows, nullptr, st, MxArgs{}, ksplit, part_elems);
     if (bm == 128)
       return launch_mfma<128, 128, kDown, 2, 8>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
-                                          mslots, static_rows, nullptr, st);
+                                          mslots, static_rows, nullptr, st, MxArgs{}, ksplit, part_elems);
     if (bm != 32) return hipErrorInvalidValue;
     // K of at least 2048: 8-wave 32 x 256 blocks, as for gate/up (Mixtral-
     // shaped decode down 0.181 -> 0.139 ms); shorter K keeps the 4-wave
@@ -1242,10 +1246,10 @@ hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int 
   }
   if (bm == 128)
     return launch_mfma<128, 128, kPlain, 2, 8>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, bias, sched, count,
-                                         mslots, static_rows, nullptr, st);
+                                         mslots, static_rows, nullptr, st, MxArgs{}, ksplit, part_elems);
   if (bm != 32) return hipErrorInvalidValue;
   return launch_mfma<32, 128, kPlain, 4, 4>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, bias, sched, count,
-                                      mslots, static_rows, nullptr, st);
+                                      mslots, static_rows, nullptr, st, MxArgs{}, ksplit, part_elems);
 }
 
 // MXFP8 gate/up + SwiGLU: A = E4M3 token rows (K = H codes each, gathered

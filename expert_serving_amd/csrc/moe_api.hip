@@ -130,6 +130,15 @@ constexpr int kFewKsplit = 8;
 // of 64 for H >= 4096)
 constexpr int kGateUpKsplitMax = 16;
 
+int router_parts(const moe_shape& s) {
+  if (s.act_dtype != MOE_BF16 || router_skinny_supported(s)) return 1;
+  // the MFMA router's tiles (as run_router picks them); K in 64-wide stages
+  const int tiles128 = (s.num_tokens + 127) / 128 * ((s.num_experts + 127) / 128);
+  const int bm = tiles128 >= 64 ? 128 : 32;
+  const long long blocks = (long long)((s.num_tokens + bm - 1) / bm) * ((s.num_experts + 127) / 128);
+  return (blocks < kComputeUnits && s.hidden / 64 >= 16) ? 2 : 1;
+}
+
 GemmPlan choose_gemm_plan(const moe_shape& s) {
   GemmPlan p;
   const long long slots = (long long)s.num_tokens * s.top_k;
@@ -273,6 +282,7 @@ WsLayout plan_workspace(const moe_shape& s, bool mx) {
   };
   w.flags = take(256);
   w.logits = take(T * E * 4);
+  w.logits_parts = take(router_parts(s) > 1 ? (size_t)router_parts(s) * T * E * 4 : 0);
   w.ids = take(slots * 4);
   w.gates = take(slots * 4);
   w.counts = take(E * 4);
@@ -304,14 +314,27 @@ WsLayout plan_workspace(const moe_shape& s, bool mx) {
 // ---- shared launch sequences --------------------------------------------------
 namespace {
 
-// S1; also clears the device flag word (inside the skinny router's launch)
+// S1; also clears the device flag word (inside the skinny router's launch).
+// With router_parts(s) = 2 the logits come as two partial sums at
+// parts_buf (T*E floats apart), which the route kernel adds and stores at
+// `logits`; `parts` reports which.
 moe_status run_router(const moe_shape& s, const void* x, const void* w_router, const float* bias,
-                      float* logits, uint32_t* flags, hipStream_t st) {
+                      float* logits, uint32_t* flags, hipStream_t st, float* parts_buf, int& parts) {
+  parts = 1;
   if (router_skinny_supported(s)) {
     MOE_HIP(launch_router_skinny(s, x, w_router, bias, logits, flags, st));
     return MOE_OK;
   }
   MOE_HIP(launch_clear_flags(flags, st));
+  if (router_parts(s) > 1) {
+    parts = router_parts(s);
+    const int tiles128 = (s.num_tokens + 127) / 128 * ((s.num_experts + 127) / 128);
+    const int bm = tiles128 >= 64 ? 128 : 32;
+    MOE_HIP(launch_gemm_plain(s.act_dtype, bm, false, x, s.hidden, w_router, s.num_experts, s.hidden,
+                              bias, parts_buf, s.num_experts, nullptr, nullptr, 0, s.num_tokens, st, parts,
+                              (long long)s.num_tokens * s.num_experts));
+    return MOE_OK;
+  }
   // 128-row tiles (8-wave blocks) once there are enough of them to spread
   // over the chip; 32-row tiles for few tokens
   const int tiles128 = (s.num_tokens + 127) / 128 * ((s.num_experts + 127) / 128);
@@ -525,14 +548,19 @@ moe_status moe_route_topk(const moe_shape* shape, const void* x, const void* w_r
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint32_t* flags = at<uint32_t>(ws, L.flags);
   const float* logits = logits_in;
+  int rparts = 1;
+  float* sum_out = nullptr;
   if (!logits) {
     float* lo = logits_out ? logits_out : at<float>(ws, L.logits);
-    MOE_TRY(run_router(s, x, w_router, router_bias, lo, flags, st));
-    logits = lo;
+    float* pb = at<float>(ws, L.logits_parts);
+    MOE_TRY(run_router(s, x, w_router, router_bias, lo, flags, st, pb, rparts));
+    logits = rparts > 1 ? pb : lo;
+    sum_out = rparts > 1 ? lo : nullptr;
   } else {
     MOE_HIP(launch_clear_flags(flags, st));
   }
-  MOE_HIP(launch_route_topk(s, logits, k_per_token, topk_ids, topk_gates, flags, st));
+  MOE_HIP(launch_route_topk(s, logits, k_per_token, topk_ids, topk_gates, flags, st, rparts,
+                            (long long)s.num_tokens * s.num_experts, sum_out));
   return MOE_OK;
 }
 
@@ -682,10 +710,13 @@ moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* 
   float* y = at<float>(ws, L.y);
 
   MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTER, true, st));
-  MOE_TRY(run_router(s, x, w_router, router_bias, logits, flags, st));
+  int rparts = 1;
+  float* lparts = at<float>(ws, L.logits_parts);
+  MOE_TRY(run_router(s, x, w_router, router_bias, logits, flags, st, lparts, rparts));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTER, false, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTE, true, st));
-  MOE_HIP(launch_route_topk(s, logits, k_per_token, ids, gates, flags, st));
+  MOE_HIP(launch_route_topk(s, rparts > 1 ? lparts : logits, k_per_token, ids, gates, flags, st, rparts,
+                            (long long)s.num_tokens * s.num_experts, rparts > 1 ? logits : nullptr));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTE, false, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_DISPATCH, true, st));
   MOE_HIP(launch_dispatch(s, ids, counts, offsets, ros, row_token, nd,
@@ -796,10 +827,13 @@ moe_status moe_layer_forward_mxfp8(const moe_shape* shape, const void* x, const 
   uint8_t* xsc = at<uint8_t>(ws, L.xsc);
 
   MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTER, true, st));
-  MOE_TRY(run_router(s, x, w_router, router_bias, logits, flags, st));
+  int rparts = 1;
+  float* lparts = at<float>(ws, L.logits_parts);
+  MOE_TRY(run_router(s, x, w_router, router_bias, logits, flags, st, lparts, rparts));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTER, false, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTE, true, st));
-  MOE_HIP(launch_route_topk(s, logits, k_per_token, ids, gates, flags, st));
+  MOE_HIP(launch_route_topk(s, rparts > 1 ? lparts : logits, k_per_token, ids, gates, flags, st, rparts,
+                            (long long)s.num_tokens * s.num_experts, rparts > 1 ? logits : nullptr));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTE, false, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_DISPATCH, true, st));
   MOE_HIP(launch_dispatch(s, ids, counts, offsets, ros, row_token, nd,

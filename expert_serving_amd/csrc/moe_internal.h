@@ -28,7 +28,7 @@ struct MTile {
 // of h (hsc, stride T*top_k) and of the shared expert's h (hssc, stride T);
 // h and hs then hold one-byte codes.
 struct WsLayout {
-  size_t flags, logits, ids, gates, counts, offsets, tile_counts, row_of_slot, row_token,
+  size_t flags, logits, logits_parts, ids, gates, counts, offsets, tile_counts, row_of_slot, row_token,
       num_dropped, sched_big, sched_small, sched_count, h, y, hs, ys, xq, xsc, xscp, hsc, hssc, gu_parts,
       total;
   int n_dispatch_tiles;
@@ -54,6 +54,11 @@ constexpr int kDown8MinK = 2048;
 // weight stream.
 constexpr int kMergedSmallRows = 64;
 
+// K-split parts of the MFMA router (E > 32 and more tokens than the sliced
+// vector router takes): 2 when its tiles keep fewer blocks than compute
+// units busy, else 1
+int router_parts(const moe_shape& s);
+
 // GEMM tile configuration chosen by the host for a shape.
 // Row tiling of the grouped GEMMs.  Experts with at least split_rows kept rows
 // are cut into tiles of bm_big rows, the others into tiles of bm_small rows;
@@ -74,8 +79,11 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // ---- launchers (each returns the launch status) ----------------------------
 hipError_t launch_clear_flags(uint32_t* flags, hipStream_t st);
 
+// logits may come in `parts` partial sums part_stride floats apart (a
+// K-split router); their sums are then also written to sum_out (nullable)
 hipError_t launch_route_topk(const moe_shape& s, const float* logits, const int32_t* k_per_token,
-                             int32_t* ids, float* gates, uint32_t* flags, hipStream_t st);
+                             int32_t* ids, float* gates, uint32_t* flags, hipStream_t st, int parts = 1,
+                             long long part_stride = 0, float* sum_out = nullptr);
 
 hipError_t launch_logistic(const float* x, float* y, long long n, hipStream_t st);
 

@@ -81,7 +81,8 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
                                                     int topk_groups, int topn,
                                                     int32_t* __restrict__ ids,
                                                     float* __restrict__ gates,
-                                                    uint32_t* __restrict__ flags) {
+                                                    uint32_t* __restrict__ flags, int parts,
+                                                    long long part_stride, float* __restrict__ sum_out) {
   __shared__ float s_logit[kWavesPerBlock][kMaxExperts];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -90,12 +91,18 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
 
   float v[EPL];
   bool elig[EPL];
+  // logits in `parts` partial sums (a K-split router) are added in part
+  // order, and the sums stored at sum_out
   const float* lt = logits + (size_t)(active ? t : 0) * E;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane * EPL + i;
     elig[i] = active && e < E;
     v[i] = elig[i] ? lt[e] : 0.0f;
+    if (parts > 1 && elig[i]) {
+      for (int p = 1; p < parts; ++p) v[i] += lt[p * part_stride + e];
+      if (sum_out) sum_out[(size_t)t * E + e] = v[i];
+    }
   }
 
   int kt = k_max;
@@ -290,7 +297,8 @@ hipError_t launch_logistic(const float* x, float* y, long long n, hipStream_t st
 }
 
 hipError_t launch_route_topk(const moe_shape& s, const float* logits, const int32_t* k_per_token,
-                             int32_t* ids, float* gates, uint32_t* flags, hipStream_t st) {
+                             int32_t* ids, float* gates, uint32_t* flags, hipStream_t st, int parts,
+                             long long part_stride, float* sum_out) {
   const int T = s.num_tokens, E = s.num_experts;
   const int grid = (T + kWavesPerBlock - 1) / kWavesPerBlock;
   const int G = s.num_groups > 1 ? s.num_groups : 1;
@@ -298,7 +306,7 @@ hipError_t launch_route_topk(const moe_shape& s, const float* logits, const int3
 #define MOE_ROUTE_LAUNCH(EPL)                                                                    \
   hipLaunchKernelGGL(k_route_topk<EPL>, dim3(grid), dim3(256), 0, st, logits, T, E, s.top_k,   \
                      k_per_token, s.score, s.renormalize, s.routed_scale, G, s.topk_groups,     \
-                     topn, ids, gates, flags)
+                     topn, ids, gates, flags, parts, part_stride, sum_out)
   if (E <= 64) MOE_ROUTE_LAUNCH(1);
   else if (E <= 128) MOE_ROUTE_LAUNCH(2);
   else if (E <= 256) MOE_ROUTE_LAUNCH(4);
