@@ -120,7 +120,7 @@ def test_layer_empty_batch(fmt):
     assert (out == 7.0).all()
 
 
-@pytest.mark.parametrize("name,T", [("mixtral_decode", 64), ("qwen3_skewed", 1024)])
+@pytest.mark.parametrize("name,T", [("mixtral_decode", 64), ("qwen3_skewed", 1024), ("deepseek_v3", 1)])
 def test_mxfp8_layer_graph_replay_matches_eager(name, T):
     """The MXFP8 layer call captured once and replayed, with eager calls and
     synchronisations between replays, reproduces the eager result bit for bit."""

@@ -15,7 +15,11 @@ from gpu_util import dev, say, workspace
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,T", [("qwen3_skewed", 1024), ("mixtral_decode", 64)])
+# qwen3_skewed T=1024: sliced vector router; T=2048: MFMA router with K split in
+# two; mixtral_decode: decode K-split down; deepseek_v3 T=1: split-K gate/up
+# (routed and shared expert) and its SwiGLU reduction
+@pytest.mark.parametrize("name,T", [("qwen3_skewed", 1024), ("qwen3_skewed", 2048), ("mixtral_decode", 64),
+                                    ("deepseek_v3", 1)])
 def test_layer_graph_replay_matches_eager(name, T):
     cfg = W.CONFIGS[name].with_tokens(T)
     say(f"graph capture {name} T={T}")
