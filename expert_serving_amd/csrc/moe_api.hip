@@ -167,6 +167,108 @@ GemmPlan choose_gemm_plan(const moe_shape& s) {
   return p;
 }
 
+namespace {
+
+// Rows-per-tile bounds of the two schedules (worst case over any routing).
+void tile_bounds(const moe_shape& s, const GemmPlan& gp, int& max_big, int& max_small) {
+  const size_t E = (size_t)s.num_experts, slots = (size_t)s.num_tokens * s.top_k;
+  max_big = gp.has_big() ? (int)(slots / (size_t)gp.bm_big + E + 1) : 0;
+  // small tiles: every expert's rows, or, with big tiles, an expert's rows
+  // below split_rows (small expert) or its tail of at most tail_rows
+  const size_t bound = slots / (size_t)gp.bm_small + E + 1;
+  if (!gp.has_small()) {
+    max_small = 0;
+  } else if (!gp.has_big()) {
+    max_small = (int)bound;
+  } else {
+    const size_t per_expert =
+        ((size_t)std::max(gp.split_rows - 1, gp.tail_rows) + gp.bm_small - 1) / gp.bm_small;
+    max_small = (int)std::min(bound, per_expert * E);
+  }
+}
+
+// Experts that can hold rows when there are few slots, one 32-row tile each
+long long few_row_tiles(const moe_shape& s) {
+  const long long slots = (long long)s.num_tokens * s.top_k;
+  return std::max<long long>(std::min<long long>(slots, (long long)s.num_experts), (slots + 31) / 32);
+}
+
+// K-split parts of the layer's down projection (partial y sums, added by
+// the combine; 1 = none).
+int down_parts(const moe_shape& s, const GemmPlan& gp, int max_tiles_small, bool mx) {
+  if (s.act_dtype != MOE_BF16) return 1;
+  const long long slots = (long long)s.num_tokens * s.top_k;
+  const long long H = s.hidden, I = s.intermediate;
+  if (!gp.has_big() && gp.has_small()) {
+    // Decode-sized layers (every expert small, few 32-row tiles) leave most
+    // compute units idle in the down projection; splitting its long K (= I)
+    // gives every unit weight rows to stream.
+    const int bnb = (mx || I >= kDown8MinK) ? 256 : 128;  // column tile of the 32-row down kernels
+    const long long blocks = (long long)max_tiles_small * ((H + bnb - 1) / bnb);
+    if (blocks <= 0 || blocks >= 512) return 1;
+    const long long few_blocks = std::min<long long>(max_tiles_small, few_row_tiles(s)) * ((H + bnb - 1) / bnb);
+    int want;
+    if (slots < s.num_experts && few_blocks > 0 && few_blocks <= kComputeUnits / 2) {
+      // fewer routed slots than experts (a few tokens): up to eight parts,
+      // so most compute units stream a slice of the few weight matrices;
+      // the combine's extra reads are a few KB per part
+      want = (int)std::min<long long>(kFewKsplit, (4LL * kComputeUnits + few_blocks - 1) / few_blocks);
+    } else {
+      // two parts measured best for both formats on the Mixtral-shaped
+      // decode layer (four or eight: slower)
+      want = (int)std::min<long long>(2, 1024 / blocks);
+    }
+    return std::max(1, std::min(want, (int)(I / 64) / 4));
+  }
+  if (gp.has_big() && gp.bm_big == 256) {
+    // Few 256-row down tiles with a long K (at an even load, at most a
+    // quarter of the compute units busy) leave the rest idle for the whole
+    // projection.  Measured on the Mixtral-shaped layer (K = 14336): 256
+    // and 512 tokens 5-10% faster per layer, both formats; at 1024 and more
+    // tokens the combine's extra reads cost about what the down projection
+    // gains, so no split there.
+    const long long big = ((slots + 255) / 256) * ((H + 255) / 256);
+    const int stages = (int)(I / 128);  // 128-element stages (MXFP8); bf16 has twice as many
+    if (big > 0 && big <= kComputeUnits / 4 && stages >= 64) {
+      const int want = (int)std::min<long long>(4, (4LL * kComputeUnits + big - 1) / big);
+      return std::max(1, std::min(want, stages / 32));
+    }
+  }
+  return 1;
+}
+
+// K-split parts of a gate/up projection on 32 x 256 weight-streaming tiles
+// that number `blocks` (fp32 partial gate and up sums, added and passed
+// through SwiGLU by a reduction kernel; 1 = none).  At most half the
+// compute units busy: about one block per unit.  Measured on the
+// DeepSeek-V3-shaped layer: one token 0.473 -> 0.289 ms, two 0.546 -> 0.359
+// ms (the shared expert's gate/up ran 8 blocks); Mixtral-shaped single
+// token unchanged (0.156 -> 0.155 ms).  `rounds`: also split when the blocks
+// fill between one and two rounds of the compute units, the rounds under
+// three quarters full: the split (up to 4) that fills them best
+// (Mixtral-shaped layer, 3 tokens: 336 blocks, 3 parts, 0.373 -> 0.332 ms
+// bf16, 0.215 -> 0.200 ms MXFP8; fuller rounds are HBM-bound already and a
+// split only adds work: 4 tokens, 448 blocks in 4 parts, 2-14% slower).
+int gate_up_parts(long long blocks, int stages, bool rounds) {
+  if (blocks <= 0) return 1;
+  if (blocks <= kComputeUnits / 2)
+    return std::max(1, std::min<int>((int)std::min<long long>(kGateUpKsplitMax,
+                                                              (kComputeUnits + blocks - 1) / blocks),
+                                     stages / 4));
+  if (!rounds || blocks > 2LL * kComputeUnits) return 1;
+  auto util = [&](long long ks) {
+    const long long n = blocks * ks, r = (n + kComputeUnits - 1) / kComputeUnits;
+    return (double)n / (double)(r * kComputeUnits);
+  };
+  if (util(1) >= 0.75) return 1;
+  int best = 1;
+  for (int ks = 2; ks <= 4 && ks <= stages / 4; ++ks)
+    if (util(ks) > util(best) + 1e-9) best = ks;
+  return best;
+}
+
+}  // namespace
+
 WsLayout plan_workspace(const moe_shape& s, bool mx) {
   WsLayout w{};
   const size_t T = (size_t)s.num_tokens, E = (size_t)s.num_experts, k = (size_t)s.top_k;
@@ -175,104 +277,19 @@ WsLayout plan_workspace(const moe_shape& s, bool mx) {
   const size_t slots = T * k;
   const GemmPlan gp = choose_gemm_plan(s);
   w.n_dispatch_tiles = (int)((slots + kDispatchTileSlots - 1) / kDispatchTileSlots);
-  w.max_tiles_big = gp.has_big() ? (int)(slots / (size_t)gp.bm_big + E + 1) : 0;
-  {
-    // a small expert has fewer than split_rows rows
-    // (small experts: under split_rows rows; big ones: a tail of at most tail_rows)
-    const size_t per_expert =
-        gp.has_big() ? ((size_t)std::max(gp.split_rows - 1, gp.tail_rows) + gp.bm_small - 1) / gp.bm_small
-                     : (size_t)-1;
-    const size_t bound = slots / (size_t)gp.bm_small + E + 1;
-    w.max_tiles_small = gp.has_small() ? (int)std::min(bound, per_expert == (size_t)-1 ? bound
-                                                                                      : per_expert * E)
-                                       : 0;
-  }
-  // Decode-sized layers (every expert small, few 32-row tiles) leave most
-  // compute units idle in the down projection; splitting its long K (= I)
-  // into partial sums that the combine adds gives every unit weight rows to
-  // stream.
-  {
-    const int bnb = (mx || I >= (size_t)kDown8MinK) ? 256 : 128;  // column tile of the 32-row down kernels
-    const long long blocks = (long long)w.max_tiles_small * ((H + bnb - 1) / bnb);
-    w.ksplit = 1;
-    // at most min(T*k, E) experts hold rows, one 32-row tile each when T*k is small
-    const long long few = std::max<long long>(std::min<long long>((long long)slots, (long long)E),
-                                              ((long long)slots + 31) / 32);
-    const long long few_blocks = std::min<long long>(w.max_tiles_small, few) * ((H + bnb - 1) / bnb);
-    if (!gp.has_big() && gp.has_small() && s.act_dtype == MOE_BF16 && blocks > 0 && blocks < 512) {
-      const int stages = (int)(I / 64);
-      int want;
-      if ((long long)slots < E && few_blocks > 0 && few_blocks <= kComputeUnits / 2) {
-        // fewer routed slots than experts (a few tokens): up to eight parts,
-        // so most compute units stream a slice of the few weight matrices;
-        // the combine's extra reads are a few KB per part
-        want = (int)std::min<long long>(kFewKsplit, (4LL * kComputeUnits + few_blocks - 1) / few_blocks);
-      } else {
-        // two parts measured best for both formats on the Mixtral-shaped
-        // decode layer (four or eight: slower)
-        want = (int)std::min<long long>(2, 1024 / blocks);
-      }
-      w.ksplit = std::max(1, std::min(want, stages / 4));
-    } else if (gp.has_big() && gp.bm_big == 256 && s.act_dtype == MOE_BF16) {
-      // Few 256-row down tiles with a long K (at an even load, at most a
-      // quarter of the compute units busy) leave the rest idle for the
-      // whole projection; splitting K gives them parts to run.  Measured on
-      // the Mixtral-shaped layer (K = 14336): 256 and 512 tokens 5-10% faster
-      // per layer, both formats; at 1024 and more tokens the combine's extra
-      // reads cost about what the down projection gains, so no split there.
-      const long long big = (long long)((slots + 255) / 256) * (long long)((H + 255) / 256);
-      const int stages = (int)(I / 128);  // 128-element stages (MXFP8); bf16 has twice as many
-      if (big > 0 && big <= kComputeUnits / 4 && stages >= 64) {
-        const int want = (int)std::min<long long>(4, (4LL * kComputeUnits + big - 1) / big);
-        w.ksplit = std::max(1, std::min(want, stages / 32));
-      }
-    }
-  }
-  // Gate/up of a token or two (routed) and of the shared expert for a few
-  // tokens: when the weight-streaming 32 x 256 tiles would keep at most half
-  // the compute units busy, K is split into about one block per unit (each
-  // streams a slice of its weight rows) and a small kernel adds the parts and
-  // applies SwiGLU.  Measured on the DeepSeek-V3-shaped layer: one token
-  // 0.473 -> 0.289 ms, two 0.546 -> 0.359 ms (the shared expert's gate/up ran
-  // 8 blocks); Mixtral-shaped single token unchanged (0.156 -> 0.155 ms).
+  tile_bounds(s, gp, w.max_tiles_big, w.max_tiles_small);
+  w.ksplit = down_parts(s, gp, w.max_tiles_small, mx);
   w.ks_gu = w.ks_gus = 1;
   if (s.act_dtype == MOE_BF16) {
     const int stages = (int)(H / (mx ? 128 : 64));  // K stages (128 codes, or 64 bf16 elements)
-    if (!gp.has_big() && gp.has_small()) {
-      const long long few = std::max<long long>(std::min<long long>((long long)slots, (long long)E),
-                                                ((long long)slots + 31) / 32);
-      const long long blocks = std::min<long long>(w.max_tiles_small, few) * (long long)((I + 255) / 256);
-      if (blocks > 0 && blocks <= kComputeUnits / 2) {
-        w.ks_gu = std::max(1, std::min<int>((int)std::min<long long>(kGateUpKsplitMax,
-                                                                     (kComputeUnits + blocks - 1) / blocks),
-                                            stages / 4));
-      }
-      else if (blocks > 0 && blocks <= 2LL * kComputeUnits) {
-        // Between one and two rounds of blocks, with the second mostly
-        // empty (the rounds under 3/4 filled): the split (up to 4) that
-        // fills the rounds best.  Mixtral-shaped layer, 3 tokens (336
-        // blocks, 3 parts): 0.373 -> 0.332 ms bf16, 0.215 -> 0.200 ms
-        // MXFP8.  Fuller rounds are HBM-bound already and a split only adds
-        // work (4 tokens, 448 blocks in 4 parts: 2-14% slower).
-        auto util = [&](long long ks) {
-          const long long n = blocks * ks, r = (n + kComputeUnits - 1) / kComputeUnits;
-          return (double)n / (double)(r * kComputeUnits);
-        };
-        if (util(1) < 0.75) {
-          int best = 1;
-          for (int ks = 2; ks <= 4 && ks <= stages / 4; ++ks)
-            if (util(ks) > util(best) + 1e-9) best = ks;
-          w.ks_gu = best;
-        }
-      }
-    }
-    if (Is > 0 && T < 128) {
-      const long long blocks = (long long)((T + 31) / 32) * (long long)((Is + 255) / 256);
-      if (blocks > 0 && blocks <= kComputeUnits / 2)
-        w.ks_gus = std::max(1, std::min<int>((int)std::min<long long>(kGateUpKsplitMax,
-                                                                      (kComputeUnits + blocks - 1) / blocks),
-                                             stages / 4));
-    }
+    // routed experts of a token or a few (decode plans only)
+    if (!gp.has_big() && gp.has_small())
+      w.ks_gu = gate_up_parts(std::min<long long>(w.max_tiles_small, few_row_tiles(s)) *
+                                  (long long)((I + 255) / 256),
+                              stages, true);
+    // the shared expert of a few tokens (32-row tiles below 128 tokens)
+    if (Is > 0 && T < 128)
+      w.ks_gus = gate_up_parts((long long)((T + 31) / 32) * (long long)((Is + 255) / 256), stages, false);
   }
   size_t o = 0;
   auto take = [&](size_t bytes) {
