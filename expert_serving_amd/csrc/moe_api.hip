@@ -118,10 +118,8 @@ T* at(void* ws, size_t off) {
 
 }  // namespace
 
-#ifndef MOE_TAIL_ROWS
-#define MOE_TAIL_ROWS 64
-#endif
-constexpr int kTailRows = MOE_TAIL_ROWS;
+// remainder rows of a big expert that ride on one small tile
+constexpr int kTailRows = 64;
 // compute units of one MI355X (8 XCDs x 32)
 constexpr int kComputeUnits = 256;
 // K-split parts of the down projection for a batch of a token or two
