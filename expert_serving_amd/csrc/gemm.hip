@@ -92,23 +92,39 @@ __device__ __forceinline__ bool block_tile(int mtiles, int ntiles, int& m, int& 
   return true;
 }
 
-// Two classes of real0 and real1 tiles: logical index L over real0 + real1
-// (XCD by XCD as above) is a class-1 tile when the count of class-1 tiles
-// among [0, L] steps up (a Bresenham spread), so the classes interleave
-// evenly in every XCD's range; idx is the tile's index within its class
-// (cls 0 or 1), in increasing order along L.
+// Two classes of real0 and real1 tiles (class 0 the long MFMA-bound tiles,
+// class 1 the short weight-streaming ones) over logical indices L (XCD by XCD
+// as above).  Each XCD's range takes its even share of both classes (the
+// count of class-1 tiles before L is floor(L * real1 / total) at the range
+// ends) and orders them in time: the last quarter of its class-1 tiles go at
+// the end of the range, the rest are spread evenly (Bresenham) over the
+// front, so short tiles fill the compute units while the XCD's last long
+// tiles finish.  idx is the tile's index within its class (cls 0 or 1), in
+// increasing order along L, so each XCD's tiles of a class are contiguous.
+constexpr int kShortTailPct = 25;
+
 __device__ __forceinline__ bool block_tile2(int real0, int real1, int& cls, int& idx) {
   const int total = real0 + real1;
   int L;
   if (!xcd_index(total, L)) return false;
-  const int c0 = (int)((long long)L * real1 / total);
-  const int c1 = (int)((long long)(L + 1) * real1 / total);
+  const int per_xcd = (total + 7) >> 3;
+  const int a = (L / per_xcd) * per_xcd;  // the XCD's range [a, a + n)
+  const int n = min(per_xcd, total - a);
+  const int sa = (int)((long long)a * real1 / total);
+  const int s = (int)((long long)(a + n) * real1 / total) - sa;  // its class-1 tiles
+  const int r = s * kShortTailPct / 100;                          // of them at the end
+  const int p = L - a;
+  // class-1 tiles among positions [0, q) of the range
+  auto before = [&](int q) {
+    return q >= n - r ? (s - r) + (q - (n - r)) : (int)((long long)q * (s - r) / (n - r));
+  };
+  const int c0 = before(p), c1 = before(p + 1);
   if (c1 > c0) {
     cls = 1;
-    idx = c0;
+    idx = sa + c0;
   } else {
     cls = 0;
-    idx = L - c0;
+    idx = a - sa + p - c0;
   }
   return true;
 }
