@@ -44,10 +44,9 @@ __device__ __forceinline__ float logistic_seq(float x) {
 }
 
 // (va, ia) ranks before (vb, ib): valid first, larger value, then lower index.
+// (Bitwise operators, so the test compiles to mask arithmetic, not branches.)
 __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
-  if (ia == INT_MAX) return false;
-  if (ib == INT_MAX) return true;
-  return va > vb || (va == vb && ia < ib);
+  return (ia != INT_MAX) & ((ib == INT_MAX) | (va > vb) | ((va == vb) & (ia < ib)));
 }
 
 __device__ __forceinline__ void wave_argbest(float& v, int& i) {
@@ -91,22 +90,32 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
 
   float v[EPL];
   bool elig[EPL];
+  int ec[EPL];  // the lane's experts, clamped to a valid address
   // logits in `parts` partial sums (a K-split router) are added in part
-  // order, and the sums stored at sum_out
+  // order, and the sums stored at sum_out.  Every load of a part is issued
+  // before the first is used.
   const float* lt = logits + (size_t)(active ? t : 0) * E;
+  int kt = k_max;
+  if (active && kpt) kt = kpt[t];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane * EPL + i;
     elig[i] = active && e < E;
-    v[i] = elig[i] ? lt[e] : 0.0f;
-    if (parts > 1 && elig[i]) {
-      for (int p = 1; p < parts; ++p) v[i] += lt[p * part_stride + e];
-      if (sum_out) sum_out[(size_t)t * E + e] = v[i];
-    }
+    ec[i] = elig[i] ? e : 0;
+    v[i] = lt[ec[i]];
   }
-
-  int kt = k_max;
-  if (active && kpt) kt = kpt[t];
+  for (int p = 1; p < parts; ++p) {
+    float w[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) w[i] = lt[p * part_stride + ec[i]];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) v[i] += w[i];
+  }
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    if (parts > 1 && sum_out && elig[i]) sum_out[(size_t)t * E + ec[i]] = v[i];
+    v[i] = elig[i] ? v[i] : 0.0f;
+  }
   const bool bad_k = active && (kt < 1 || kt > k_max);
 
   // ---- group limit: lane g ends with group g's score, the wave keeps the best groups ----
