@@ -96,13 +96,18 @@ __device__ __forceinline__ bool block_tile(int mtiles, int ntiles, int& m, int& 
 // class 1 the short weight-streaming ones) over logical indices L (XCD by XCD
 // as above).  Each XCD's range takes its even share of both classes (the
 // count of class-1 tiles before L is floor(L * real1 / total) at the range
-// ends) and orders them in time: the last quarter of its class-1 tiles go at
-// the end of the range, the rest are spread evenly (Bresenham) over the
-// front, so short tiles fill the compute units while the XCD's last long
-// tiles finish.  idx is the tile's index within its class (cls 0 or 1), in
-// increasing order along L, so each XCD's tiles of a class are contiguous.
-constexpr int kShortTailPct = 25;
-
+// ends) and orders them in time: the last r of its s class-1 tiles go at the
+// end of the range, the rest are spread evenly (Bresenham) over the front.
+// Blocks reach an XCD's compute units in range order, so short tiles at the
+// end fill the units while the last long tiles finish:
+//   - many short tiles (real1 > real0 / 4, skewed layers): r = s / 4; more
+//     would end the launch on a phase of weight streams alone;
+//   - few short tiles and at most about two and a half rounds of long tiles
+//     on the 256 compute units: r = s, longest first;
+//   - few short tiles over many rounds: r = 0, their weight streams spread
+//     between the MFMA-bound tiles.
+// idx is the tile's index within its class (cls 0 or 1), in increasing order
+// along L, so each XCD's tiles of a class are contiguous.
 __device__ __forceinline__ bool block_tile2(int real0, int real1, int& cls, int& idx) {
   const int total = real0 + real1;
   int L;
@@ -112,7 +117,7 @@ __device__ __forceinline__ bool block_tile2(int real0, int real1, int& cls, int&
   const int n = min(per_xcd, total - a);
   const int sa = (int)((long long)a * real1 / total);
   const int s = (int)((long long)(a + n) * real1 / total) - sa;  // its class-1 tiles
-  const int r = s * kShortTailPct / 100;                          // of them at the end
+  const int r = 4LL * real1 > real0 ? s / 4 : (2LL * real0 <= 5 * 256 ? s : 0);
   const int p = L - a;
   // class-1 tiles among positions [0, q) of the range
   auto before = [&](int q) {
