@@ -65,9 +65,12 @@ def lib():
         L.oracle_e4m3_value.restype = ctypes.c_double
         L.oracle_mxfp8_quantize.argtypes = [i32, i32, i32, vp, vp, vp]
         L.oracle_grouped_ffn_mxfp8.argtypes = [i32, i32, i32] + [vp] * 9 + [vp, i32, vp, vp]
+        L.oracle_ep_layout.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.oracle_ep_layout.restype = i32
+        L.oracle_ep_combine.argtypes = [i32, i32, i32, vp, vp, vp, vp]
         L.oracle_layer_forward.argtypes = (
             [i32] * 6 + [vp, vp, vp, vp] + [i32, i32, f32, i32, i32, i32, f32] + [vp, vp, vp]
-            + [i32, vp, vp, vp] + [vp, i32, vp] + [vp] * 8)
+            + [i32, vp, vp, vp] + [vp, i32, vp] + [vp] * 8 + [vp])
         _lib = L
     return _lib
 
@@ -154,6 +157,40 @@ def map_replicas(ids, replica_offsets, replica_experts, num_physical):
     return phys, int(bad)
 
 
+def ep_layout(ids, gates, E, G):
+    """Send layout of the dispatch exchange over G ranks (experts in G
+    contiguous blocks): one row per (rank, token) pair with any of the
+    token's experts on that rank, destination-major, tokens ascending.
+    Returns dict(rank_counts, rank_offsets, send_token, send_ids (local expert
+    ids), send_gates, slot_send_pos, S = rows sent)."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    g = np.ascontiguousarray(gates, dtype=np.float32)
+    T, k = ids.shape
+    n_rows = T * min(k, G)
+    rc = np.empty(G, np.int32)
+    ro = np.empty(G + 1, np.int32)
+    st = np.empty(n_rows, np.int32)
+    sid = np.empty((n_rows, k), np.int32)
+    sg = np.empty((n_rows, k), np.float32)
+    ssp = np.empty((T, k), np.int32)
+    S = lib().oracle_ep_layout(T, E, k, G, _p(ids), _p(g), _p(rc), _p(ro), _p(st), _p(sid), _p(sg), _p(ssp))
+    return dict(rank_counts=rc, rank_offsets=ro, send_token=st, send_ids=sid, send_gates=sg, slot_send_pos=ssp,
+                S=int(S))
+
+
+def ep_combine(partial, slot_send_pos, y_shared=None) -> np.ndarray:
+    """out[t] = sum over the token's distinct send rows (ascending) of
+    partial[row] (+ y_shared[t])."""
+    pt = np.ascontiguousarray(partial, dtype=np.float32)
+    ssp = np.ascontiguousarray(slot_send_pos, dtype=np.int32)
+    T, k = ssp.shape
+    H = pt.shape[1]
+    ys = None if y_shared is None else np.ascontiguousarray(y_shared, dtype=np.float32)
+    out = np.empty((T, H), np.float32)
+    lib().oracle_ep_combine(T, H, k, _p(pt), _p(ssp), _p(ys), _p(out))
+    return out
+
+
 def grouped_ffn(x_perm, offsets, w_gate, w_up, w_down, rows=None) -> np.ndarray:
     x, dt = _act(x_perm)
     wg, _ = _act(w_gate)
@@ -183,8 +220,10 @@ def combine(y_perm, row_of_slot, gates, y_shared=None) -> np.ndarray:
 
 def layer_forward(x, w_router, w_gate, w_up, w_down, k_max, bias=None, k_per_token=None,
                   score=0, renorm=1, routed_scale=1.0, num_groups=1, topk_groups=1, group_topn=0,
-                  capacity_factor=0.0, ws_gate=None, ws_up=None, ws_down=None, tokens=None):
-    """Whole layer; returns dict(out=[n,H] for `tokens` (or all), plus routing)."""
+                  capacity_factor=0.0, ws_gate=None, ws_up=None, ws_down=None, tokens=None, logits=None):
+    """Whole layer; returns dict(out=[n,H] for `tokens` (or all), plus routing).
+    logits (optional, [T,E] fp32): route on these instead of the oracle's own
+    router logits (for comparing routing given the same fp32 logits)."""
     x, dt = _act(x)
     wr, _ = _act(w_router)
     wg, _ = _act(w_gate)
@@ -205,7 +244,6 @@ def layer_forward(x, w_router, w_gate, w_up, w_down, k_max, bias=None, k_per_tok
     tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
     n = T if tok is None else len(tok)
     out = np.empty((n, H), np.float32)
-    logits = np.empty((T, E), np.float32)
     ids = np.empty((T, k_max), np.int32)
     gates = np.empty((T, k_max), np.float32)
     counts = np.empty(E, np.int32)
@@ -213,16 +251,22 @@ def layer_forward(x, w_router, w_gate, w_up, w_down, k_max, bias=None, k_per_tok
     ros = np.empty((T, k_max), np.int32)
     row_token = np.full(T * k_max, -1, np.int32)
     nd = np.zeros(1, np.int32)
+    lin = None
+    if logits is not None:
+        lin = np.ascontiguousarray(logits, dtype=np.float32)
+        assert lin.shape == (T, E), lin.shape
+    logits = np.empty((T, E), np.float32)
     lib().oracle_layer_forward(T, H, E, I, k_max, dt, _p(x), _p(wr), _p(b), _p(kpt), score, renorm,
                                routed_scale, num_groups, topk_groups, group_topn, capacity_factor,
                                _p(wg), _p(wu), _p(wd), Is, _p(sg), _p(su), _p(sd), _p(tok),
                                0 if tok is None else len(tok), _p(out), _p(logits), _p(ids),
-                               _p(gates), _p(counts), _p(offsets), _p(ros), _p(row_token), _p(nd))
+                               _p(gates), _p(counts), _p(offsets), _p(ros), _p(row_token), _p(nd),
+                               _p(lin))
     return dict(out=out, logits=logits, ids=ids, gates=gates, counts=counts, offsets=offsets,
                 row_of_slot=ros, row_token=row_token, num_dropped=int(nd[0]))
 
 
-def layer_forward_cfg(cfg, inputs_np, tokens=None):
+def layer_forward_cfg(cfg, inputs_np, tokens=None, logits=None):
     """layer_forward with the routing options of a workloads.LayerConfig."""
     i = inputs_np
     return layer_forward(i["x"], i["w_router"], i["w_gate"], i["w_up"], i["w_down"], cfg.top_k,
@@ -231,7 +275,7 @@ def layer_forward_cfg(cfg, inputs_np, tokens=None):
                          num_groups=cfg.num_groups, topk_groups=cfg.topk_groups,
                          group_topn=cfg.group_topn, capacity_factor=cfg.capacity_factor,
                          ws_gate=i.get("ws_gate"), ws_up=i.get("ws_up"), ws_down=i.get("ws_down"),
-                         tokens=tokens)
+                         tokens=tokens, logits=logits)
 
 
 # ---- MXFP8 (OCP Microscaling MXFP8, E4M3 elements, 32-element blocks) --------
@@ -288,7 +332,7 @@ def grouped_ffn_mxfp8(xq, xs, offsets, w_gate, w_up, w_down, rows=None, return_h
 
 def layer_forward_mxfp8(x, w_router, wq, k_max, bias=None, k_per_token=None, score=0, renorm=1,
                         routed_scale=1.0, num_groups=1, topk_groups=1, group_topn=0,
-                        capacity_factor=0.0, shared=None, tokens=None):
+                        capacity_factor=0.0, shared=None, tokens=None, logits=None):
     """Layer with MXFP8 experts: routing on the high-precision x and router
     (as layer_forward), x quantised to MXFP8 per token, the kept rows through
     grouped_ffn_mxfp8, the weighted sum as combine.  wq / shared: dicts with
@@ -296,8 +340,12 @@ def layer_forward_mxfp8(x, w_router, wq, k_max, bias=None, k_per_token=None, sco
     for `tokens` (or all tokens), the routing, and the FFN rows computed:
     need (kept rows, ascending), ros_c (row_of_slot of `tokens` as indices
     into need), h / h_shared (fp32 SwiGLU activations before their MXFP8
-    rounding, per need row / per token))."""
-    logits = router_logits(x, w_router, bias)
+    rounding, per need row / per token)).  logits (optional, [T,E] fp32): route on
+    these instead of the oracle's own router logits."""
+    if logits is None:
+        logits = router_logits(x, w_router, bias)
+    else:
+        logits = np.ascontiguousarray(logits, dtype=np.float32)
     ids, gates = route(logits, k_max, k_per_token, score, renorm, routed_scale, num_groups,
                        topk_groups, group_topn)
     E = wq["gate"][0].shape[0]

@@ -391,7 +391,10 @@ void oracle_combine(int T, int H, int k_max, const float* y_perm, const int32_t*
  * them); the FFN part runs for the tokens in `tokens` (n_tok entries, or all T
  * when tokens is NULL).  out is [n][H] in the order of `tokens`.
  * logits/ids/gates/counts/offsets/row_of_slot/row_token are caller buffers
- * (sizes T*E, T*k_max, T*k_max, E, E+1, T*k_max, T*k_max). */
+ * (sizes T*E, T*k_max, T*k_max, E, E+1, T*k_max, T*k_max).
+ * logits_in (nullable): router logits [T][E] to route on instead of computing
+ * them -- routing is then a function of these fp32 values alone, which is how
+ * another implementation's routing is compared with this one bit for bit. */
 void oracle_layer_forward(int T, int H, int E, int I, int k_max, int dtype, const void* x,
                           const void* w_router, const float* bias, const int32_t* k_per_token,
                           int score, int renorm, float routed_scale, int G, int topk_groups,
@@ -400,8 +403,11 @@ void oracle_layer_forward(int T, int H, int E, int I, int k_max, int dtype, cons
                           const void* ws_down, const int32_t* tokens, int n_tok, float* out,
                           float* logits, int32_t* ids, float* gates, int32_t* counts,
                           int32_t* offsets, int32_t* row_of_slot, int32_t* row_token,
-                          int32_t* num_dropped) {
-  oracle_router_logits(T, H, E, dtype, x, w_router, bias, logits);
+                          int32_t* num_dropped, const float* logits_in) {
+  if (logits_in)
+    memcpy(logits, logits_in, sizeof(float) * (size_t)T * (size_t)E);
+  else
+    oracle_router_logits(T, H, E, dtype, x, w_router, bias, logits);
   oracle_route(T, E, logits, k_max, k_per_token, score, renorm, routed_scale, G, topk_groups,
                topn, ids, gates);
   oracle_dispatch(T, E, k_max, ids, cf, counts, offsets, row_of_slot, row_token, num_dropped);
@@ -608,5 +614,109 @@ void oracle_grouped_ffn_mxfp8(int E, int H, int I, const uint8_t* xq, const uint
     free(hs);
     free(yb);
     free(dec);
+  }
+}
+
+/* ---- expert-parallel exchange over G ranks ---------------------------------
+ * "Expert Parallelism: MoE model parallel split" (jwzheng96 sglang-learning):
+ * §8, with expert parallelism over G GPUs the experts form G contiguous blocks
+ * of E/G (rank d holds experts d*E/G .. (d+1)*E/G - 1); §3 and §12 Q2, each
+ * MoE layer exchanges twice: dispatch sends a token's hidden state to the
+ * ranks of its chosen experts, combine sends the expert outputs back to the
+ * token's own rank, where they are summed with the router weights; §7 and
+ * §12, token sorting: the rows bound for one rank are grouped so they travel
+ * in one send.  "Expert parallelism for MoE serving", deployment examples:
+ * node-limited routing bounds the number of nodes a token's experts span,
+ * which lowers traffic only if a token travels once to each rank that holds
+ * any of its experts (not once per expert) -- the reading taken here; the
+ * receiving rank then applies the token's several experts to that one row
+ * and returns their gate-weighted sum as one row.
+ *
+ * Layout of the send buffer (destination-major, ragged, no padding rows):
+ * for d = 0 .. G-1, for t ascending, one row for each token with at least one
+ * routed slot (expert id in [0, E)) on rank d.
+ *   rank_counts[d]     rows for rank d                               [G]
+ *   rank_offsets       exclusive prefix sum of rank_counts           [G+1]
+ *   send_token[p]      the token of row p                            [n_rows]
+ *   send_ids[p][j]     id[t][j] - d*E/G for each slot j of t on rank d,
+ *                      -1 for its other slots                        [n_rows][k]
+ *   send_gates[p][j]   gates[t][j] where send_ids[p][j] >= 0, else 0 [n_rows][k]
+ *   slot_send_pos[t][j] the row p of token t's row for the rank of slot
+ *                      j, -1 for an unused slot                      [T][k]
+ * n_rows = T * min(k, G) rows are provided; rows from rank_offsets[G] on hold
+ * send_token -1, send_ids -1 and send_gates 0.  Ids outside [-1, E) count as
+ * unused.  Returns the number of rows sent, rank_offsets[G]. */
+int32_t oracle_ep_layout(int T, int E, int k, int G, const int32_t* ids, const float* gates,
+                         int32_t* rank_counts, int32_t* rank_offsets, int32_t* send_token,
+                         int32_t* send_ids, float* send_gates, int32_t* slot_send_pos) {
+  const int epr = E / G;
+  const int n_rows = T * (k < G ? k : G);
+  for (int64_t s = 0; s < (int64_t)T * k; ++s) slot_send_pos[s] = -1;
+  for (int p = 0; p < n_rows; ++p) {
+    send_token[p] = -1;
+    for (int j = 0; j < k; ++j) {
+      send_ids[(size_t)p * k + j] = -1;
+      send_gates[(size_t)p * k + j] = 0.0f;
+    }
+  }
+  int32_t p = 0;
+  rank_offsets[0] = 0;
+  for (int d = 0; d < G; ++d) {
+    for (int t = 0; t < T; ++t) {
+      int on_rank = 0;
+      for (int j = 0; j < k; ++j) {
+        const int e = ids[(size_t)t * k + j];
+        if (e >= 0 && e < E && e / epr == d) on_rank = 1;
+      }
+      if (!on_rank) continue;
+      send_token[p] = t;
+      for (int j = 0; j < k; ++j) {
+        const int e = ids[(size_t)t * k + j];
+        if (e >= 0 && e < E && e / epr == d) {
+          send_ids[(size_t)p * k + j] = e - d * epr;
+          send_gates[(size_t)p * k + j] = gates[(size_t)t * k + j];
+          slot_send_pos[(size_t)t * k + j] = p;
+        }
+      }
+      ++p;
+    }
+    rank_counts[d] = p - rank_offsets[d];
+    rank_offsets[d + 1] = p;
+  }
+  return p;
+}
+
+/* The combine exchange's last step, at the token's own rank: every rank that
+ * received token t returned one row, the gate-weighted sum of its experts'
+ * outputs for t (partial[p], p = the token's row in the send layout);
+ * out[t] = the sum of those rows, ascending p (ascending rank), plus
+ * y_shared[t] when given (the shared expert, weight 1, added last); fp64
+ * sums rounded once.  A token with no routed slot gets y_shared[t] or 0. */
+void oracle_ep_combine(int T, int H, int k, const float* partial, const int32_t* slot_send_pos,
+                       const float* y_shared, float* out) {
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    /* the token's distinct rows, ascending */
+    int32_t rows[64];
+    int n = 0;
+    for (int j = 0; j < k; ++j) {
+      const int32_t r = slot_send_pos[(size_t)t * k + j];
+      if (r < 0) continue;
+      int seen = 0;
+      for (int q = 0; q < n; ++q) seen |= rows[q] == r;
+      if (!seen) rows[n++] = r;
+    }
+    for (int a = 1; a < n; ++a)
+      for (int b = a; b > 0 && rows[b - 1] > rows[b]; --b) {
+        const int32_t tmp = rows[b];
+        rows[b] = rows[b - 1];
+        rows[b - 1] = tmp;
+      }
+    for (int c = 0; c < H; ++c) {
+      double acc = 0.0;
+      for (int q = 0; q < n; ++q) acc += (double)partial[(size_t)rows[q] * H + c];
+      if (y_shared) acc += (double)y_shared[(size_t)t * H + c];
+      out[(size_t)t * H + c] = (float)acc;
+    }
   }
 }

@@ -211,3 +211,54 @@ def test_layer_mxfp8_routing_is_the_high_precision_routing():
     # tokens subset
     sub = oracle.layer_forward_mxfp8(inp["x"], inp["w_router"], wq, cfg.top_k, tokens=[63, 2], **kw)
     assert np.array_equal(sub["out"], got["out"][[63, 2]])
+
+
+@pytest.mark.parametrize("tokens", [None, [17, 0, 5]])
+def test_layer_mxfp8_with_shared_expert_matches_float64_numpy(tokens):
+    """The MXFP8 layer with a shared expert, composed independently in
+    float64 numpy: each token's x quantised on its own (frexp scales, torch
+    E4M3 rounding), every kept slot's expert FFN on the decoded codes with h
+    re-quantised along I, the gate-weighted sum over the slots in order, and
+    the shared expert's FFN on the same quantised x added last with weight 1
+    (not scaled by the routed scale).  Routing (ids, gates, kept slots) is the
+    high-precision routing pinned elsewhere; dropping the shared term, scaling
+    it by 2.5, or quantising the shared expert's x with other scales fails."""
+    import workloads as W
+    cfg = W.CONFIGS["deepseek_v3"].with_tokens(24).replace(hidden=128, inter=64, experts=16, top_k=4,
+                                                           num_groups=4, topk_groups=2, shared_inter=96)
+    inp = {k: W.to_numpy_raw(v) for k, v in W.make_layer_inputs(cfg, "cpu", salt=4).items()}
+    wq = {n: oracle.mxfp8_quantize(inp[f"w_{n}"]) for n in ("gate", "up", "down")}
+    sq = {n: oracle.mxfp8_quantize(inp[f"ws_{n}"]) for n in ("gate", "up", "down")}
+    got = oracle.layer_forward_mxfp8(inp["x"], inp["w_router"], wq, cfg.top_k, bias=inp["bias"],
+                                     score=cfg.score, routed_scale=cfg.routed_scale, num_groups=cfg.num_groups,
+                                     topk_groups=cfg.topk_groups, group_topn=cfg.group_topn, shared=sq,
+                                     tokens=tokens)
+    x32 = W.bf16_bits_to_f32(inp["x"])
+    dec = {n: torch_e4m3_decode(wq[n][0]) * np.ldexp(1.0, np.repeat(wq[n][1].astype(np.int64), 32, -1) - 127)
+           for n in wq}
+    sdec = {n: torch_e4m3_decode(sq[n][0]) * np.ldexp(1.0, np.repeat(sq[n][1].astype(np.int64), 32, -1) - 127)
+            for n in sq}
+
+    def ffn(xd, g, u, d):
+        h = numpy_mx((silu(xd @ g.T) * (xd @ u.T)).astype(np.float32))
+        return h @ d.T
+
+    toks = range(cfg.tokens) if tokens is None else tokens
+    ref = np.zeros((len(toks), cfg.hidden))
+    shared_part = np.zeros_like(ref)
+    for q, t in enumerate(toks):
+        xd = numpy_mx(x32[t][None])           # this token's x alone: per-token scales
+        for j in range(cfg.top_k):
+            if got["row_of_slot"][t, j] < 0:
+                continue
+            e = got["ids"][t, j]
+            ref[q] += float(got["gates"][t, j]) * ffn(xd, dec["gate"][e], dec["up"][e], dec["down"][e])[0]
+        shared_part[q] = ffn(xd, sdec["gate"], sdec["up"], sdec["down"])[0]
+    full = ref + shared_part
+    r = np.sqrt(np.mean(full ** 2))
+    assert np.max(np.abs(got["out"] - full)) <= 1e-5 * r
+    # the shared term is a sizeable part of the output (so a dropped or
+    # mis-scaled term cannot hide inside the tolerance)
+    assert np.sqrt(np.mean(shared_part ** 2)) >= 0.2 * r
+    assert np.max(np.abs(got["out"] - (ref + 2.5 * shared_part))) > 1e-2 * r
+    assert np.isclose(got["gates"].sum(1), cfg.routed_scale, rtol=1e-6).all()

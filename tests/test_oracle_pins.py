@@ -466,6 +466,42 @@ def test_layer_matches_dense_masked_evaluation(bf16, cf, Is):
     assert np.array_equal(sub["out"], res["out"][tok])
 
 
+@pytest.mark.parametrize("cf", [0.0, 1.0])
+def test_layer_routes_on_given_logits(cf):
+    """layer_forward(logits=L) routes on L (the way a GPU's routing is
+    checked given its own fp32 logits): with the oracle's own logits it is the
+    default call bit for bit; with other logits the routing, dispatch and
+    output follow them -- checked against the dense masked float64 layer
+    built from stable argsort and library dispatch on those logits."""
+    E, k = 6, 2
+    d = _tiny_layer(True, E=E, seed=11)
+    base = oracle.layer_forward(d["x"], d["w_router"], d["w_gate"], d["w_up"], d["w_down"], k, capacity_factor=cf)
+    same = oracle.layer_forward(d["x"], d["w_router"], d["w_gate"], d["w_up"], d["w_down"], k, capacity_factor=cf,
+                                logits=base["logits"])
+    for key in ("out", "logits", "ids", "gates", "counts", "offsets", "row_of_slot"):
+        assert np.array_equal(same[key], base[key]), key
+    rng = np.random.default_rng(5)
+    L = rng.standard_normal(base["logits"].shape).astype(np.float32)
+    res = oracle.layer_forward(d["x"], d["w_router"], d["w_gate"], d["w_up"], d["w_down"], k, capacity_factor=cf,
+                               logits=L)
+    assert np.array_equal(res["logits"], L)
+    T = L.shape[0]
+    ids = np.stack([stable_topk(L[t], k) for t in range(T)])
+    assert np.array_equal(res["ids"], ids)
+    assert not np.array_equal(ids, base["ids"])
+    C = math.ceil(cf * T * k / E) if cf > 0 else 10 ** 12
+    _, _, ros, _, _ = library_dispatch(ids, E, C)
+    assert np.array_equal(res["row_of_slot"], ros)
+    G = np.zeros((T, E))
+    for t in range(T):
+        g = special.softmax(L[t, ids[t]].astype(np.float64))
+        for j in range(k):
+            if ros[t, j] >= 0:
+                G[t, ids[t, j]] = g[j]
+    ref = _dense_masked_layer(d, G)
+    assert np.abs(res["out"] - ref).max() <= 2e-6 * np.sqrt((ref ** 2).mean())
+
+
 def test_identical_experts_give_routing_independent_output():
     d = _tiny_layer(False, E=5, seed=3)
     for key in ("w_gate", "w_up", "w_down"):
