@@ -23,7 +23,8 @@ MOE_FLAG_BAD_K, MOE_FLAG_BAD_EXPERT, MOE_FLAG_H_RANGE, MOE_FLAG_BAD_REPLICA = 1,
 EXPORTED = ("moe_workspace_size", "moe_route_topk", "moe_dispatch", "moe_map_replicas", "moe_grouped_ffn",
             "moe_combine", "moe_layer_forward", "moe_group_score_sigmoid", "moe_status_string",
             "moe_last_hip_error", "moe_read_device_flags", "moe_quantize_mxfp8", "moe_workspace_size_mxfp8",
-            "moe_grouped_ffn_mxfp8", "moe_layer_forward_mxfp8")
+            "moe_grouped_ffn_mxfp8", "moe_layer_forward_mxfp8", "moe_layer_forward_noalloc")
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeShape(ctypes.Structure):
@@ -84,6 +85,8 @@ def lib():
         L.moe_combine.argtypes = [sp, vp, vp, vp, vp, vp, vp]
         L.moe_layer_forward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                         ctypes.POINTER(MoeDebug), vp, sz, vp]
+        L.moe_layer_forward_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                ctypes.POINTER(MoeDebug), vp]
         L.moe_group_score_sigmoid.argtypes = [vp, vp, ctypes.c_int64, vp]
         L.moe_status_string.argtypes = [st]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -193,6 +196,20 @@ def moe_layer_forward(shape, x, w_router, router_bias, k_per_token, w_gate, w_up
                                    ctypes.byref(d) if d is not None else None, _ptr(ws),
                                    ws.numel() if ws_bytes is None else ws_bytes, _stream(stream)),
            "moe_layer_forward")
+
+
+def moe_layer_forward_noalloc(shape, x, w_router, router_bias, k_per_token, w_gate, w_up, w_down, ws_gate,
+                              ws_up, ws_down, out, dbg: Optional[dict], stream=None):
+    d = None
+    if isinstance(dbg, MoeDebug):
+        d = dbg
+    elif dbg:
+        d = MoeDebug(**{k: _ptr(v) for k, v in dbg.items()})
+    _check(lib().moe_layer_forward_noalloc(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(router_bias),
+                                           _ptr(k_per_token), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                           _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(out),
+                                           ctypes.byref(d) if d is not None else None, _stream(stream)),
+           "moe_layer_forward_noalloc")
 
 
 def moe_group_score_sigmoid(x, y, n=None, stream=None):

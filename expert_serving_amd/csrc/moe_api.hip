@@ -4,6 +4,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -525,6 +526,117 @@ moe_status run_shared(const moe_shape& s, const void* x, const void* wsg, const 
   return MOE_OK;
 }
 
+// ---- the layer, shared by the workspace and the no-allocation entry points ---
+
+// Host checks of moe_layer_forward's arguments (all but the workspace).
+moe_status check_layer_args(const moe_shape* shape, const void* x, const void* w_router,
+                            const float* router_bias, const int32_t* k_per_token, const void* w_gate,
+                            const void* w_up, const void* w_down, const void* ws_gate,
+                            const void* ws_up, const void* ws_down, const void* out,
+                            const moe_debug* dbg) {
+  MOE_TRY(check_shape(shape));
+  const moe_shape& s = *shape;
+  MOE_TRY(need(x));
+  MOE_TRY(need(w_router));
+  MOE_TRY(opt4(router_bias));
+  MOE_TRY(opt4(k_per_token));
+  MOE_TRY(need(w_gate));
+  MOE_TRY(need(w_up));
+  MOE_TRY(need(w_down));
+  if (s.shared_intermediate > 0) {
+    MOE_TRY(need(ws_gate));
+    MOE_TRY(need(ws_up));
+    MOE_TRY(need(ws_down));
+  }
+  MOE_TRY(need(out));
+  if (dbg) {
+    if (dbg->logits) MOE_TRY(need(dbg->logits));
+    MOE_TRY(opt4(dbg->topk_ids));
+    MOE_TRY(opt4(dbg->topk_gates));
+    MOE_TRY(opt4(dbg->expert_counts));
+    MOE_TRY(opt4(dbg->expert_offsets));
+    MOE_TRY(opt4(dbg->row_of_slot));
+    MOE_TRY(opt4(dbg->num_dropped));
+  }
+  return MOE_OK;
+}
+
+// S1-S10 on validated arguments, T > 0, with workspace `ws` laid out as L.
+moe_status run_layer(const moe_shape& s, const void* x, const void* w_router, const float* router_bias,
+                     const int32_t* k_per_token, const void* w_gate, const void* w_up,
+                     const void* w_down, const void* ws_gate, const void* ws_up, const void* ws_down,
+                     void* out, const moe_debug* dbg, void* ws, const WsLayout& L, hipStream_t st) {
+  float* logits = (dbg && dbg->logits) ? dbg->logits : at<float>(ws, L.logits);
+  int32_t* ids = (dbg && dbg->topk_ids) ? dbg->topk_ids : at<int32_t>(ws, L.ids);
+  float* gates = (dbg && dbg->topk_gates) ? dbg->topk_gates : at<float>(ws, L.gates);
+  int32_t* counts = (dbg && dbg->expert_counts) ? dbg->expert_counts : at<int32_t>(ws, L.counts);
+  int32_t* offsets = (dbg && dbg->expert_offsets) ? dbg->expert_offsets : at<int32_t>(ws, L.offsets);
+  int32_t* ros = (dbg && dbg->row_of_slot) ? dbg->row_of_slot : at<int32_t>(ws, L.row_of_slot);
+  int32_t* nd = (dbg && dbg->num_dropped) ? dbg->num_dropped : at<int32_t>(ws, L.num_dropped);
+  uint32_t* flags = at<uint32_t>(ws, L.flags);
+  int32_t* row_token = at<int32_t>(ws, L.row_token);
+  float* y = at<float>(ws, L.y);
+
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTER, true, st));
+  int rparts = 1;
+  float* lparts = at<float>(ws, L.logits_parts);
+  MOE_TRY(run_router(s, x, w_router, router_bias, logits, flags, st, lparts, rparts));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTER, false, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTE, true, st));
+  MOE_HIP(launch_route_topk(s, rparts > 1 ? lparts : logits, k_per_token, ids, gates, flags, st, rparts,
+                            (long long)s.num_tokens * s.num_experts, rparts > 1 ? logits : nullptr));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTE, false, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_DISPATCH, true, st));
+  MOE_HIP(launch_dispatch(s, ids, counts, offsets, ros, row_token, nd,
+                          at<int32_t>(ws, L.tile_counts), L.n_dispatch_tiles, flags, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_DISPATCH, false, st));
+  // S6 gather: fused into the gate/up GEMM's tile loads (rows x[row_token[r]])
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_GATHER, true, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_GATHER, false, st));
+  MOE_TRY(run_ffn(s, x, row_token, offsets, w_gate, w_up, w_down, y, ws, L, st, dbg, L.ksplit));
+  const float* ys = nullptr;
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_SHARED, true, st));
+  if (s.shared_intermediate > 0) {
+    MOE_TRY(run_shared(s, x, ws_gate, ws_up, ws_down, ws, L, st));
+    ys = at<float>(ws, L.ys);
+  }
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_SHARED, false, st));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_COMBINE, true, st));
+  MOE_HIP(launch_combine(s, y, ros, gates, ys, out, st, L.ksplit,
+                         (long long)s.num_tokens * s.top_k * s.hidden));
+  MOE_HIP(stage_mark(dbg, MOE_STAGE_COMBINE, false, st));
+  return MOE_OK;
+}
+
+// ---- workspace of the no-allocation entry point --------------------------------
+// One array in the library's own device memory; every GPU the library runs on
+// holds its own copy (placed when the code object is loaded on that GPU) until
+// the process ends.  In host code `scratch` names a host-side stand-in, never
+// the device array: host code uses only the address hipGetSymbolAddress gives
+// for the current device, kept per device below.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxScratchDevices];
+
+// Device address of the current GPU's `scratch`, looked up on the first call
+// on that GPU (with it current) and kept.
+moe_status static_scratch(void** ptr) {
+  int dev = -1;
+  MOE_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxScratchDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    MOE_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return MOE_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *ptr = g_scratch_dev[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -683,76 +795,30 @@ moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* 
                              const void* ws_gate, const void* ws_up, const void* ws_down,
                              void* out, const moe_debug* dbg, void* ws, size_t ws_bytes,
                              void* stream) {
-  MOE_TRY(check_shape(shape));
-  const moe_shape& s = *shape;
-  MOE_TRY(need(x));
-  MOE_TRY(need(w_router));
-  MOE_TRY(opt4(router_bias));
-  MOE_TRY(opt4(k_per_token));
-  MOE_TRY(need(w_gate));
-  MOE_TRY(need(w_up));
-  MOE_TRY(need(w_down));
-  if (s.shared_intermediate > 0) {
-    MOE_TRY(need(ws_gate));
-    MOE_TRY(need(ws_up));
-    MOE_TRY(need(ws_down));
-  }
-  MOE_TRY(need(out));
+  MOE_TRY(check_layer_args(shape, x, w_router, router_bias, k_per_token, w_gate, w_up, w_down, ws_gate,
+                           ws_up, ws_down, out, dbg));
   MOE_TRY(need(ws));
-  if (dbg) {
-    if (dbg->logits) MOE_TRY(need(dbg->logits));
-    MOE_TRY(opt4(dbg->topk_ids));
-    MOE_TRY(opt4(dbg->topk_gates));
-    MOE_TRY(opt4(dbg->expert_counts));
-    MOE_TRY(opt4(dbg->expert_offsets));
-    MOE_TRY(opt4(dbg->row_of_slot));
-    MOE_TRY(opt4(dbg->num_dropped));
-  }
-  const WsLayout L = plan_workspace(s);
+  const WsLayout L = plan_workspace(*shape);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
-  if (s.num_tokens == 0) return MOE_OK;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (shape->num_tokens == 0) return MOE_OK;
+  return run_layer(*shape, x, w_router, router_bias, k_per_token, w_gate, w_up, w_down, ws_gate, ws_up,
+                   ws_down, out, dbg, ws, L, static_cast<hipStream_t>(stream));
+}
 
-  float* logits = (dbg && dbg->logits) ? dbg->logits : at<float>(ws, L.logits);
-  int32_t* ids = (dbg && dbg->topk_ids) ? dbg->topk_ids : at<int32_t>(ws, L.ids);
-  float* gates = (dbg && dbg->topk_gates) ? dbg->topk_gates : at<float>(ws, L.gates);
-  int32_t* counts = (dbg && dbg->expert_counts) ? dbg->expert_counts : at<int32_t>(ws, L.counts);
-  int32_t* offsets = (dbg && dbg->expert_offsets) ? dbg->expert_offsets : at<int32_t>(ws, L.offsets);
-  int32_t* ros = (dbg && dbg->row_of_slot) ? dbg->row_of_slot : at<int32_t>(ws, L.row_of_slot);
-  int32_t* nd = (dbg && dbg->num_dropped) ? dbg->num_dropped : at<int32_t>(ws, L.num_dropped);
-  uint32_t* flags = at<uint32_t>(ws, L.flags);
-  int32_t* row_token = at<int32_t>(ws, L.row_token);
-  float* y = at<float>(ws, L.y);
-
-  MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTER, true, st));
-  int rparts = 1;
-  float* lparts = at<float>(ws, L.logits_parts);
-  MOE_TRY(run_router(s, x, w_router, router_bias, logits, flags, st, lparts, rparts));
-  MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTER, false, st));
-  MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTE, true, st));
-  MOE_HIP(launch_route_topk(s, rparts > 1 ? lparts : logits, k_per_token, ids, gates, flags, st, rparts,
-                            (long long)s.num_tokens * s.num_experts, rparts > 1 ? logits : nullptr));
-  MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTE, false, st));
-  MOE_HIP(stage_mark(dbg, MOE_STAGE_DISPATCH, true, st));
-  MOE_HIP(launch_dispatch(s, ids, counts, offsets, ros, row_token, nd,
-                          at<int32_t>(ws, L.tile_counts), L.n_dispatch_tiles, flags, st));
-  MOE_HIP(stage_mark(dbg, MOE_STAGE_DISPATCH, false, st));
-  // S6 gather: fused into the gate/up GEMM's tile loads (rows x[row_token[r]])
-  MOE_HIP(stage_mark(dbg, MOE_STAGE_GATHER, true, st));
-  MOE_HIP(stage_mark(dbg, MOE_STAGE_GATHER, false, st));
-  MOE_TRY(run_ffn(s, x, row_token, offsets, w_gate, w_up, w_down, y, ws, L, st, dbg, L.ksplit));
-  const float* ys = nullptr;
-  MOE_HIP(stage_mark(dbg, MOE_STAGE_SHARED, true, st));
-  if (s.shared_intermediate > 0) {
-    MOE_TRY(run_shared(s, x, ws_gate, ws_up, ws_down, ws, L, st));
-    ys = at<float>(ws, L.ys);
-  }
-  MOE_HIP(stage_mark(dbg, MOE_STAGE_SHARED, false, st));
-  MOE_HIP(stage_mark(dbg, MOE_STAGE_COMBINE, true, st));
-  MOE_HIP(launch_combine(s, y, ros, gates, ys, out, st, L.ksplit,
-                         (long long)s.num_tokens * s.top_k * s.hidden));
-  MOE_HIP(stage_mark(dbg, MOE_STAGE_COMBINE, false, st));
-  return MOE_OK;
+moe_status moe_layer_forward_noalloc(const moe_shape* shape, const void* x, const void* w_router,
+                                     const float* router_bias, const int32_t* k_per_token,
+                                     const void* w_gate, const void* w_up, const void* w_down,
+                                     const void* ws_gate, const void* ws_up, const void* ws_down,
+                                     void* out, const moe_debug* dbg, void* stream) {
+  MOE_TRY(check_layer_args(shape, x, w_router, router_bias, k_per_token, w_gate, w_up, w_down, ws_gate,
+                           ws_up, ws_down, out, dbg));
+  const WsLayout L = plan_workspace(*shape);
+  if (L.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  if (shape->num_tokens == 0) return MOE_OK;
+  void* ws = nullptr;
+  MOE_TRY(static_scratch(&ws));
+  return run_layer(*shape, x, w_router, router_bias, k_per_token, w_gate, w_up, w_down, ws_gate, ws_up,
+                   ws_down, out, dbg, ws, L, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_quantize_mxfp8(int32_t rows, int32_t cols, int32_t src_dtype, const void* src,

@@ -27,7 +27,8 @@
  *     aligned to 16 bytes.  The library allocates no memory and keeps no state
  *     between calls; scratch space is the caller's workspace `ws` of at least
  *     moe_workspace_size() bytes.  Calls on different streams need distinct
- *     workspaces.
+ *     workspaces.  (The one exception, moe_layer_forward_noalloc, takes its
+ *     workspace from an array in the library's own device memory.)
  *   - Weights are output-major with K contiguous: router [E][H]; gate and up
  *     [E][I][H]; down [E][H][I]; shared gate/up [Is][H], shared down [H][Is].
  *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
@@ -227,6 +228,31 @@ moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* 
                              const void* ws_gate, const void* ws_up, const void* ws_down,
                              void* out, const moe_debug* dbg, void* ws, size_t ws_bytes,
                              void* stream);
+
+/* ---- the layer without a caller workspace ------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Computes
+ * exactly what moe_layer_forward computes (same kernels, bit-identical
+ * results) with its workspace taken from an array the library keeps in its
+ * own device memory: MOE_NOALLOC_SCRATCH_BYTES per GPU, placed when the
+ * library's code is loaded on that GPU and held until the process ends.  The
+ * call allocates nothing (no hipMalloc, hipFree or allocating library call);
+ * its first call on a GPU looks up that GPU's array (the current device's;
+ * `stream` must belong to it).  Shapes whose moe_workspace_size() exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_WORKSPACE before anything is
+ * enqueued (e.g. decode-sized layers fit: 64 tokens of a Mixtral-8x7B-shaped
+ * layer need 7.5 MiB, of a DeepSeek-V3-shaped layer 34 MiB).  Every call on a
+ * GPU shares that GPU's array and leaves its contents behind; each call
+ * clears what it needs cleared (the flag word) itself.  Calls that overlap in
+ * time on one GPU (different streams or threads, or a graph replay beside an
+ * eager call) race on the array: serialise them.  The flag word of the array
+ * is not readable through moe_read_device_flags. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_layer_forward_noalloc(const moe_shape* shape, const void* x, const void* w_router,
+                                     const float* router_bias, const int32_t* k_per_token,
+                                     const void* w_gate, const void* w_up, const void* w_down,
+                                     const void* ws_gate, const void* ws_up, const void* ws_down,
+                                     void* out, const moe_debug* dbg, void* stream);
 
 /* ---- 8-bit experts (MXFP8) ---------------------------------------------
  * The pages serve the experts with FP8 quantisation and keep the router in

@@ -154,3 +154,33 @@ def test_zero_tokens_is_a_no_op():
 def test_binding_raises_on_error():
     with pytest.raises(abi.MoeError):
         abi.moe_workspace_size(base_shape(top_k=0))
+
+
+def test_noalloc_entry_point_checks_before_any_hip_call():
+    """The no-allocation layer call validates like moe_layer_forward, rejects
+    shapes whose workspace exceeds its fixed device array, and enqueues
+    nothing for zero tokens -- all before any HIP call."""
+    L = abi.lib()
+    assert abi.MOE_NOALLOC_SCRATCH_BYTES == 64 << 20
+    header = open(HEADER).read()
+    assert "#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)" in header
+
+    def call(s, out=FAKE, wg=FAKE):
+        return L.moe_layer_forward_noalloc(ctypes.byref(s), FAKE, FAKE, None, None, wg, FAKE, FAKE,
+                                           FAKE, FAKE, FAKE, out, None, None)
+
+    big = abi.make_shape(W.CONFIGS["mixtral_prefill"])            # 4096 tokens: ~400 MB of workspace
+    assert abi.moe_workspace_size(big) > abi.MOE_NOALLOC_SCRATCH_BYTES
+    assert call(big) == abi.MOE_ERR_WORKSPACE
+    ds = abi.make_shape(W.CONFIGS["deepseek_v3"], num_tokens=1024)   # 289 MiB
+    assert call(ds) == abi.MOE_ERR_WORKSPACE
+    # decode-sized layers fit
+    for name, T in (("mixtral_decode", 64), ("deepseek_v3", 64), ("qwen3_skewed", 512)):
+        s = abi.make_shape(W.CONFIGS[name], num_tokens=T)
+        assert abi.moe_workspace_size(s) <= abi.MOE_NOALLOC_SCRATCH_BYTES, name
+    # argument errors come first, whatever the size
+    assert call(big, out=None) == abi.MOE_ERR_INVALID_ARG
+    assert call(abi.make_shape(W.CONFIGS["mixtral_decode"]), wg=FAKE_ODD) == abi.MOE_ERR_INVALID_ARG
+    assert call(abi.make_shape(W.CONFIGS["mixtral_decode"], top_k=0)) == abi.MOE_ERR_INVALID_ARG
+    # zero tokens: valid, nothing enqueued (no device is touched)
+    assert call(abi.make_shape(W.CONFIGS["mixtral_decode"], num_tokens=0)) == abi.MOE_OK
