@@ -464,9 +464,11 @@ double oracle_e4m3_value(int code) {
 
 /* Nearest E4M3 value to q (|q| < 512 here), ties to the even code; values at
  * or beyond 448 in magnitude saturate to 448.  The sign is kept, so a
- * negative value that rounds to zero gives 0x80.  pos[c] is the value of
- * code c for c = 0 .. 0x7E (increasing), searched by bisection. */
-static uint8_t e4m3_encode(double q, const double* pos) {
+ * negative value that rounds to zero gives 0x80.  The code of the rounded
+ * value r is read off its binary form, inverting oracle_e4m3_value: r =
+ * (1 + m/8) * 2^E with E >= -6 is code ((E + 7) << 3) | m; below 2^-6, r =
+ * m * 2^-9 is code m. */
+static uint8_t e4m3_encode(double q) {
   const int neg = signbit(q) != 0;
   double a = fabs(q);
   uint8_t mag;
@@ -481,15 +483,15 @@ static uint8_t e4m3_encode(double q, const double* pos) {
     if (e < -6) e = -6;
     const double ulp = ldexp(1.0, e - 3);
     const double r = rint(a / ulp) * ulp; /* default rounding: to nearest, ties to even */
-    /* the code whose value is r (r is representable; the positive codes
-     * are increasing in value) */
-    int lo = 0, hi = 0x7E;
-    while (lo < hi) {
-      const int mid = (lo + hi) / 2;
-      if (pos[mid] < r) lo = mid + 1;
-      else hi = mid;
+    if (r < 0x1p-6) {
+      mag = (uint8_t)(r * 512.0);          /* subnormal (or zero): m * 2^-9 */
+    } else {
+      int er;
+      (void)frexp(r, &er);                 /* r in [2^(er-1), 2^er) */
+      const int E = er - 1;
+      const int m = (int)((ldexp(r, -E) - 1.0) * 8.0);
+      mag = (uint8_t)(((E + 7) << 3) | m);
     }
-    mag = (uint8_t)lo;
   }
   return (uint8_t)(mag | (neg ? 0x80 : 0));
 }
@@ -503,8 +505,6 @@ static uint8_t e4m3_encode(double q, const double* pos) {
 void oracle_mxfp8_quantize(int rows, int cols, int dtype, const void* src, uint8_t* codes,
                            uint8_t* scales) {
   const int nb = cols / 32;
-  double pos[0x7F];
-  for (int c = 0; c <= 0x7E; ++c) pos[c] = oracle_e4m3_value(c);
 #pragma omp parallel for schedule(static)
   for (int r = 0; r < rows; ++r) {
     for (int b = 0; b < nb; ++b) {
@@ -523,7 +523,8 @@ void oracle_mxfp8_quantize(int rows, int cols, int dtype, const void* src, uint8
         if (s > 127) s = 127;
       }
       scales[(size_t)r * nb + b] = (uint8_t)(s + 127);
-      for (int i = 0; i < 32; ++i) codes[o + i] = e4m3_encode(ldexp(elem(src, dtype, o + i), -s), pos);
+      const double inv = ldexp(1.0, -s); /* 2^-s: the division by the scale is exact */
+      for (int i = 0; i < 32; ++i) codes[o + i] = e4m3_encode(elem(src, dtype, o + i) * inv);
     }
   }
 }
@@ -545,31 +546,29 @@ static void mx_decode_row(const double* tbl, const uint8_t* codes, const uint8_t
  * a = Wg . x and u = Wu . x over the decoded values (fp64 sums in ascending
  * k); h = silu(a)*u is rounded to fp32 and re-quantised to MXFP8 along I (the
  * input of the down projection is 8-bit as well); y = Wd . h over the decoded
- * h (fp64, ascending i).  wg/wu rows e*I .. e*I+I-1 of [E*I][H]; wd rows
- * e*H .. of [E*H][I].  Scratch: xd, wgd, wud [H]; hd, wdd [I]. */
+ * h (fp64, ascending i).  dg, du: the expert's decoded gate and up weights
+ * [I][H]; dd: its decoded down weights [H][I] (mx_decode_row of every weight
+ * row, done once per expert by the caller).  Scratch: xd [H], hd [I]. */
 static void ffn_row_mxfp8(const double* tbl, int H, int I, const uint8_t* xq, const uint8_t* xs,
-                          size_t xrow, const uint8_t* wgq, const uint8_t* wgs, const uint8_t* wuq,
-                          const uint8_t* wus, const uint8_t* wdq, const uint8_t* wds, int e,
-                          float* h32, uint8_t* hq, uint8_t* hs, double* xd, double* wgd,
-                          double* wud, double* hd, double* wdd, double* y) {
+                          size_t xrow, const double* dg, const double* du, const double* dd,
+                          float* h32, uint8_t* hq, uint8_t* hs, double* xd, double* hd, double* y) {
   mx_decode_row(tbl, xq, xs, H, xrow, xd);
   for (int i = 0; i < I; ++i) {
-    const size_t wr = (size_t)e * I + i;
-    mx_decode_row(tbl, wgq, wgs, H, wr, wgd);
-    mx_decode_row(tbl, wuq, wus, H, wr, wud);
+    const double* wg = dg + (size_t)i * H;
+    const double* wu = du + (size_t)i * H;
     double a = 0.0, u = 0.0;
     for (int k = 0; k < H; ++k) {
-      a += wgd[k] * xd[k];
-      u += wud[k] * xd[k];
+      a += wg[k] * xd[k];
+      u += wu[k] * xd[k];
     }
     h32[i] = (float)(a / (1.0 + exp(-a)) * u);
   }
   oracle_mxfp8_quantize(1, I, OR_F32, h32, hq, hs);
   mx_decode_row(tbl, hq, hs, I, 0, hd);
   for (int c = 0; c < H; ++c) {
-    mx_decode_row(tbl, wdq, wds, I, (size_t)e * H + c, wdd);
+    const double* wd = dd + (size_t)c * I;
     double s = 0.0;
-    for (int i = 0; i < I; ++i) s += wdd[i] * hd[i];
+    for (int i = 0; i < I; ++i) s += wd[i] * hd[i];
     y[c] = s;
   }
 }
@@ -587,34 +586,61 @@ void oracle_grouped_ffn_mxfp8(int E, int H, int I, const uint8_t* xq, const uint
   int n = rows ? n_rows : offsets[E];
   double tbl[256];
   for (int c = 0; c < 256; ++c) tbl[c] = oracle_e4m3_value(c);
-#pragma omp parallel
-  {
-    float* h32 = (float*)malloc(sizeof(float) * (size_t)I);
-    uint8_t* hq = (uint8_t*)malloc((size_t)I);
-    uint8_t* hs = (uint8_t*)malloc((size_t)I / 32 + 1);
-    double* yb = (double*)malloc(sizeof(double) * (size_t)H);
-    double* dec = (double*)malloc(sizeof(double) * (3 * (size_t)H + 2 * (size_t)I));
-#pragma omp for schedule(dynamic, 1)
-    for (int q = 0; q < n; ++q) {
-      int r = rows ? rows[q] : q;
-      int e = 0;
-      while (e < E && !(r >= offsets[e] && r < offsets[e + 1])) ++e;
-      if (e == E) {
-        for (int c = 0; c < H; ++c) y[(size_t)q * H + c] = 0.0f;
-        if (h_out) memset(h_out + (size_t)q * I, 0, sizeof(float) * (size_t)I);
-        continue;
-      }
-      ffn_row_mxfp8(tbl, H, I, xq, xs, (size_t)r, wgq, wgs, wuq, wus, wdq, wds, e, h32, hq, hs, dec,
-                    dec + H, dec + 2 * (size_t)H, dec + 3 * (size_t)H, dec + 3 * (size_t)H + I, yb);
-      for (int c = 0; c < H; ++c) y[(size_t)q * H + c] = (float)yb[c];
-      if (h_out) memcpy(h_out + (size_t)q * I, h32, sizeof(float) * (size_t)I);
+  /* the expert of every requested row (E: none) */
+  int* eq = (int*)malloc(sizeof(int) * (size_t)(n > 0 ? n : 1));
+  for (int q = 0; q < n; ++q) {
+    int r = rows ? rows[q] : q;
+    int e = 0;
+    while (e < E && !(r >= offsets[e] && r < offsets[e + 1])) ++e;
+    eq[q] = e;
+    if (e == E) {
+      for (int c = 0; c < H; ++c) y[(size_t)q * H + c] = 0.0f;
+      if (h_out) memset(h_out + (size_t)q * I, 0, sizeof(float) * (size_t)I);
     }
-    free(h32);
-    free(hq);
-    free(hs);
-    free(yb);
-    free(dec);
   }
+  /* expert by expert: its weights decoded once, then its rows */
+  double* dg = (double*)malloc(sizeof(double) * (size_t)I * H);
+  double* du = (double*)malloc(sizeof(double) * (size_t)I * H);
+  double* dd = (double*)malloc(sizeof(double) * (size_t)H * I);
+  for (int e = 0; e < E; ++e) {
+    int any = 0;
+    for (int q = 0; q < n && !any; ++q) any = eq[q] == e;
+    if (!any) continue;
+#pragma omp parallel for schedule(static)
+    for (int i = 0; i < I; ++i) {
+      mx_decode_row(tbl, wgq, wgs, H, (size_t)e * I + i, dg + (size_t)i * H);
+      mx_decode_row(tbl, wuq, wus, H, (size_t)e * I + i, du + (size_t)i * H);
+    }
+#pragma omp parallel for schedule(static)
+    for (int c = 0; c < H; ++c) mx_decode_row(tbl, wdq, wds, I, (size_t)e * H + c, dd + (size_t)c * I);
+#pragma omp parallel
+    {
+      float* h32 = (float*)malloc(sizeof(float) * (size_t)I);
+      uint8_t* hq = (uint8_t*)malloc((size_t)I);
+      uint8_t* hs = (uint8_t*)malloc((size_t)I / 32 + 1);
+      double* yb = (double*)malloc(sizeof(double) * (size_t)H);
+      double* xd = (double*)malloc(sizeof(double) * (size_t)H);
+      double* hd = (double*)malloc(sizeof(double) * (size_t)I);
+#pragma omp for schedule(dynamic, 1)
+      for (int q = 0; q < n; ++q) {
+        if (eq[q] != e) continue;
+        int r = rows ? rows[q] : q;
+        ffn_row_mxfp8(tbl, H, I, xq, xs, (size_t)r, dg, du, dd, h32, hq, hs, xd, hd, yb);
+        for (int c = 0; c < H; ++c) y[(size_t)q * H + c] = (float)yb[c];
+        if (h_out) memcpy(h_out + (size_t)q * I, h32, sizeof(float) * (size_t)I);
+      }
+      free(h32);
+      free(hq);
+      free(hs);
+      free(yb);
+      free(xd);
+      free(hd);
+    }
+  }
+  free(dg);
+  free(du);
+  free(dd);
+  free(eq);
 }
 
 /* ---- expert-parallel exchange over G ranks ---------------------------------
