@@ -16,14 +16,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
-MOE_F32, MOE_BF16 = 0, 1
+MOE_F32, MOE_BF16, MOE_F16 = 0, 1, 2
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
-MOE_FLAG_BAD_K, MOE_FLAG_BAD_EXPERT, MOE_FLAG_H_RANGE, MOE_FLAG_BAD_REPLICA = 1, 2, 4, 8
+MOE_FLAG_BAD_K, MOE_FLAG_BAD_EXPERT, MOE_FLAG_H_RANGE, MOE_FLAG_BAD_REPLICA, MOE_FLAG_Y_RANGE = 1, 2, 4, 8, 16
 
 EXPORTED = ("moe_workspace_size", "moe_route_topk", "moe_dispatch", "moe_map_replicas", "moe_grouped_ffn",
             "moe_combine", "moe_layer_forward", "moe_group_score_sigmoid", "moe_status_string",
             "moe_last_hip_error", "moe_read_device_flags", "moe_quantize_mxfp8", "moe_workspace_size_mxfp8",
-            "moe_grouped_ffn_mxfp8", "moe_layer_forward_mxfp8", "moe_layer_forward_noalloc")
+            "moe_grouped_ffn_mxfp8", "moe_layer_forward_mxfp8", "moe_layer_forward_noalloc",
+            "moe_ep_dispatch_layout", "moe_ep_combine", "moe_convert_bf16_to_f16")
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -35,7 +36,7 @@ class MoeShape(ctypes.Structure):
                 ("num_groups", ctypes.c_int32), ("topk_groups", ctypes.c_int32),
                 ("group_topn", ctypes.c_int32), ("capacity_factor", ctypes.c_float),
                 ("shared_intermediate", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
-                ("out_dtype", ctypes.c_int32)]
+                ("out_dtype", ctypes.c_int32), ("down_dtype", ctypes.c_int32)]
 
 
 MOE_STAGES = ("router", "route", "dispatch", "gather", "gate_up", "down", "shared", "combine")
@@ -47,7 +48,8 @@ class MoeDebug(ctypes.Structure):
                 ("expert_offsets", ctypes.c_void_p), ("row_of_slot", ctypes.c_void_p),
                 ("num_dropped", ctypes.c_void_p),
                 ("stage_start", ctypes.c_void_p * len(MOE_STAGES)),
-                ("stage_stop", ctypes.c_void_p * len(MOE_STAGES))]
+                ("stage_stop", ctypes.c_void_p * len(MOE_STAGES)),
+                ("row_token", ctypes.c_void_p)]
 
 
 class MoeMxfp8Ffn(ctypes.Structure):
@@ -87,6 +89,8 @@ def lib():
                                         ctypes.POINTER(MoeDebug), vp, sz, vp]
         L.moe_layer_forward_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                 ctypes.POINTER(MoeDebug), vp]
+        L.moe_ep_dispatch_layout.argtypes = [sp, ctypes.c_int32] + [vp] * 11 + [sz, vp]
+        L.moe_ep_combine.argtypes = [sp, ctypes.c_int32, vp, vp, vp, vp, vp]
         L.moe_group_score_sigmoid.argtypes = [vp, vp, ctypes.c_int64, vp]
         L.moe_status_string.argtypes = [st]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -94,6 +98,7 @@ def lib():
         L.moe_read_device_flags.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
         i32, mp = ctypes.c_int32, ctypes.POINTER(MoeMxfp8Ffn)
         L.moe_quantize_mxfp8.argtypes = [i32, i32, i32, vp, i32, vp, vp, vp]
+        L.moe_convert_bf16_to_f16.argtypes = [ctypes.c_int64, vp, vp, vp]
         L.moe_workspace_size_mxfp8.argtypes = [sp, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_grouped_ffn_mxfp8.argtypes = [sp, vp, vp, i32, vp, mp, vp, vp, sz, vp]
         L.moe_layer_forward_mxfp8.argtypes = [sp, vp, vp, vp, vp, mp, mp, vp, ctypes.POINTER(MoeDebug), vp,
@@ -109,7 +114,7 @@ def make_shape(cfg=None, **kw) -> MoeShape:
     """A moe_shape from a workloads.LayerConfig and/or keyword overrides."""
     d = dict(num_tokens=0, hidden=0, num_experts=0, intermediate=0, top_k=1, score=0, renormalize=1,
              routed_scale=1.0, num_groups=1, topk_groups=1, group_topn=0, capacity_factor=0.0,
-             shared_intermediate=0, act_dtype=MOE_BF16, out_dtype=MOE_F32)
+             shared_intermediate=0, act_dtype=MOE_BF16, out_dtype=MOE_F32, down_dtype=0)
     if cfg is not None:
         d.update(num_tokens=cfg.tokens, hidden=cfg.hidden, num_experts=cfg.experts,
                  intermediate=cfg.inter, top_k=cfg.top_k, score=cfg.score, renormalize=cfg.renormalize,
@@ -212,6 +217,20 @@ def moe_layer_forward_noalloc(shape, x, w_router, router_bias, k_per_token, w_ga
            "moe_layer_forward_noalloc")
 
 
+def moe_ep_dispatch_layout(shape, num_ranks, topk_ids, topk_gates, x, rank_counts, rank_offsets, send_token,
+                           send_ids, send_gates, slot_send_pos, send_x, ws, ws_bytes=None, stream=None):
+    _check(lib().moe_ep_dispatch_layout(ctypes.byref(shape), int(num_ranks), _ptr(topk_ids), _ptr(topk_gates),
+                                        _ptr(x), _ptr(rank_counts), _ptr(rank_offsets), _ptr(send_token),
+                                        _ptr(send_ids), _ptr(send_gates), _ptr(slot_send_pos), _ptr(send_x),
+                                        _ptr(ws), ws.numel() if ws_bytes is None else ws_bytes, _stream(stream)),
+           "moe_ep_dispatch_layout")
+
+
+def moe_ep_combine(shape, num_ranks, partial, slot_send_pos, y_shared, out, stream=None):
+    _check(lib().moe_ep_combine(ctypes.byref(shape), int(num_ranks), _ptr(partial), _ptr(slot_send_pos),
+                                _ptr(y_shared), _ptr(out), _stream(stream)), "moe_ep_combine")
+
+
 def moe_group_score_sigmoid(x, y, n=None, stream=None):
     _check(lib().moe_group_score_sigmoid(_ptr(x), _ptr(y), x.numel() if n is None else n, _stream(stream)),
            "moe_group_score_sigmoid")
@@ -236,6 +255,20 @@ def moe_last_hip_error() -> int:
 def moe_quantize_mxfp8(rows, cols, src_dtype, src, scale_stride, codes, scales, stream=None):
     _check(lib().moe_quantize_mxfp8(int(rows), int(cols), int(src_dtype), _ptr(src), int(scale_stride),
                                     _ptr(codes), _ptr(scales), _stream(stream)), "moe_quantize_mxfp8")
+
+
+def moe_convert_bf16_to_f16(n, src, dst, stream=None):
+    _check(lib().moe_convert_bf16_to_f16(int(n), _ptr(src), _ptr(dst), _stream(stream)), "moe_convert_bf16_to_f16")
+
+
+def to_f16_weights(w, stream=None):
+    """fp16 copy (a float16 tensor) of a bf16 device weight tensor, made by the
+    library's conversion, for shapes with down_dtype = MOE_F16."""
+    import torch
+    assert w.dtype == torch.bfloat16
+    out = torch.empty(w.shape, dtype=torch.float16, device=w.device)
+    moe_convert_bf16_to_f16(w.numel(), w.contiguous(), out, stream)
+    return out
 
 
 def mx_scale_bytes(rows: int, cols: int, stride: Optional[int] = None) -> int:

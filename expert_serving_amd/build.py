@@ -25,7 +25,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["moe_api.hip", "router.hip", "route.hip", "dispatch.hip", "gemm.hip", "combine.hip",
-           "mxfp8.hip"]
+           "mxfp8.hip", "ep.hip"]
 PEAKS_SRC = "peaks.hip"
 PEAKS_BIN = os.path.join(HERE, "moe_peaks")
 NO_CONTRACT = {"route.hip"}

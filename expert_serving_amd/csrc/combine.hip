@@ -17,6 +17,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (b + (((b >> 16) & 1u) + 0x7FFFu)) >> 16;
 }
 
+// Four fp16 values (8 bytes) widened to fp32.
+__device__ __forceinline__ f32x4 load_h4(const void* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  const auto lo = __builtin_bit_cast(_Float16 __attribute__((ext_vector_type(2))), w.x);
+  const auto hi = __builtin_bit_cast(_Float16 __attribute__((ext_vector_type(2))), w.y);
+  return f32x4{(float)lo[0], (float)lo[1], (float)hi[0], (float)hi[1]};
+}
+
 // One block per token (and column slice: a small batch splits the columns
 // over gridDim.y blocks so that more compute units share the reads); thread
 // i owns 4 consecutive columns per pass.  KM is
@@ -24,13 +32,18 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 // token's rows are issued before the first multiply-add waits on them.  y may
 // come in `parts` partial sums (a K-split down projection), each `part_stride`
 // floats apart; they are added in part order before the gate multiplies.
-template <bool OUT_BF16, int KM>
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, int parts,
+// YH: y and y_shared hold fp16 values (one part), widened exactly to fp32.
+template <bool OUT_BF16, int KM, bool YH>
+__global__ __launch_bounds__(256) void k_combine(const void* __restrict__ yv, int parts,
                                                  long long part_stride,
                                                  const int32_t* __restrict__ row_of_slot,
                                                  const float* __restrict__ gates,
-                                                 const float* __restrict__ y_shared, int H,
+                                                 const void* __restrict__ ysv, int H,
                                                  int k_max, void* __restrict__ out) {
+  const float* y = static_cast<const float*>(yv);
+  const float* y_shared = static_cast<const float*>(ysv);
+  const uint16_t* yh = static_cast<const uint16_t*>(yv);
+  const uint16_t* ysh = static_cast<const uint16_t*>(ysv);
   const int t = blockIdx.x;
   __shared__ int s_row[KM];
   __shared__ float s_g[KM];
@@ -47,9 +60,13 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, in
       const int r = s_row[j];
       v[j] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (r >= 0) {
-        v[j] = *reinterpret_cast<const f32x4*>(y + (size_t)r * H + c);
-        for (int p = 1; p < parts; ++p)
-          v[j] += *reinterpret_cast<const f32x4*>(y + p * part_stride + (size_t)r * H + c);
+        if constexpr (YH) {
+          v[j] = load_h4(yh + (size_t)r * H + c);
+        } else {
+          v[j] = *reinterpret_cast<const f32x4*>(y + (size_t)r * H + c);
+          for (int p = 1; p < parts; ++p)
+            v[j] += *reinterpret_cast<const f32x4*>(y + p * part_stride + (size_t)r * H + c);
+        }
       }
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -62,9 +79,9 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, in
       acc[2] = fmaf(g, v[j][2], acc[2]);
       acc[3] = fmaf(g, v[j][3], acc[3]);
     }
-    if (y_shared) {
-      const f32x4 w = *reinterpret_cast<const f32x4*>(y_shared + (size_t)t * H + c);
-      acc += w;
+    if (ysv) {
+      if constexpr (YH) acc += load_h4(ysh + (size_t)t * H + c);
+      else acc += *reinterpret_cast<const f32x4*>(y_shared + (size_t)t * H + c);
     }
     if constexpr (OUT_BF16) {
       uint2 pk;
@@ -77,34 +94,45 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, in
   }
 }
 
-template <int KM>
-hipError_t launch_combine_k(const moe_shape& s, const float* y, int parts, long long part_stride,
-                            const int32_t* row_of_slot, const float* gates, const float* y_shared,
+template <int KM, bool YH>
+hipError_t launch_combine_k(const moe_shape& s, const void* y, int parts, long long part_stride,
+                            const int32_t* row_of_slot, const float* gates, const void* y_shared,
                             void* out, hipStream_t st) {
   // fewer than 512 tokens: up to one block per 1024 columns of a token
   const int ysplit = s.num_tokens < 512 ? std::max(1, s.hidden / 1024) : 1;
   const dim3 grid(s.num_tokens, ysplit);
   if (s.out_dtype == MOE_BF16)
-    hipLaunchKernelGGL((k_combine<true, KM>), grid, dim3(256), 0, st, y, parts, part_stride, row_of_slot,
+    hipLaunchKernelGGL((k_combine<true, KM, YH>), grid, dim3(256), 0, st, y, parts, part_stride, row_of_slot,
                        gates, y_shared, s.hidden, s.top_k, out);
   else
-    hipLaunchKernelGGL((k_combine<false, KM>), grid, dim3(256), 0, st, y, parts, part_stride, row_of_slot,
+    hipLaunchKernelGGL((k_combine<false, KM, YH>), grid, dim3(256), 0, st, y, parts, part_stride, row_of_slot,
                        gates, y_shared, s.hidden, s.top_k, out);
   return hipGetLastError();
 }
 
+template <bool YH>
+hipError_t launch_combine_y(const moe_shape& s, const void* y_perm, const int32_t* row_of_slot,
+                            const float* gates, const void* y_shared, void* out, hipStream_t st, int parts,
+                            long long part_stride) {
+  if (s.top_k <= 2)
+    return launch_combine_k<2, YH>(s, y_perm, parts, part_stride, row_of_slot, gates, y_shared, out, st);
+  if (s.top_k <= 4)
+    return launch_combine_k<4, YH>(s, y_perm, parts, part_stride, row_of_slot, gates, y_shared, out, st);
+  if (s.top_k <= 8)
+    return launch_combine_k<8, YH>(s, y_perm, parts, part_stride, row_of_slot, gates, y_shared, out, st);
+  return launch_combine_k<kMaxTopK, YH>(s, y_perm, parts, part_stride, row_of_slot, gates, y_shared, out, st);
+}
+
 }  // namespace
 
-hipError_t launch_combine(const moe_shape& s, const float* y_perm, const int32_t* row_of_slot,
-                          const float* gates, const float* y_shared, void* out, hipStream_t st,
-                          int parts, long long part_stride) {
-  if (s.top_k <= 2)
-    return launch_combine_k<2>(s, y_perm, parts, part_stride, row_of_slot, gates, y_shared, out, st);
-  if (s.top_k <= 4)
-    return launch_combine_k<4>(s, y_perm, parts, part_stride, row_of_slot, gates, y_shared, out, st);
-  if (s.top_k <= 8)
-    return launch_combine_k<8>(s, y_perm, parts, part_stride, row_of_slot, gates, y_shared, out, st);
-  return launch_combine_k<kMaxTopK>(s, y_perm, parts, part_stride, row_of_slot, gates, y_shared, out, st);
+hipError_t launch_combine(const moe_shape& s, const void* y_perm, const int32_t* row_of_slot,
+                          const float* gates, const void* y_shared, void* out, hipStream_t st,
+                          int parts, long long part_stride, bool y_half) {
+  if (y_half) {
+    if (parts != 1) return hipErrorInvalidValue;
+    return launch_combine_y<true>(s, y_perm, row_of_slot, gates, y_shared, out, st, 1, 0);
+  }
+  return launch_combine_y<false>(s, y_perm, row_of_slot, gates, y_shared, out, st, parts, part_stride);
 }
 
 }  // namespace moe

@@ -149,8 +149,11 @@ __device__ __forceinline__ bool block_tile2(int real0, int real1, int& cls, int&
 //   kGateUpPart: as kGateUp on one K range of a split K, without SwiGLU: the
 //            fp32 partial sums A.B0^T at Out and A.B1^T at Out + up_off
 //   kGateUpMXPart: the same on MXFP8 operands
+//   kDownW16: kDown with the down weights already fp16 (converted once, ahead
+//            of the layer calls, by the same conversion kDown applies)
 enum GemmMode {
-  kGateUp = 0, kDown = 1, kPlain = 2, kGateUpMX = 3, kDownMX = 4, kGateUpPart = 5, kGateUpMXPart = 6
+  kGateUp = 0, kDown = 1, kPlain = 2, kGateUpMX = 3, kDownMX = 4, kGateUpPart = 5, kGateUpMXPart = 6,
+  kDownW16 = 7
 };
 
 // modes that multiply by both the gate and the up weights
@@ -222,7 +225,7 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
 
 template <int MODE>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
-  if constexpr (MODE == kDown)
+  if constexpr (MODE == kDown || MODE == kDownW16)
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                    __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   else
@@ -282,7 +285,7 @@ __device__ __forceinline__ void gemm_tile(
     int lda, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, long long strideB,
     int N, int K, void* __restrict__ Out, int ldo, const float* __restrict__ bias,
     const MTile* __restrict__ sched, int static_rows, uint32_t* __restrict__ flags, const MxArgs mx,
-    int mi, int ni, int kst0, int kstn, long long up_off = 0) {
+    int mi, int ni, int kst0, int kstn, long long up_off = 0, bool out_half = false) {
   constexpr bool DUAL = gemm_dual(MODE);
   constexpr bool MX = gemm_mx(MODE);
   constexpr int WAVES_M = BM >= 64 ? 2 : 1, WAVES_N = NW / WAVES_M;
@@ -293,8 +296,9 @@ __device__ __forceinline__ void gemm_tile(
   // 8-wave blocks: register-staged ping-pong over two LDS stages; 4-wave
   // blocks: direct-to-LDS loads over an NS-stage ring
   constexpr bool PING = NW == 8;
-  // down weights are converted to fp16 once when staged through registers
-  // (8-wave blocks), else on every fragment read
+  // bf16 down weights are converted to fp16 once when staged through
+  // registers (8-wave blocks), else on every fragment read; kDownW16 weights
+  // arrive as fp16
   constexpr bool CVT_ON_READ = MODE == kDown && !PING;
   static_assert(BM % 32 == 0 && BNB % 32 == 0 && FM >= 1 && FN >= 1, "tile shape");
   static_assert(!PING || NS == 2, "ping-pong uses two LDS stages");
@@ -835,6 +839,17 @@ __device__ __forceinline__ void gemm_tile(
         for (int ob = 0; ob < (gemm_part(MODE) ? 2 : 1); ++ob) {
           const f32x16 acc = ob ? acc1[DUAL ? a : 0][DUAL ? b : 0] : acc0[a][b];
           f32x4 v = {acc[4 * qi], acc[4 * qi + 1], acc[4 * qi + 2], acc[4 * qi + 3]};
+          if (out_half) {
+            // fp16 outputs (a layer's down projection; N is a multiple of 64
+            // and n of 4, so a run of four is all in or all out)
+            if (n >= N) continue;
+            overflow |= !(fabsf(v[0]) <= 65504.f && fabsf(v[1]) <= 65504.f && fabsf(v[2]) <= 65504.f &&
+                          fabsf(v[3]) <= 65504.f);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Out) + o) =
+                uint2{f32_to_f16_bits(v[0]) | (f32_to_f16_bits(v[1]) << 16),
+                      f32_to_f16_bits(v[2]) | (f32_to_f16_bits(v[3]) << 16)};
+            continue;
+          }
           float* dst = static_cast<float*>(Out) + o + (ob ? up_off : 0);
           if (n + 3 < N && (ldo & 3) == 0) {
             if (bias) {
@@ -854,9 +869,7 @@ __device__ __forceinline__ void gemm_tile(
     }
   }
   }
-  if constexpr (DUAL) {
-    if (overflow && flags) atomicOr(flags, (uint32_t)MOE_FLAG_H_RANGE);
-  }
+  if (overflow && flags) atomicOr(flags, DUAL ? (uint32_t)MOE_FLAG_H_RANGE : (uint32_t)MOE_FLAG_Y_RANGE);
 }
 
 // One row-tile class per launch: block -> (row tile, column tile) by block_tile.
@@ -870,7 +883,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
     const uint16_t* __restrict__ B1, long long strideB, int N, int K, void* __restrict__ Out,
     int ldo, const float* __restrict__ bias, const MTile* __restrict__ sched,
     const int32_t* __restrict__ count, int mslots, int ntiles, int static_rows,
-    uint32_t* __restrict__ flags, const MxArgs mx, int ksplit, long long part_elems) {
+    uint32_t* __restrict__ flags, const MxArgs mx, int ksplit, long long part_elems, int out_half) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   int mi, nn;
   const int mtiles = sched ? min(*count, mslots) : (static_rows + BM - 1) / BM;
@@ -884,7 +897,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_mfma(
   }
   gemm_tile<BM, BNB, MODE, NS, NW>(smem, A, a_rows, lda, B0, B1, strideB, N, K, Out, ldo, bias, sched,
                                    static_rows, flags, mx, mi, ni, kst0, kst1 - kst0,
-                                   gemm_part(MODE) ? ksplit * part_elems : 0);
+                                   gemm_part(MODE) ? ksplit * part_elems : 0, out_half != 0);
 }
 
 // Both row-tile classes of a skewed layer in one launch (8-wave blocks): the
@@ -902,7 +915,7 @@ __global__ __launch_bounds__(512) void k_gemm_mfma2(
     int K, void* __restrict__ Out, int ldo, uint32_t* __restrict__ flags, const MxArgs mx,
     const MTile* __restrict__ sched1, const int32_t* __restrict__ count1, int mslots1,
     int ntiles1, const MTile* __restrict__ sched2, const int32_t* __restrict__ count2,
-    int mslots2, int ntiles2, int ksplit, long long part_elems) {
+    int mslots2, int ntiles2, int ksplit, long long part_elems, int out_half) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const int m1 = min(*count1, mslots1), m2 = min(*count2, mslots2);
   int cls, idx, mi, nn;
@@ -915,10 +928,10 @@ __global__ __launch_bounds__(512) void k_gemm_mfma2(
   if (part) Out = static_cast<float*>(Out) + part * part_elems;
   if (cls == 0) {
     gemm_tile<BM1, BNB1, MODE, 2, 8>(smem, A, a_rows, lda, B0, B1, strideB, N, K, Out, ldo, nullptr,
-                                     sched1, 0, flags, mx, mi, ni, kst0, kst1 - kst0);
+                                     sched1, 0, flags, mx, mi, ni, kst0, kst1 - kst0, 0, out_half != 0);
   } else {
     gemm_tile<BM2, BNB2, MODE, 2, 8>(smem, A, a_rows, lda, B0, B1, strideB, N, K, Out, ldo, nullptr,
-                                     sched2, 0, flags, mx, mi, ni, kst0, kst1 - kst0);
+                                     sched2, 0, flags, mx, mi, ni, kst0, kst1 - kst0, 0, out_half != 0);
   }
 }
 
@@ -1090,7 +1103,7 @@ hipError_t launch_mfma(const void* A, const int32_t* a_rows, int lda, const void
                        void* out, int ldo, const float* bias, const MTile* sched,
                        const int32_t* count, int mslots, int static_rows, uint32_t* flags,
                        hipStream_t st, const MxArgs mx = MxArgs{}, int ksplit = 1,
-                       long long part_elems = 0) {
+                       long long part_elems = 0, bool out_half = false) {
   constexpr int lds = gemm_lds_bytes(BM, BNB, MODE, NS, NW);
   static_assert(lds <= 160 * 1024, "LDS");
   if constexpr (lds > 65536) {
@@ -1114,7 +1127,7 @@ hipError_t launch_mfma(const void* A, const int32_t* a_rows, int lda, const void
                      static_cast<const uint16_t*>(A), a_rows, lda,
                      static_cast<const uint16_t*>(B0), static_cast<const uint16_t*>(B1),
                      (long long)N * K, N, K, out, ldo, bias,
-                     sched, count, mslots, ntiles, static_rows, flags, mx, ksplit, part_elems);
+                     sched, count, mslots, ntiles, static_rows, flags, mx, ksplit, part_elems, out_half ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -1147,7 +1160,7 @@ hipError_t launch_mfma2(const void* A, const int32_t* a_rows, int lda, const voi
                         int N, int K, void* out, int ldo, uint32_t* flags, const MTile* s1,
                         const int32_t* c1, int ms1, const MTile* s2, const int32_t* c2, int ms2,
                         hipStream_t st, const MxArgs mx = MxArgs{}, int ksplit = 1,
-                        long long part_elems = 0) {
+                        long long part_elems = 0, bool out_half = false) {
   constexpr int l1 = gemm_lds_bytes(BM1, BNB1, MODE, 2, 8), l2 = gemm_lds_bytes(BM2, BNB2, MODE, 2, 8);
   constexpr int lds = l1 > l2 ? l1 : l2;
   static_assert(lds <= 160 * 1024, "LDS");
@@ -1160,7 +1173,7 @@ hipError_t launch_mfma2(const void* A, const int32_t* a_rows, int lda, const voi
   hipLaunchKernelGGL((k_gemm_mfma2<BM1, BNB1, BM2, BNB2, MODE>), grid, dim3(512), lds, st,
                      static_cast<const uint16_t*>(A), a_rows, lda, static_cast<const uint16_t*>(B0),
                      static_cast<const uint16_t*>(B1), (long long)N * K, N, K, out, ldo, flags, mx, s1, c1,
-                     ms1, nt1, s2, c2, ms2, nt2, ksplit, part_elems);
+                     ms1, nt1, s2, c2, ms2, nt2, ksplit, part_elems, out_half ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -1224,11 +1237,66 @@ hipError_t launch_swiglu_parts(const float* parts, int nparts, long long part_el
   return hipGetLastError();
 }
 
+namespace {
+// The down projection on fp16 weights: the tile configurations of kDown.
+hipError_t launch_down_w16(int bm, const void* A, int lda, const void* B, int N, int K, void* Y, int ldy,
+                           const MTile* sched, const int32_t* count, int mslots, int static_rows, hipStream_t st,
+                           int ksplit, long long part_elems, bool y_half, uint32_t* flags) {
+  if (bm == 256)
+    return launch_mfma<256, 256, kDownW16, 2, 8>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
+                                                 mslots, static_rows, flags, st, MxArgs{}, ksplit, part_elems,
+                                                 y_half);
+  if (bm == 128)
+    return launch_mfma<128, 128, kDownW16, 2, 8>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
+                                                 mslots, static_rows, flags, st, MxArgs{}, ksplit, part_elems,
+                                                 y_half);
+  if (bm != 32) return hipErrorInvalidValue;
+  if (K >= kDown8MinK)
+    return launch_mfma<32, 256, kDownW16, 2, 8>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
+                                                mslots, static_rows, flags, st, MxArgs{}, ksplit, part_elems,
+                                                y_half);
+  if ((long long)mslots * ((N + 127) / 128) <= 1024)
+    return launch_mfma<32, 128, kDownW16, 6, 4>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
+                                                mslots, static_rows, flags, st, MxArgs{}, ksplit, part_elems,
+                                                y_half);
+  return launch_mfma<32, 128, kDownW16, 4, 4>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
+                                              mslots, static_rows, flags, st, MxArgs{}, ksplit, part_elems, y_half);
+}
+
+// bf16 -> fp16 of n elements, with the conversion kDown applies to its
+// weights while staging them (so a layer on converted weights computes the
+// same products); eight elements per thread, the tail one by one.
+__global__ __launch_bounds__(256) void k_bf16_to_f16(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                                     long long n) {
+  const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i + 8 <= n) {
+    *reinterpret_cast<u32x4*>(dst + i) = bf16x8_to_f16x8(*reinterpret_cast<const u32x4*>(src + i));
+  } else {
+    for (long long j = i; j < n; ++j) {
+      const uint32_t w = bf16x2_to_f16x2((uint32_t)src[j]);
+      dst[j] = (uint16_t)(w & 0xFFFFu);
+    }
+  }
+}
+}  // namespace
+
+hipError_t launch_bf16_to_f16(const void* src, void* dst, long long n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const long long blocks = (n + 2047) / 2048;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_bf16_to_f16, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<const uint16_t*>(src),
+                     static_cast<uint16_t*>(dst), n);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int lda,
-                             const void* B, int N, int K, const float* bias, float* Y, int ldy,
+                             const void* B, int N, int K, const float* bias, void* Y, int ldy,
                              const MTile* sched, const int32_t* count, int max_tiles,
-                             int static_rows, hipStream_t st, int ksplit, long long part_elems) {
+                             int static_rows, hipStream_t st, int ksplit, long long part_elems,
+                             bool y_half, uint32_t* flags, bool w16) {
   const long long strideB = (long long)N * K;
+  if (y_half && (dtype != MOE_BF16 || !a_is_h || ksplit != 1 || bias)) return hipErrorInvalidValue;
+  if (w16 && (dtype != MOE_BF16 || !a_is_h)) return hipErrorInvalidValue;
   if (dtype == MOE_F32) {
     if (ksplit > 1) return hipErrorInvalidValue;  // the fp32 kernel does not split K
     const int mslots = sched ? max_tiles : (static_rows + 31) / 32;
@@ -1236,34 +1304,38 @@ hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int 
     if (mslots == 0) return hipSuccess;
     hipLaunchKernelGGL(k_gemm_f32<false>, dim3(grid_for(mslots, ntiles)), dim3(256), 0, st,
                        static_cast<const float*>(A), nullptr, lda, static_cast<const float*>(B), nullptr,
-                       strideB, N, K, Y, ldy, bias, sched, count, mslots, ntiles, static_rows);
+                       strideB, N, K, static_cast<float*>(Y), ldy, bias, sched, count, mslots, ntiles,
+                       static_rows);
     return hipGetLastError();
   }
   const int mslots = sched ? max_tiles : (static_rows + bm - 1) / bm;
   if (mslots == 0) return hipSuccess;
+  if (a_is_h && w16)
+    return launch_down_w16(bm, A, lda, B, N, K, Y, ldy, sched, count, mslots, static_rows, st, ksplit, part_elems,
+                           y_half, flags);
   if (a_is_h) {
     if (bm == 256)
       return launch_mfma<256, 256, kDown, 2, 8>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
-                                          mslots, static_rows, nullptr, st, MxArgs{}, ksplit, part_elems);
+                                          mslots, static_rows, flags, st, MxArgs{}, ksplit, part_elems, y_half);
     if (bm == 128)
       return launch_mfma<128, 128, kDown, 2, 8>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
-                                          mslots, static_rows, nullptr, st, MxArgs{}, ksplit, part_elems);
+                                          mslots, static_rows, flags, st, MxArgs{}, ksplit, part_elems, y_half);
     if (bm != 32) return hipErrorInvalidValue;
     // K of at least 2048: 8-wave 32 x 256 blocks, as for gate/up (Mixtral-
     // shaped decode down 0.181 -> 0.139 ms); shorter K keeps the 4-wave
     // 32 x 128 blocks (I = 768: 0.025 against 0.030 ms)
     if (K >= kDown8MinK)
       return launch_mfma<32, 256, kDown, 2, 8>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sched,
-                                               count, mslots, static_rows, nullptr, st, MxArgs{}, ksplit,
-                                               part_elems);
+                                               count, mslots, static_rows, flags, st, MxArgs{}, ksplit,
+                                               part_elems, y_half);
     // few blocks (decode-sized layers): a deeper ring keeps more weight bytes
     // in flight per compute unit
     if ((long long)mslots * ((N + 127) / 128) <= 1024)
       return launch_mfma<32, 128, kDown, 6, 4>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sched,
-                                               count, mslots, static_rows, nullptr, st, MxArgs{}, ksplit,
-                                               part_elems);
+                                               count, mslots, static_rows, flags, st, MxArgs{}, ksplit,
+                                               part_elems, y_half);
     return launch_mfma<32, 128, kDown, 4, 4>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sched, count,
-                                       mslots, static_rows, nullptr, st, MxArgs{}, ksplit, part_elems);
+                                       mslots, static_rows, flags, st, MxArgs{}, ksplit, part_elems, y_half);
   }
   if (bm == 128)
     return launch_mfma<128, 128, kPlain, 2, 8>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, bias, sched, count,
@@ -1330,23 +1402,24 @@ hipError_t launch_swiglu_parts_mx(const float* parts, int nparts, long long part
 // Y fp32 [rows][ldy].
 hipError_t launch_gemm_down_mx(int bm, const void* A, const uint8_t* hsc, int hs_stride,
                                const void* B, const uint8_t* sb, int sb_stride, int N, int K,
-                               float* Y, int ldy, const MTile* sched, const int32_t* count,
+                               void* Y, int ldy, const MTile* sched, const int32_t* count,
                                int max_tiles, int static_rows, hipStream_t st, int ksplit,
-                               long long part_elems) {
+                               long long part_elems, bool y_half, uint32_t* flags) {
   const int mslots = sched ? max_tiles : (static_rows + bm - 1) / bm;
   if (mslots == 0) return hipSuccess;
+  if (y_half && ksplit != 1) return hipErrorInvalidValue;
   const MxArgs mx{hsc, sb, nullptr, nullptr, hs_stride, sb_stride, 0};
   const int K2 = K / 2;
   if (bm == 256)
     return launch_mfma<256, 256, kDownMX, 2, 8>(A, nullptr, K2, B, nullptr, N, K2, Y, ldy, nullptr,
-                                                sched, count, mslots, static_rows, nullptr, st, mx);
+                                                sched, count, mslots, static_rows, flags, st, mx, 1, 0, y_half);
   if (bm == 128)
     return launch_mfma<128, 128, kDownMX, 2, 8>(A, nullptr, K2, B, nullptr, N, K2, Y, ldy, nullptr,
-                                                sched, count, mslots, static_rows, nullptr, st, mx);
+                                                sched, count, mslots, static_rows, flags, st, mx, 1, 0, y_half);
   if (bm != 32) return hipErrorInvalidValue;
   return launch_mfma<32, 256, kDownMX, 2, 8>(A, nullptr, K2, B, nullptr, N, K2, Y, ldy, nullptr,
-                                             sched, count, mslots, static_rows, nullptr, st, mx, ksplit,
-                                             part_elems);
+                                             sched, count, mslots, static_rows, flags, st, mx, ksplit,
+                                             part_elems, y_half);
 }
 
 // Both row-tile classes of a layer in one launch (big: 256-row tiles,
@@ -1359,12 +1432,17 @@ hipError_t launch_gemm_gateup2(const void* A, const int32_t* a_rows, int lda, co
                                                   ss, cs, ms, st);
 }
 
-hipError_t launch_gemm_down2(const void* A, int lda, const void* B, int N, int K, float* Y, int ldy,
+hipError_t launch_gemm_down2(const void* A, int lda, const void* B, int N, int K, void* Y, int ldy,
                              const MTile* sb, const int32_t* cb, int mb, const MTile* ss,
                              const int32_t* cs, int ms, hipStream_t st, int ksplit,
-                             long long part_elems) {
-  return launch_mfma2<256, 256, kMergedSmallRows, 256, kDown>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, nullptr, sb, cb,
-                                                mb, ss, cs, ms, st, MxArgs{}, ksplit, part_elems);
+                             long long part_elems, bool y_half, uint32_t* flags, bool w16) {
+  if (y_half && ksplit != 1) return hipErrorInvalidValue;
+  if (w16)
+    return launch_mfma2<256, 256, kMergedSmallRows, 256, kDownW16>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, flags,
+                                                                   sb, cb, mb, ss, cs, ms, st, MxArgs{}, ksplit,
+                                                                   part_elems, y_half);
+  return launch_mfma2<256, 256, kMergedSmallRows, 256, kDown>(A, nullptr, lda, B, nullptr, N, K, Y, ldy, flags, sb, cb,
+                                                mb, ss, cs, ms, st, MxArgs{}, ksplit, part_elems, y_half);
 }
 
 hipError_t launch_gemm_gateup_mx2(const void* A, const int32_t* a_rows, const uint8_t* sa, int sa_stride,
@@ -1379,13 +1457,14 @@ hipError_t launch_gemm_gateup_mx2(const void* A, const int32_t* a_rows, const ui
 }
 
 hipError_t launch_gemm_down_mx2(const void* A, const uint8_t* hsc, int hs_stride, const void* B,
-                                const uint8_t* sb_w, int sb_stride, int N, int K, float* Y, int ldy,
+                                const uint8_t* sb_w, int sb_stride, int N, int K, void* Y, int ldy,
                                 const MTile* sb, const int32_t* cb, int mb, const MTile* ss,
                                 const int32_t* cs, int ms, hipStream_t st, int ksplit,
-                                long long part_elems) {
+                                long long part_elems, bool y_half, uint32_t* flags) {
+  if (y_half && ksplit != 1) return hipErrorInvalidValue;
   const MxArgs mx{hsc, sb_w, nullptr, nullptr, hs_stride, sb_stride, 0};
-  return launch_mfma2<256, 256, kMergedSmallRows, 256, kDownMX>(A, nullptr, K / 2, B, nullptr, N, K / 2, Y, ldy, nullptr, sb,
-                                                  cb, mb, ss, cs, ms, st, mx, ksplit, part_elems);
+  return launch_mfma2<256, 256, kMergedSmallRows, 256, kDownMX>(A, nullptr, K / 2, B, nullptr, N, K / 2, Y, ldy, flags, sb,
+                                                  cb, mb, ss, cs, ms, st, mx, ksplit, part_elems, y_half);
 }
 
 }  // namespace moe

@@ -35,6 +35,9 @@ moe_status check_shape(const moe_shape* s) {
     return MOE_ERR_INVALID_ARG;
   if (s->act_dtype != MOE_F32 && s->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (s->out_dtype != MOE_F32 && s->out_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (s->down_dtype != 0 && s->down_dtype != s->act_dtype && s->down_dtype != MOE_F16)
+    return MOE_ERR_INVALID_ARG;
+  if (s->down_dtype == MOE_F16 && s->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (s->shared_intermediate < 0) return MOE_ERR_INVALID_ARG;
   if (s->num_groups < 1) return MOE_ERR_INVALID_ARG;
   if (s->num_groups > 1) {
@@ -88,7 +91,7 @@ inline moe_status opt4(const void* p) { return p ? need4(p) : MOE_OK; }
 // MXFP8 layers: bf16 x and router, 128-column groups along every K
 moe_status check_mx_shape(const moe_shape* s) {
   MOE_TRY(check_shape(s));
-  if (s->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (s->act_dtype != MOE_BF16 || s->down_dtype == MOE_F16) return MOE_ERR_UNSUPPORTED;
   if (s->hidden % 128 || s->intermediate % 128 || s->shared_intermediate % 128)
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
@@ -316,6 +319,7 @@ WsLayout plan_workspace(const moe_shape& s, bool mx) {
   w.ys = take(Is ? T * H * 4 : 0);
   w.gu_parts = take(std::max(w.ks_gu > 1 ? 2 * (size_t)w.ks_gu * slots * I * 4 : 0,
                              w.ks_gus > 1 ? 2 * (size_t)w.ks_gus * T * Is * 4 : 0));
+  w.ep_tile_counts = take((size_t)ep_tiles((int)T) * kMaxRanks * 4);
   if (mx) {
     w.xq = take(T * H);
     w.xsc = take(T * H / 32);
@@ -361,11 +365,12 @@ moe_status run_router(const moe_shape& s, const void* x, const void* w_router, c
 }
 
 // a_rows (nullable): rows of x_perm are x[a_rows[r]] (gather fused into the GEMM)
+// y_half: y is fp16 (a layer call's internal rows; ksplit must be 1)
 moe_status run_ffn(const moe_shape& s, const void* x_perm, const int32_t* a_rows,
                    const int32_t* offsets, const void* w_gate, const void* w_up,
-                   const void* w_down, float* y, void* ws,
+                   const void* w_down, void* y, void* ws,
                    const WsLayout& L, hipStream_t st, const moe_debug* dbg = nullptr,
-                   int ksplit = 1) {
+                   int ksplit = 1, bool y_half = false) {
   const GemmPlan gp = choose_gemm_plan(s);
   const int E = s.num_experts, H = s.hidden, I = s.intermediate;
   MTile* sb = at<MTile>(ws, L.sched_big);
@@ -401,17 +406,19 @@ moe_status run_ffn(const moe_shape& s, const void* x_perm, const int32_t* a_rows
   }
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATE_UP, false, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_DOWN, true, st));
+  const bool w16 = s.down_dtype == MOE_F16;
   if (merged) {
     MOE_HIP(launch_gemm_down2(h, I, w_down, H, I, y, H, sb, cnt, L.max_tiles_big, ss, cnt + 1,
-                              L.max_tiles_small, st, ksplit, (long long)s.num_tokens * s.top_k * H));
+                              L.max_tiles_small, st, ksplit, (long long)s.num_tokens * s.top_k * H, y_half,
+                              flags, w16));
   } else {
     if (gp.has_big())
       MOE_HIP(launch_gemm_plain(s.act_dtype, gp.bm_big, true, h, I, w_down, H, I, nullptr, y, H, sb,
-                                cnt, L.max_tiles_big, 0, st));
+                                cnt, L.max_tiles_big, 0, st, 1, 0, y_half, flags, w16));
     if (gp.has_small())
       MOE_HIP(launch_gemm_plain(s.act_dtype, gp.bm_small, true, h, I, w_down, H, I, nullptr, y, H,
                                 ss, cnt + 1, L.max_tiles_small, 0, st, gp.has_big() ? 1 : ksplit,
-                                (long long)s.num_tokens * s.top_k * H));
+                                (long long)s.num_tokens * s.top_k * H, y_half, flags, w16));
   }
   MOE_HIP(stage_mark(dbg, MOE_STAGE_DOWN, false, st));
   return MOE_OK;
@@ -505,7 +512,7 @@ moe_status run_shared_mx(const moe_shape& s, const void* xq, const uint8_t* xsc,
 }
 
 moe_status run_shared(const moe_shape& s, const void* x, const void* wsg, const void* wsu,
-                      const void* wsd, void* ws, const WsLayout& L, hipStream_t st) {
+                      const void* wsd, void* ws, const WsLayout& L, hipStream_t st, bool y_half = false) {
   const int T = s.num_tokens, H = s.hidden, Is = s.shared_intermediate;
   const int bm = s.act_dtype == MOE_F32 ? 32 : (T >= 2048 ? 256 : (T >= 128 ? 128 : 32));
   void* hs = at<void>(ws, L.hs);
@@ -522,7 +529,7 @@ moe_status run_shared(const moe_shape& s, const void* x, const void* wsg, const 
                                nullptr, 0, T, at<uint32_t>(ws, L.flags), st));
   }
   MOE_HIP(launch_gemm_plain(s.act_dtype, bm, true, hs, Is, wsd, H, Is, nullptr, ys, H, nullptr,
-                            nullptr, 0, T, st));
+                            nullptr, 0, T, st, 1, 0, y_half, at<uint32_t>(ws, L.flags), s.down_dtype == MOE_F16));
   return MOE_OK;
 }
 
@@ -557,6 +564,7 @@ moe_status check_layer_args(const moe_shape* shape, const void* x, const void* w
     MOE_TRY(opt4(dbg->expert_offsets));
     MOE_TRY(opt4(dbg->row_of_slot));
     MOE_TRY(opt4(dbg->num_dropped));
+    MOE_TRY(opt4(dbg->row_token));
   }
   return MOE_OK;
 }
@@ -574,8 +582,12 @@ moe_status run_layer(const moe_shape& s, const void* x, const void* w_router, co
   int32_t* ros = (dbg && dbg->row_of_slot) ? dbg->row_of_slot : at<int32_t>(ws, L.row_of_slot);
   int32_t* nd = (dbg && dbg->num_dropped) ? dbg->num_dropped : at<int32_t>(ws, L.num_dropped);
   uint32_t* flags = at<uint32_t>(ws, L.flags);
-  int32_t* row_token = at<int32_t>(ws, L.row_token);
-  float* y = at<float>(ws, L.y);
+  int32_t* row_token = (dbg && dbg->row_token) ? dbg->row_token : at<int32_t>(ws, L.row_token);
+  void* y = at<void>(ws, L.y);
+  // The expert outputs y (and the shared expert's) go to the combine as fp16
+  // in bf16 layers whose down projection is not split (half the bytes of the
+  // round trip through HBM); a split projection's partial sums stay fp32.
+  const bool y_half = s.act_dtype == MOE_BF16 && L.ksplit == 1;
 
   MOE_HIP(stage_mark(dbg, MOE_STAGE_ROUTER, true, st));
   int rparts = 1;
@@ -593,17 +605,17 @@ moe_status run_layer(const moe_shape& s, const void* x, const void* w_router, co
   // S6 gather: fused into the gate/up GEMM's tile loads (rows x[row_token[r]])
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATHER, true, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_GATHER, false, st));
-  MOE_TRY(run_ffn(s, x, row_token, offsets, w_gate, w_up, w_down, y, ws, L, st, dbg, L.ksplit));
-  const float* ys = nullptr;
+  MOE_TRY(run_ffn(s, x, row_token, offsets, w_gate, w_up, w_down, y, ws, L, st, dbg, L.ksplit, y_half));
+  const void* ys = nullptr;
   MOE_HIP(stage_mark(dbg, MOE_STAGE_SHARED, true, st));
   if (s.shared_intermediate > 0) {
-    MOE_TRY(run_shared(s, x, ws_gate, ws_up, ws_down, ws, L, st));
-    ys = at<float>(ws, L.ys);
+    MOE_TRY(run_shared(s, x, ws_gate, ws_up, ws_down, ws, L, st, y_half));
+    ys = at<void>(ws, L.ys);
   }
   MOE_HIP(stage_mark(dbg, MOE_STAGE_SHARED, false, st));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_COMBINE, true, st));
   MOE_HIP(launch_combine(s, y, ros, gates, ys, out, st, L.ksplit,
-                         (long long)s.num_tokens * s.top_k * s.hidden));
+                         (long long)s.num_tokens * s.top_k * s.hidden, y_half));
   MOE_HIP(stage_mark(dbg, MOE_STAGE_COMBINE, false, st));
   return MOE_OK;
 }
@@ -821,6 +833,65 @@ moe_status moe_layer_forward_noalloc(const moe_shape* shape, const void* x, cons
                    ws_down, out, dbg, ws, L, static_cast<hipStream_t>(stream));
 }
 
+moe_status moe_ep_dispatch_layout(const moe_shape* shape, int32_t num_ranks, const int32_t* topk_ids,
+                                  const float* topk_gates, const void* x, int32_t* rank_counts,
+                                  int32_t* rank_offsets, int32_t* send_token, int32_t* send_ids,
+                                  float* send_gates, int32_t* slot_send_pos, void* send_x, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  MOE_TRY(check_shape(shape));
+  const moe_shape& s = *shape;
+  if (num_ranks < 1) return MOE_ERR_INVALID_ARG;
+  if (num_ranks > kMaxRanks) return MOE_ERR_UNSUPPORTED;
+  if (s.num_experts % num_ranks != 0) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(need4(topk_ids));
+  MOE_TRY(need4(topk_gates));
+  MOE_TRY(need4(rank_counts));
+  MOE_TRY(need4(rank_offsets));
+  MOE_TRY(need4(send_token));
+  MOE_TRY(need4(send_ids));
+  MOE_TRY(need4(send_gates));
+  MOE_TRY(need4(slot_send_pos));
+  if ((x == nullptr) != (send_x == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (x) {
+    MOE_TRY(need(x));
+    MOE_TRY(need(send_x));
+  }
+  MOE_TRY(need(ws));
+  const WsLayout L = plan_workspace(s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (s.num_tokens == 0) return MOE_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t* flags = at<uint32_t>(ws, L.flags);
+  MOE_HIP(launch_clear_flags(flags, st));
+  MOE_HIP(launch_ep_layout(s, num_ranks, topk_ids, topk_gates, rank_counts, rank_offsets, send_token, send_ids,
+                           send_gates, slot_send_pos, at<int32_t>(ws, L.ep_tile_counts), flags, st));
+  if (x) {
+    // the payload: row p of the send buffer is x[send_token[p]] for p below
+    // rank_offsets[G] (the gather of the dispatch, over G groups of rows)
+    moe_shape g = s;
+    g.num_experts = num_ranks;
+    g.top_k = std::min(s.top_k, (int32_t)num_ranks);
+    MOE_HIP(launch_gather(g, x, send_token, rank_offsets, send_x, st));
+  }
+  return MOE_OK;
+}
+
+moe_status moe_ep_combine(const moe_shape* shape, int32_t num_ranks, const float* partial,
+                          const int32_t* slot_send_pos, const float* y_shared, void* out, void* stream) {
+  MOE_TRY(check_shape(shape));
+  const moe_shape& s = *shape;
+  if (num_ranks < 1) return MOE_ERR_INVALID_ARG;
+  if (num_ranks > kMaxRanks) return MOE_ERR_UNSUPPORTED;
+  if (s.num_experts % num_ranks != 0) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(need(partial));
+  MOE_TRY(need4(slot_send_pos));
+  if (y_shared) MOE_TRY(need(y_shared));
+  MOE_TRY(need(out));
+  if (s.num_tokens == 0) return MOE_OK;
+  MOE_HIP(launch_ep_combine(s, num_ranks, partial, slot_send_pos, y_shared, out, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
 moe_status moe_quantize_mxfp8(int32_t rows, int32_t cols, int32_t src_dtype, const void* src,
                               int32_t scale_stride, void* codes, uint8_t* scales, void* stream) {
   if (rows < 0 || cols <= 0 || scale_stride < rows) return MOE_ERR_INVALID_ARG;
@@ -832,6 +903,15 @@ moe_status moe_quantize_mxfp8(int32_t rows, int32_t cols, int32_t src_dtype, con
   if (rows == 0) return MOE_OK;
   MOE_HIP(launch_quant_mxfp8(src_dtype, src, rows, cols, scale_stride, static_cast<uint8_t*>(codes),
                              scales, nullptr, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_convert_bf16_to_f16(int64_t n, const void* src, void* dst, void* stream) {
+  if (n < 0) return MOE_ERR_INVALID_ARG;
+  if (n == 0) return MOE_OK;
+  MOE_TRY(need(src));
+  MOE_TRY(need(dst));
+  MOE_HIP(launch_bf16_to_f16(src, dst, (long long)n, static_cast<hipStream_t>(stream)));
   return MOE_OK;
 }
 
@@ -887,6 +967,7 @@ moe_status moe_layer_forward_mxfp8(const moe_shape* shape, const void* x, const 
     MOE_TRY(opt4(dbg->expert_offsets));
     MOE_TRY(opt4(dbg->row_of_slot));
     MOE_TRY(opt4(dbg->num_dropped));
+    MOE_TRY(opt4(dbg->row_token));
   }
   const WsLayout L = plan_workspace(s, true);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
@@ -902,7 +983,7 @@ moe_status moe_layer_forward_mxfp8(const moe_shape* shape, const void* x, const 
   int32_t* ros = (dbg && dbg->row_of_slot) ? dbg->row_of_slot : at<int32_t>(ws, L.row_of_slot);
   int32_t* nd = (dbg && dbg->num_dropped) ? dbg->num_dropped : at<int32_t>(ws, L.num_dropped);
   uint32_t* flags = at<uint32_t>(ws, L.flags);
-  int32_t* row_token = at<int32_t>(ws, L.row_token);
+  int32_t* row_token = (dbg && dbg->row_token) ? dbg->row_token : at<int32_t>(ws, L.row_token);
   float* y = at<float>(ws, L.y);
   uint8_t* xq = at<uint8_t>(ws, L.xq);
   uint8_t* xsc = at<uint8_t>(ws, L.xsc);

@@ -30,7 +30,7 @@ struct MTile {
 struct WsLayout {
   size_t flags, logits, logits_parts, ids, gates, counts, offsets, tile_counts, row_of_slot, row_token,
       num_dropped, sched_big, sched_small, sched_count, h, y, hs, ys, xq, xsc, xscp, hsc, hssc, gu_parts,
-      total;
+      ep_tile_counts, total;
   int n_dispatch_tiles;
   // K-split of the layer's down projection (decode-sized layers, and layers
   // with few 256-row tiles): y holds ksplit partial sums,
@@ -153,11 +153,16 @@ hipError_t launch_swiglu_parts_mx(const float* parts, int nparts, long long part
 // fp16 h of a bf16 layer (down projection), B is converted to fp16 on load.
 // ksplit > 1 (32-row down tiles): K in ksplit ranges of whole 64-element
 // stages, range p's partial sums at Y + p * part_elems.
+// y_half (down projections of a bf16 layer, ksplit 1): Y is fp16 instead of
+// fp32; values outside fp16's range set MOE_FLAG_Y_RANGE in flags.
 hipError_t launch_gemm_plain(int dtype, int bm, bool a_is_h, const void* A, int lda,
-                             const void* B, int N, int K, const float* bias, float* Y, int ldy,
+                             const void* B, int N, int K, const float* bias, void* Y, int ldy,
                              const MTile* sched, const int32_t* count, int max_tiles,
                              int static_rows, hipStream_t st,
-                             int ksplit = 1, long long part_elems = 0);
+                             int ksplit = 1, long long part_elems = 0, bool y_half = false,
+                             uint32_t* flags = nullptr, bool w16 = false);
+// w16 (down projections, a_is_h): B holds fp16 weights (moe_convert_bf16_to_f16)
+hipError_t launch_bf16_to_f16(const void* src, void* dst, long long n, hipStream_t st);
 
 // MXFP8 path (codes + E8M0 scales; scale words group-major, see mxfp8.hip).
 // Quantises rows x cols (cols a multiple of 128) of bf16 / fp32 src; inf/NaN
@@ -177,9 +182,10 @@ hipError_t launch_gemm_gateup_mx(int bm, const void* A, const int32_t* a_rows, c
                                  uint32_t* flags, hipStream_t st, bool sa_direct = false);
 hipError_t launch_gemm_down_mx(int bm, const void* A, const uint8_t* hsc, int hs_stride,
                                const void* B, const uint8_t* sb, int sb_stride, int N, int K,
-                               float* Y, int ldy, const MTile* sched, const int32_t* count,
+                               void* Y, int ldy, const MTile* sched, const int32_t* count,
                                int max_tiles, int static_rows, hipStream_t st,
-                               int ksplit = 1, long long part_elems = 0);
+                               int ksplit = 1, long long part_elems = 0, bool y_half = false,
+                               uint32_t* flags = nullptr);
 
 // Both row-tile classes (256-row and 32-row tiles of the big and small
 // schedules) in one interleaved launch.
@@ -187,10 +193,11 @@ hipError_t launch_gemm_gateup2(const void* A, const int32_t* a_rows, int lda, co
                                const void* Bu, int N, int K, void* h, int ldh, const MTile* sb,
                                const int32_t* cb, int mb, const MTile* ss, const int32_t* cs, int ms,
                                uint32_t* flags, hipStream_t st);
-hipError_t launch_gemm_down2(const void* A, int lda, const void* B, int N, int K, float* Y, int ldy,
+hipError_t launch_gemm_down2(const void* A, int lda, const void* B, int N, int K, void* Y, int ldy,
                              const MTile* sb, const int32_t* cb, int mb, const MTile* ss,
                              const int32_t* cs, int ms, hipStream_t st, int ksplit = 1,
-                             long long part_elems = 0);
+                             long long part_elems = 0, bool y_half = false, uint32_t* flags = nullptr,
+                             bool w16 = false);
 hipError_t launch_gemm_gateup_mx2(const void* A, const int32_t* a_rows, const uint8_t* sa, int sa_stride,
                                   const void* Bg, const uint8_t* sbg, const void* Bu, const uint8_t* sbu,
                                   int sb_stride, int N, int K, void* h, uint8_t* hsc, int hs_stride,
@@ -198,16 +205,28 @@ hipError_t launch_gemm_gateup_mx2(const void* A, const int32_t* a_rows, const ui
                                   const int32_t* cs, int ms, uint32_t* flags, hipStream_t st,
                                   bool sa_direct = false);
 hipError_t launch_gemm_down_mx2(const void* A, const uint8_t* hsc, int hs_stride, const void* B,
-                                const uint8_t* sb_w, int sb_stride, int N, int K, float* Y, int ldy,
+                                const uint8_t* sb_w, int sb_stride, int N, int K, void* Y, int ldy,
                                 const MTile* sb, const int32_t* cb, int mb, const MTile* ss,
                                 const int32_t* cs, int ms, hipStream_t st, int ksplit = 1,
-                                long long part_elems = 0);
+                                long long part_elems = 0, bool y_half = false, uint32_t* flags = nullptr);
 
 // Row-tile height the GEMM launchers use for a dtype and a requested height.
 int gemm_tile_rows(int dtype, int bm_hint);
 
-hipError_t launch_combine(const moe_shape& s, const float* y_perm, const int32_t* row_of_slot,
-                          const float* gates, const float* y_shared, void* out, hipStream_t st,
-                          int parts = 1, long long part_stride = 0);
+// ---- expert-parallel exchange over G virtual ranks (ep.hip) -----------------
+constexpr int kMaxRanks = 64;
+// 64-token tiles of the send-layout kernels (tile_counts: tiles x G ints)
+int ep_tiles(int num_tokens);
+hipError_t launch_ep_layout(const moe_shape& s, int G, const int32_t* ids, const float* gates,
+                            int32_t* rank_counts, int32_t* rank_offsets, int32_t* send_token,
+                            int32_t* send_ids, float* send_gates, int32_t* slot_send_pos,
+                            int32_t* tile_counts, uint32_t* flags, hipStream_t st);
+hipError_t launch_ep_combine(const moe_shape& s, int G, const float* partial, const int32_t* slot_send_pos,
+                             const float* y_shared, void* out, hipStream_t st);
+
+// y_half: y_perm and y_shared hold fp16 values (then parts must be 1)
+hipError_t launch_combine(const moe_shape& s, const void* y_perm, const int32_t* row_of_slot,
+                          const float* gates, const void* y_shared, void* out, hipStream_t st,
+                          int parts = 1, long long part_stride = 0, bool y_half = false);
 
 }  // namespace moe

@@ -63,7 +63,7 @@ typedef enum {
   MOE_ERR_HIP = -4           /* a HIP call or kernel launch failed                */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_F16 = 2 } moe_dtype;
 typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
 
 /* device flag bits (moe_read_device_flags) */
@@ -72,6 +72,8 @@ typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
 #define MOE_FLAG_H_RANGE 4u     /* some SwiGLU activation h exceeded fp16 range (bf16 layers)
                                    or was not finite (MXFP8 layers)                           */
 #define MOE_FLAG_BAD_REPLICA 8u /* a routed expert without a replica, or a replica id out of range */
+#define MOE_FLAG_Y_RANGE 16u    /* some expert output exceeded fp16 range inside a layer call
+                                   (moe_layer_forward, moe_layer_forward_mxfp8)                */
 
 typedef struct {
   int32_t num_tokens;          /* T >= 0                                                  */
@@ -88,8 +90,12 @@ typedef struct {
                                   0 means 1; at most E/G                                   */
   float capacity_factor;       /* C = ceil(cf * A / E), A = routed slots; <= 0: no limit   */
   int32_t shared_intermediate; /* Is; 0 = no shared expert; same rule as H                 */
-  int32_t act_dtype;           /* moe_dtype of x and of every weight                        */
-  int32_t out_dtype;           /* moe_dtype of the layer output                             */
+  int32_t act_dtype;           /* moe_dtype of x and of every weight (MOE_F32 or MOE_BF16)  */
+  int32_t out_dtype;           /* moe_dtype of the layer output (MOE_F32 or MOE_BF16)       */
+  int32_t down_dtype;          /* 0 or act_dtype: the down weights (routed and shared) have
+                                  act_dtype; MOE_F16 (bf16 layers only): they were converted
+                                  once by moe_convert_bf16_to_f16 -- the same products, without
+                                  the conversion inside every call                           */
 } moe_shape;
 /* Element offsets are int32 inside the kernels: T*top_k <= 2^30 and each of
  * T*H, E*H, I*H and Is*H <= 2^31-1, else MOE_ERR_UNSUPPORTED. */
@@ -109,7 +115,9 @@ typedef enum {
 
 /* Optional outputs of moe_layer_forward for inspection and timing.  Each
  * member may be NULL.  Device buffer sizes: logits T*E, topk_ids/topk_gates/
- * row_of_slot T*top_k, expert_counts E, expert_offsets E+1, num_dropped 1.
+ * row_of_slot/row_token T*top_k, expert_counts E, expert_offsets E+1,
+ * num_dropped 1 (row_token as moe_dispatch writes it: entries at and beyond
+ * expert_offsets[E] are left untouched).
  * stage_start[i]/stage_stop[i] are hipEvent_t handles recorded on the call's
  * stream immediately before the first and after the last launch of stage i
  * (a stage that does not run records both at the same point). */
@@ -123,13 +131,19 @@ typedef struct {
   int32_t* num_dropped;
   void* stage_start[MOE_NUM_STAGES];
   void* stage_stop[MOE_NUM_STAGES];
+  int32_t* row_token;
 } moe_debug;
 
 /* Bytes of workspace every call below needs for this shape (host only, no HIP
  * call).  The same workspace serves all calls. */
 moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes);
 
-/* S1 + S2: router logits and top-k selection.
+/* S1 + S2: router logits and top-k selection.  A router picks the top-k
+ * experts of each token ("Expert parallelism for MoE serving", deep dive;
+ * "Expert Parallelism: MoE model parallel split", §1: router -> top-k experts
+ * -> weighted sum), optionally limited to a few groups of experts (node-
+ * limited routing, "Expert parallelism for MoE serving", deployment
+ * examples), with k chosen per request (MoE-Prism summary, §1 and §5).
  * logits[t][e] = sum_h x[t][h] * w_router[e][h] + router_bias[e], fp32 accumulate.
  * If logits_in is non-NULL it is used instead and x/w_router/router_bias are
  * ignored (may be NULL).  logits_out (nullable) receives the computed logits.
@@ -173,8 +187,8 @@ moe_status moe_dispatch(const moe_shape* shape, const void* x, const int32_t* to
  *       silu(z) = z / (1 + exp(-z)); fp32 accumulation; h is kept in fp32
  *       for fp32 layers and rounded to fp16 (11-bit significand) for bf16
  *       layers, whose down projection then runs on fp16 inputs (w_down
- *       converted from bf16, exact for |w| >= 2^-14); |h| > 65504 sets
- *       MOE_FLAG_H_RANGE
+ *       converted from bf16, exact for |w| >= 2^-14, or already fp16 when
+ *       shape->down_dtype is MOE_F16); |h| > 65504 sets MOE_FLAG_H_RANGE
  *   y_perm[r] = h . w_down[e]^T                                    (fp32)
  * Rows at or beyond expert_offsets[E] are not written.  x_perm [T*top_k][H],
  * y_perm [T*top_k][H] fp32.  expert_offsets must be non-decreasing with
@@ -218,16 +232,79 @@ moe_status moe_map_replicas(const moe_shape* shape, const int32_t* topk_ids,
 moe_status moe_combine(const moe_shape* shape, const float* y_perm, const int32_t* row_of_slot,
                        const float* topk_gates, const float* y_shared, void* out, void* stream);
 
-/* The whole layer: S1-S10 in one call (may fuse steps internally).
- * out[t] = sum over kept slots of gate * FFN_e(x[t]) + FFN_shared(x[t]).
+/* The whole layer: S1-S10 in one call (may fuse steps internally).  The four
+ * steps of an MoE layer of "LLM MoE Expert Parallel production practice"
+ * (route each token to its top-K experts, send its activations to them, run
+ * the expert FFNs, send the outputs back and merge them), with the sends of
+ * expert parallelism replaced by an on-device permutation and its inverse
+ * ("Expert Parallelism: MoE model parallel split", §1 weighted sum, §3 the
+ * dispatch and combine exchanges, §12 Q2 k target positions per token;
+ * "Expert parallelism for MoE serving", deep dive and technical notes).
+ * out[t] = sum over kept slots of gate * FFN_e(x[t]) + FFN_shared(x[t]):
+ * the routing, dispatch, FFN and combine of moe_route_topk, moe_dispatch,
+ * moe_grouped_ffn and moe_combine, with the same argument rules.
  * The shared expert runs when shape->shared_intermediate > 0 (then ws_gate,
- * ws_up and ws_down are required).  dbg (nullable) receives intermediates. */
+ * ws_up and ws_down are required; "LLM MoE Expert Parallel production
+ * practice", launch checklist; "Expert Parallelism…" §4).  dbg (nullable)
+ * receives intermediates.  Clears the workspace flag word. */
 moe_status moe_layer_forward(const moe_shape* shape, const void* x, const void* w_router,
                              const float* router_bias, const int32_t* k_per_token,
                              const void* w_gate, const void* w_up, const void* w_down,
                              const void* ws_gate, const void* ws_up, const void* ws_down,
                              void* out, const moe_debug* dbg, void* ws, size_t ws_bytes,
                              void* stream);
+
+/* ---- the expert-parallel exchange over G ranks, on one GPU -------------
+ * With expert parallelism over G GPUs ("Expert Parallelism: MoE model
+ * parallel split", §8: each GPU holds one contiguous block of E/G experts)
+ * every MoE layer exchanges twice (§3, §12 Q2): dispatch sends each token's
+ * hidden state to the ranks holding its experts, combine returns their
+ * outputs to the token's own rank.  Rows bound for one rank are grouped into
+ * one send (§7 and §12, token sorting), and a token travels once to each
+ * rank holding any of its experts -- with node-limited routing ("Expert
+ * parallelism for MoE serving", deployment examples; group-limited routing
+ * with num_groups = G here) at most topk_groups ranks rather than k copies.
+ * The two calls below are the source side of both exchanges, run with G
+ * virtual ranks on one GPU: the send layout, and the sum of the rows the
+ * ranks return.  A rank's own work on the rows it receives is the step
+ * chain moe_dispatch / moe_grouped_ffn / moe_combine with its local expert
+ * ids, its E/G experts' weights and the received gates (num_tokens = its
+ * row count): one pre-reduced row per received row.  Capacity, if any, is
+ * the receiving rank's: the layout sends every routed slot. */
+
+/* Send layout of the dispatch exchange.  Rank d holds experts d*E/G ..
+ * (d+1)*E/G - 1 (1 <= G <= 64, E % G == 0).  Rows are destination-major,
+ * tokens ascending within a rank, no padding:
+ *   rank_counts[d]      rows for rank d                                  [G]
+ *   rank_offsets        exclusive prefix sum of rank_counts              [G+1]
+ *   send_token[p]       token of row p                                   [n_rows]
+ *   send_ids[p][j]      topk_ids[t][j] - d*E/G for the slots j of token t
+ *                       on rank d, -1 for its other slots                [n_rows][k]
+ *   send_gates[p][j]    topk_gates[t][j] where send_ids[p][j] >= 0, else 0
+ *   slot_send_pos[t][j] row p of token t's row for the rank of slot j,
+ *                       -1 for an unused slot                            [T][k]
+ *   send_x[p]           x[send_token[p]] for p < rank_offsets[G]  [n_rows][H]
+ *                       (skipped when x and send_x are NULL)
+ * n_rows = T * min(top_k, G).  Rows from rank_offsets[G] to n_rows - 1 get
+ * send_token -1, send_ids -1 and send_gates 0 (send_x is not written there).
+ * topk_ids / topk_gates as moe_route_topk writes them; ids outside [-1, E)
+ * count as unused and set MOE_FLAG_BAD_EXPERT.  Uses the workspace of
+ * `shape`; clears its flag word.  Positions are bitwise deterministic. */
+moe_status moe_ep_dispatch_layout(const moe_shape* shape, int32_t num_ranks, const int32_t* topk_ids,
+                                  const float* topk_gates, const void* x, int32_t* rank_counts,
+                                  int32_t* rank_offsets, int32_t* send_token, int32_t* send_ids,
+                                  float* send_gates, int32_t* slot_send_pos, void* send_x, void* ws,
+                                  size_t ws_bytes, void* stream);
+
+/* The combine exchange's last step at the source: partial [n_rows][H] fp32
+ * holds, at each row p of the send layout, the gate-weighted sum of the
+ * outputs of the experts of rank d for token send_token[p] (what rank d
+ * returns).  out[t] = sum of the token's distinct rows (the non-negative
+ * slot_send_pos[t][*]) in ascending order -- ascending rank -- plus
+ * y_shared[t] when non-NULL; fp32 arithmetic; out in out_dtype.  A token
+ * with no routed slot gets y_shared[t] or 0.  No workspace. */
+moe_status moe_ep_combine(const moe_shape* shape, int32_t num_ranks, const float* partial,
+                          const int32_t* slot_send_pos, const float* y_shared, void* out, void* stream);
 
 /* ---- the layer without a caller workspace ------------------------------
  * For callers that cannot allocate device memory: code under HIP graph
@@ -293,6 +370,15 @@ typedef struct {
  * quantised once with this call (rows = E*I or E*H). */
 moe_status moe_quantize_mxfp8(int32_t rows, int32_t cols, int32_t src_dtype, const void* src,
                               int32_t scale_stride, void* codes, uint8_t* scales, void* stream);
+
+/* Weight preparation for bf16 layers: dst[i] = src[i] (bf16) as fp16, for
+ * i < n (device arrays, 16-byte aligned), with the conversion the down
+ * projection applies to bf16 weights inside every layer call (fp16 is the
+ * down projection's operand type; exact for |w| in [2^-14, 65504]); layer
+ * calls whose shape has down_dtype = MOE_F16 take the converted down weights
+ * and skip that conversion, with identical results.  Down weights are
+ * converted once with this call (n = E*H*I, and H*Is for the shared expert). */
+moe_status moe_convert_bf16_to_f16(int64_t n, const void* src, void* dst, void* stream);
 
 /* Workspace of the two MXFP8 calls below (host only). */
 moe_status moe_workspace_size_mxfp8(const moe_shape* shape, size_t* bytes);

@@ -68,6 +68,8 @@ def base_shape(**kw):
     (dict(num_groups=4, topk_groups=1, group_topn=3), abi.MOE_ERR_INVALID_ARG),  # > E/G
     (dict(num_groups=8, topk_groups=1, top_k=2), abi.MOE_ERR_INVALID_ARG),      # 1 group of 1 < k
     (dict(act_dtype=abi.MOE_F32, hidden=4098), abi.MOE_ERR_UNSUPPORTED),
+    (dict(down_dtype=5), abi.MOE_ERR_INVALID_ARG),
+    (dict(down_dtype=abi.MOE_F16, act_dtype=abi.MOE_F32), abi.MOE_ERR_UNSUPPORTED),
     # int32 element offsets: T*H, I*H and E*H must stay below 2^31
     (dict(num_tokens=524288, hidden=4096), abi.MOE_ERR_UNSUPPORTED),
     (dict(num_tokens=16, intermediate=524288, hidden=4096), abi.MOE_ERR_UNSUPPORTED),
@@ -184,3 +186,17 @@ def test_noalloc_entry_point_checks_before_any_hip_call():
     assert call(abi.make_shape(W.CONFIGS["mixtral_decode"], top_k=0)) == abi.MOE_ERR_INVALID_ARG
     # zero tokens: valid, nothing enqueued (no device is touched)
     assert call(abi.make_shape(W.CONFIGS["mixtral_decode"], num_tokens=0)) == abi.MOE_OK
+
+
+def test_down_dtype_values():
+    """down_dtype: 0 or act_dtype (weights in act_dtype) or MOE_F16 (bf16
+    layers); MXFP8 layers take no fp16 down weights."""
+    for dd in (0, abi.MOE_BF16, abi.MOE_F16):
+        assert abi.moe_workspace_size(base_shape(down_dtype=dd)) > 0
+    n = ctypes.c_size_t(0)
+    s = base_shape(down_dtype=abi.MOE_F16)
+    assert abi.lib().moe_workspace_size_mxfp8(ctypes.byref(s), ctypes.byref(n)) == abi.MOE_ERR_UNSUPPORTED
+    L = abi.lib()
+    assert L.moe_convert_bf16_to_f16(-1, FAKE, FAKE, None) == abi.MOE_ERR_INVALID_ARG
+    assert L.moe_convert_bf16_to_f16(16, FAKE_ODD, FAKE, None) == abi.MOE_ERR_INVALID_ARG
+    assert L.moe_convert_bf16_to_f16(0, None, None, None) == abi.MOE_OK

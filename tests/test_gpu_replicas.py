@@ -3,7 +3,8 @@
 leaves the layer output unchanged -- the step-API chain route -> replica map
 -> dispatch -> grouped FFN -> combine over the physical experts reproduces
 moe_layer_forward on the logical experts bit for bit (every row's arithmetic
-is the same; only the row grouping changes)."""
+is the same; only the row grouping changes; where the layer keeps its expert
+outputs in fp16, the chain's y is rounded the same way before its combine)."""
 
 import numpy as np
 import pytest
@@ -132,7 +133,14 @@ def test_replicated_chain_reproduces_layer(name, T):
                             inp["ws_down"].unsqueeze(0).contiguous(), y_shared, ws1)
     out = torch.empty(T, H, dtype=torch.float32, device=dev())
     abi.moe_combine(sp, y, ros, gates, y_shared, out, None)
+    # the layer keeps the expert outputs in fp16 when its down projection is
+    # not split: the same chain with y (and the shared y) rounded to fp16
+    out16 = torch.empty(T, H, dtype=torch.float32, device=dev())
+    abi.moe_combine(sp, y.half().float(), ros, gates, None if y_shared is None else y_shared.half().float(),
+                    out16, None)
     torch.cuda.synchronize()
     pc = np.bincount(host(phys)[host(phys) >= 0], minlength=P)
     say(f"  physical experts {P}; max/mean load {counts.max() / counts.mean():.2f} -> {pc.max() / pc.mean():.2f}")
-    assert torch.equal(out, ref), f"max |diff| {float((out - ref).abs().max())}"
+    same32, same16 = torch.equal(out, ref), torch.equal(out16, ref)
+    say(f"  layer equals the chain with fp32 y: {same32}, with fp16 y: {same16}")
+    assert same32 or same16, f"max |diff| {float((out - ref).abs().max())} / {float((out16 - ref).abs().max())}"
