@@ -12,8 +12,9 @@ import torch
 import workloads as W
 from expert_serving_amd import abi
 
-from gpu_util import dev, say
-from test_gpu_layer import compare_layer
+import oracle
+from gpu_util import assert_close_rms, dev, say, tile_cover_tokens
+from test_gpu_layer import check_routing, compare_layer, gpu_layer, oracle_inputs
 from test_gpu_mxfp8 import compare_layer_mx
 
 pytestmark = pytest.mark.gpu
@@ -68,7 +69,7 @@ def test_layer_interleaved_classes_with_shared_expert(fmt):
     inp = W.make_layer_inputs(cfg, dev(), salt=10)
     rng = np.random.default_rng(3)
     sample = np.array(sorted(set([0, 2047]) | set(rng.choice(2048, 14, replace=False).tolist())), np.int32)
-    (compare_layer if fmt == "bf16" else compare_layer_mx)(cfg, inp, sample=sample)
+    (compare_layer if fmt == "bf16" else compare_layer_mx)(cfg, inp, sample=sample, tiles=True)
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "mxfp8"])
@@ -79,24 +80,40 @@ def test_layer_big_tiles_k_split_three(fmt):
     cfg = W.CONFIGS["mixtral_prefill"].with_tokens(256)
     say(f"big tiles, K split in three {fmt}")
     inp = W.make_layer_inputs(cfg, dev(), salt=11)
-    rng = np.random.default_rng(4)
-    sample = np.array(sorted(set([0, 255]) | set(rng.choice(256, 14, replace=False).tolist())), np.int32)
-    (compare_layer if fmt == "bf16" else compare_layer_mx)(cfg, inp, sample=sample)
+    # bf16: every token; MXFP8: the tokens covering every row tile (each
+    # K-split part contributes to every row)
+    if fmt == "bf16":
+        compare_layer(cfg, inp)
+    else:
+        compare_layer_mx(cfg, inp, sample=np.array([0, 255], np.int32), tiles=True)
 
 
-def test_layer_large_batch_sampled():
+def test_layer_large_batch_every_tile():
     """32 times the Mixtral-shaped prefill batch: 131072 tokens, 262144 routed
-    rows (h 7.5 GB and y 4.3 GB of workspace).  Routing, counts and
-    permutation are compared on every token (near ties allowed as in
-    test_gpu_layer.py), outputs on a sample: the index arithmetic far past
-    the benchmark's sizes."""
+    rows (h 7.5 GB and y 4.3 GB of workspace): the index arithmetic far past
+    the benchmark's sizes.  Routing, counts and permutation are compared on
+    every token (bit-exact, as in test_gpu_layer.py); outputs on the tokens
+    that put two compared rows into every 256-row run of every expert's rows.
+    Every expert holds about 32768 rows here, so the grouped GEMMs cut them
+    into 256-row tiles from the expert's first row, with a remainder of at
+    most 64 rows on one small tile at the start of the last run: each tile is
+    one run."""
     cfg = W.CONFIGS["mixtral_prefill"].with_tokens(131072)
     say(f"large batch: T={cfg.tokens}")
     inp = W.make_layer_inputs(cfg, dev(), salt=5)
+    g = gpu_layer(cfg, inp)
+    torch.cuda.synchronize()
+    d = check_routing(cfg, g, inp)
+    assert g["flags"] == 0
+    assert d["counts"].min() >= 256
+    cover, runs, covered = tile_cover_tokens(d["offsets"], d["row_token"], d["row_of_slot"], block=256)
+    assert covered == runs
     rng = np.random.default_rng(6)
-    sample = np.array(sorted(set([0, cfg.tokens - 1]) | set(rng.choice(cfg.tokens, 10, replace=False).tolist())),
-                      np.int32)
-    compare_layer(cfg, inp, sample=sample)
+    tokens = np.union1d(cover, rng.choice(cfg.tokens, 10, replace=False)).astype(np.int32)
+    say(f"  256-row runs covered: {covered} of {runs} by {len(cover)} tokens")
+    oi = oracle_inputs(cfg, inp, tokens, g["ids"])
+    ref = oracle.layer_forward_cfg(cfg, oi, tokens=tokens, logits=g["logits"])
+    assert_close_rms(g["out"].cpu().numpy()[tokens], ref["out"], 2e-2, f"out[{len(tokens)} tokens]")
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "mxfp8"])

@@ -29,8 +29,9 @@ import oracle
 import workloads as W
 from expert_serving_amd import abi
 
-from gpu_util import assert_close_rms, dev, host, i32, lazy_expert_copy, rms, say
+from gpu_util import dev, host, i32, lazy_expert_copy, rms, say, tile_cover_tokens
 from mx_check import check_flips
+from test_gpu_layer import check_routing
 
 pytestmark = pytest.mark.gpu
 
@@ -168,19 +169,26 @@ def gpu_layer_mx(cfg, inp, mw, mws):
     out = torch.empty(T, H, dtype=torch.float32, device=dev())
     dbg = dict(logits=torch.empty(T, E, dtype=torch.float32, device=dev()), topk_ids=i32(T * k),
                topk_gates=torch.empty(T * k, dtype=torch.float32, device=dev()), expert_counts=i32(E),
-               expert_offsets=i32(E + 1), row_of_slot=i32(T * k), num_dropped=i32(1))
+               expert_offsets=i32(E + 1), row_of_slot=i32(T * k), num_dropped=i32(1), row_token=i32(T * k))
     abi.moe_layer_forward_mxfp8(shape, inp["x"], inp["w_router"], inp["bias"], inp["k_per_token"], mw, mws,
                                 out, dbg, ws)
     flags = abi.moe_read_device_flags(ws)
     res = {key: v.cpu().numpy() for key, v in dbg.items()}
     res["ids"] = res.pop("topk_ids").reshape(T, k)
+    res["gates"] = res.pop("topk_gates").reshape(T, k)
     res["row_of_slot"] = res["row_of_slot"].reshape(T, k)
+    res["num_dropped"] = int(res["num_dropped"][0])
     res["out"] = out.cpu().numpy()
     res["flags"] = flags
     return res
 
 
-def compare_layer_mx(cfg, inp, sample=None):
+def compare_layer_mx(cfg, inp, sample=None, tiles=False, per_run=1):
+    """Routing and dispatch bit-exact on every token (the oracle routes on
+    the GPU's logits, as in test_gpu_layer.py); outputs of `sample` (None:
+    all tokens), plus with `tiles` the tokens that put per_run compared rows
+    into every 32-row run of every expert's rows (so every row tile of 64 or
+    more rows has at least two), checked for rounding flips."""
     T = cfg.tokens
     say(f"mx layer {cfg.name}: T={T} H={cfg.hidden} E={cfg.experts} k={cfg.top_k} I={cfg.inter}")
     mw = mx_weights_gpu(inp["w_gate"], inp["w_up"], inp["w_down"])
@@ -188,17 +196,17 @@ def compare_layer_mx(cfg, inp, sample=None):
     g = gpu_layer_mx(cfg, inp, mw, mws)
     assert g["flags"] == 0
     x_h, wr_h, b_h, kpt_h = host(inp["x"]), host(inp["w_router"]), host(inp["bias"]), host(inp["k_per_token"])
-    lo = oracle.router_logits(x_h, wr_h, b_h)
-    assert_close_rms(g["logits"], lo, 1e-5, "logits")
-    ids_o, _ = oracle.route(lo, cfg.top_k, kpt_h, cfg.score, cfg.renormalize, cfg.routed_scale,
-                            cfg.num_groups, cfg.topk_groups, cfg.group_topn)
-    # routing is the bf16 path's (its parity, near ties included, is covered
-    # there); here the workloads' seeds route identically
-    assert np.array_equal(g["ids"], ids_o)
-    d = oracle.dispatch(ids_o, cfg.experts, cfg.capacity_factor)
-    assert np.array_equal(g["row_of_slot"], d["row_of_slot"])
+    d = check_routing(cfg, g, inp)
+    ids_o = g["ids"]
     tokens = np.arange(T, dtype=np.int32) if sample is None else np.asarray(sample, np.int32)
+    if tiles:
+        cover, runs, covered = tile_cover_tokens(d["offsets"], d["row_token"], d["row_of_slot"], per_block=per_run)
+        assert covered == runs
+        say(f"  32-row runs of expert rows covered ({per_run} row each): {covered} of {runs} "
+            f"(by {len(cover)} tokens)")
+        tokens = np.union1d(tokens, cover).astype(np.int32)
     used = sorted(set(int(e) for e in ids_o[tokens].reshape(-1) if e >= 0))
+    say(f"  quantising the weights of {len(used)} experts (oracle) ...")
     wq = {}
     for key, name in (("w_gate", "gate"), ("w_up", "up"), ("w_down", "down")):
         wl = lazy_expert_copy(inp[key], used)
@@ -211,9 +219,10 @@ def compare_layer_mx(cfg, inp, sample=None):
     if cfg.shared_inter:
         shared = {n: oracle.mxfp8_quantize(host(inp[key]))
                   for key, n in (("ws_gate", "gate"), ("ws_up", "up"), ("ws_down", "down"))}
+    say(f"  oracle layer on {len(tokens)} tokens ...")
     ref = oracle.layer_forward_mxfp8(x_h, wr_h, wq, cfg.top_k, b_h, kpt_h, cfg.score, cfg.renormalize,
                                      cfg.routed_scale, cfg.num_groups, cfg.topk_groups, cfg.group_topn,
-                                     cfg.capacity_factor, shared, tokens=tokens)
+                                     cfg.capacity_factor, shared, tokens=tokens, logits=g["logits"])
     assert np.array_equal(ref["ids"], ids_o)
     got = g["out"][tokens]
     assert np.all(np.isfinite(got))
@@ -229,6 +238,8 @@ def compare_layer_mx(cfg, inp, sample=None):
             parts.append((1.0, shared["down"], ref["h_shared"][ti]))
         f, m = check_flips(got[ti].astype(np.float64) - ref["out"][ti], parts, r_ref, f"{cfg.name} token {t}")
         flips, rem = flips + f, max(rem, m)
+        if ti % 200 == 199:
+            say(f"  ... {ti + 1} of {len(tokens)} tokens checked")
     say(f"  {cfg.name}: {len(tokens)} tokens, {flips} rounding flips of h, remainder {rem / r_ref:.2e} * rms, "
         f"max|err|/rms {np.abs(got - ref['out']).max() / r_ref:.2e}")
 
@@ -257,10 +268,12 @@ def sample_tokens(T, n, seed=0):
 
 
 @pytest.mark.parametrize("name,n", [("mixtral_prefill", 12), ("deepseek_v3", 6), ("qwen3_skewed", 64)])
-def test_layer_mxfp8_full_size_sampled(name, n):
+def test_layer_mxfp8_full_size_every_tile(name, n):
+    """Full workload sizes: outputs of a random sample plus the tokens that
+    cover every row tile of both classes."""
     cfg = W.CONFIGS[name]
     inp = W.make_layer_inputs(cfg, dev())
-    compare_layer_mx(cfg, inp, sample=sample_tokens(cfg.tokens, n))
+    compare_layer_mx(cfg, inp, sample=sample_tokens(cfg.tokens, n), tiles=True)
 
 
 def test_layer_mxfp8_shared_mid_tiles_and_determinism():
