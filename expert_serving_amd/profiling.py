@@ -2,6 +2,7 @@
 
     python -m expert_serving_amd.profiling stats <kernel_stats.csv> <out.md> "<command>"
     python -m expert_serving_amd.profiling traffic <fetch_dir> <write_dir> <kernel_substring> <out.txt> "<commands>"
+    python -m expert_serving_amd.profiling mfma <pmc_dir> "<kernel>;<kernel>" <out.md> "<command>"
 
 `stats` keeps the per-kernel call count and average/total duration.
 `traffic` reads two --pmc runs (FETCH_SIZE, then WRITE_SIZE) of a program that
@@ -91,6 +92,64 @@ def traffic_summary(fetch_dir: str, write_dir: str, kernel: str, out_path: str, 
     return rec
 
 
+def _dispatch_ns(run_dir: str):
+    """Kernel duration (ns) by dispatch id from a --kernel-trace CSV."""
+    out = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            try:
+                out[r["Dispatch_Id"]] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+            except (KeyError, ValueError):
+                continue
+    return out
+
+
+def mfma_summary(run_dir: str, kernels, out_path: str, command: str) -> dict:
+    """MFMA utilisation of the given kernels from one --pmc run of MfmaUtil,
+    GRBM_GUI_ACTIVE and the bf16 / f16 MFMA op counters (with --kernel-trace
+    for the durations): per kernel, medians over its dispatches (the first,
+    cold, left out) of the MFMA-busy share of SIMD cycles, the average clock
+    (GRBM_GUI_ACTIVE cycles, summed over the XCDs, per XCD over the duration)
+    and the MFMA flop rate the op counters give (512 flops per counted op;
+    padding rows of partly filled tiles count too)."""
+    vals = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            k = short_name(r["Kernel_Name"])
+            vals.setdefault(k, {}).setdefault(r.get("Dispatch_Id", ""), {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    dur = _dispatch_ns(run_dir)
+    # GRBM_GUI_ACTIVE is summed over the GPU's XCDs (accelerator complex dies)
+    xcc = 8
+    for f in glob.glob(os.path.join(run_dir, "**", "*agent_info.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r.get("Agent_Type") == "GPU" and r.get("Num_Xcc"):
+                xcc = int(r["Num_Xcc"])
+    recs = {}
+    lines = ["# MFMA utilisation per dispatch (rocprofv3 --pmc)", "", f"Command: `{command}`", "",
+             "| kernel | dispatches | MFMA busy (% of SIMD cycles) | clock (GHz) | duration (us) | "
+             "MFMA TFLOP/s from op counters |", "|---|---|---|---|---|---|"]
+    for kern in kernels:
+        name = next((k for k in vals if kern in k), None)
+        if name is None:
+            continue
+        ds = sorted(vals[name].items(), key=lambda kv: float(kv[0]) if kv[0] else 0.0)
+        ds = ds[1:] or ds
+        util = statistics.median(v.get("MfmaUtil", float("nan")) for _, v in ds)
+        gui = statistics.median(v.get("GRBM_GUI_ACTIVE", float("nan")) for _, v in ds)
+        mops = statistics.median(v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + v.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0)
+                                 for _, v in ds)
+        ns = [dur[d] for d, _ in ds if d in dur]
+        t = statistics.median(ns) if ns else float("nan")
+        rec = dict(kernel=name, dispatches=len(vals[name]), mfma_busy_pct=util, clock_ghz=gui / xcc / t if ns else None,
+                   duration_us=t / 1e3, mfma_tflops=mops * 512 / t / 1e3 if ns else None)
+        recs[kern] = rec
+        lines.append(f"| `{name}` | {rec['dispatches']} | {util:.1f} | "
+                     f"{(rec['clock_ghz'] or float('nan')):.2f} | {rec['duration_us']:.1f} | "
+                     f"{(rec['mfma_tflops'] or float('nan')):.0f} |")
+    open(out_path, "w").write("\n".join(lines) + "\n")
+    return recs
+
+
 def read_traffic(path: str):
     """The record written by traffic_summary, or None."""
     if not os.path.exists(path):
@@ -112,3 +171,5 @@ if __name__ == "__main__":
         stats_summary(sys.argv[2], sys.argv[3], sys.argv[4])
     elif sys.argv[1] == "traffic":
         print(traffic_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6]))
+    elif sys.argv[1] == "mfma":
+        print(mfma_summary(sys.argv[2], sys.argv[3].split(";"), sys.argv[4], sys.argv[5]))
