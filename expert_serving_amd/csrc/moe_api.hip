@@ -94,6 +94,9 @@ moe_status check_mx_shape(const moe_shape* s) {
   if (s->act_dtype != MOE_BF16 || s->down_dtype == MOE_F16) return MOE_ERR_UNSUPPORTED;
   if (s->hidden % 128 || s->intermediate % 128 || s->shared_intermediate % 128)
     return MOE_ERR_UNSUPPORTED;
+  // the scale-word strides of the weights (E*I rows of gate/up, E*H of down;
+  // E*H is bounded by check_shape) are int32 inside the kernels
+  if ((long long)s->num_experts * s->intermediate > (long long)INT_MAX) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

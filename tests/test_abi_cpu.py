@@ -200,3 +200,15 @@ def test_down_dtype_values():
     assert L.moe_convert_bf16_to_f16(-1, FAKE, FAKE, None) == abi.MOE_ERR_INVALID_ARG
     assert L.moe_convert_bf16_to_f16(16, FAKE_ODD, FAKE, None) == abi.MOE_ERR_INVALID_ARG
     assert L.moe_convert_bf16_to_f16(0, None, None, None) == abi.MOE_OK
+
+
+def test_mxfp8_scale_strides_bounded():
+    """MXFP8 layers pass E*I (the gate/up weights' scale-word stride) as an
+    int32; shapes beyond it are rejected, while the bf16 layer, whose offsets
+    are 64-bit there, still takes them."""
+    s = abi.make_shape(num_tokens=16, hidden=128, num_experts=512, intermediate=4194304, top_k=2)
+    n = ctypes.c_size_t(0)
+    assert abi.lib().moe_workspace_size_mxfp8(ctypes.byref(s), ctypes.byref(n)) == abi.MOE_ERR_UNSUPPORTED
+    assert abi.lib().moe_workspace_size(ctypes.byref(s), ctypes.byref(n)) == abi.MOE_OK
+    ok = abi.make_shape(num_tokens=16, hidden=128, num_experts=256, intermediate=4194304 - 128, top_k=2)
+    assert abi.lib().moe_workspace_size_mxfp8(ctypes.byref(ok), ctypes.byref(n)) == abi.MOE_OK
