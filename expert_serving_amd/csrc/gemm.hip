@@ -8,20 +8,27 @@
 // padding); rows past a group's end inside a tile are clamped on load and
 // masked on store.
 //
-// bf16 kernel (gfx950):
-//   * v_mfma_f32_16x16x32_bf16, fp32 accumulation;
-//   * the weight tile is the MFMA A operand and the token tile the B
-//     operand, so each lane's 4 accumulators are 4 consecutive output
-//     columns of one token row (8-byte bf16 / 16-byte fp32 stores);
-//   * block = 4 wavefronts in a 2x2 grid; K step 64; LDS tiles [rows][64] with
-//     16-byte chunks XOR-swizzled by row; the next K step is prefetched into
-//     registers while the current one is multiplied;
+// bf16 kernels (gfx950):
+//   * v_mfma_f32_32x32x16_bf16 (f16 for the down projection), fp32
+//     accumulation; the weight tile is the MFMA A operand and the token tile
+//     the B operand, so a lane's accumulators are runs of consecutive output
+//     columns of one token row;
+//   * 8-wave blocks (256-, 128-, 64- and 32-row tiles): two waves per SIMD
+//     in a ping-pong over register-staged loads and two LDS stages of K = 64
+//     (128-byte rows, 16-byte chunks XOR-swizzled by row); 4-wave blocks (the
+//     32-row tiles of some small-expert launches): direct-to-LDS loads into a
+//     ring of K = 32 stages;
 //   * gate/up variant: one block computes the same column range of X.Wg^T
 //     and X.Wu^T and applies SwiGLU in the epilogue (h never exists unfused);
+//   * skewed loads: the big experts' tiles and the small experts' tiles run
+//     interleaved in one launch; tiles of at most four token rows there take
+//     a vector-ALU path that streams the weights straight into registers;
 //   * block -> tile map: blocks are dealt round-robin to the 8 XCDs, so block
 //     b is remapped to give each XCD a contiguous range of logical tiles, and
 //     logical tiles sweep groups of kGroupM row tiles across all column tiles
 //     so the XCD's L2 serves both the token rows and the weight rows.
+// The MXFP8 modes run the same 8-wave schedule on E4M3 codes with the scaled
+// fp8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4).
 #include <atomic>
 
 #include "moe_internal.h"
@@ -253,6 +260,9 @@ constexpr int gemm_lds_bytes(int BM, int BNB, int MODE, int NS, int NW) {
   return NS * gemm_stage_rows(BM, BNB, MODE, NW) *
          ((NW == 8 ? kPingRowElems : kSK) * 2 + (gemm_mx(MODE) ? 4 : 0));
 }
+
+// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format).
+constexpr int kBufferRsrcWord3 = 0x00020000;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
@@ -876,6 +886,177 @@ __device__ __forceinline__ void gemm_tile(
   if (overflow && flags) atomicOr(flags, DUAL ? (uint32_t)MOE_FLAG_H_RANGE : (uint32_t)MOE_FLAG_Y_RANGE);
 }
 
+// Small-expert tiles of at most kSkinnyRows token rows in the interleaved
+// launches (bf16 gate/up and the down projection).  A 64-row MFMA tile runs
+// 16 to 64 times the needed MFMA work on such a tile (clamped duplicate rows)
+// while its weight stream is bound by the compute unit's memory path, not by
+// the MFMAs or the LDS (both tile kinds stream about 50 GB/s per compute unit
+// when few run, and about 7 TB/s together when every unit runs one).  Here the
+// weights go from memory straight into registers in whole 128-byte lines (8
+// rows x 8 lanes per wavefront load) and the vector ALUs form the dot
+// products: v_dot2 (two products per lane and instruction, fp32 sums) on bf16
+// pairs for gate/up and on fp16 pairs for the down projection, whose bf16
+// weights are converted to fp16 by the conversion the MFMA tiles apply.
+//
+// Wave w owns output columns n0 + 32w .. n0 + 32w + 31 (all in range or all
+// out: N is a multiple of 64).  Lane l takes 16-byte chunk l % 8 of every
+// 64-element K segment of weight rows n0 + 32w + 8g + l / 8 (g = 0..3; of
+// both matrices for gate/up) and of each token row, so it holds partial sums
+// for 4 (or 2 x 4) weight rows x R token rows; the 8 lanes of a weight row
+// then add theirs across lanes and lane 8j + 2g writes column
+// n0 + 32w + 8g + j.  D segments of loads stay in flight.  Rows past t.rows
+// (R = 4 for three rows) repeat the last row and are not stored.
+constexpr int kSkinnyRows = 4;
+
+constexpr bool skinny_mode(int MODE) { return MODE == kGateUp || MODE == kDown || MODE == kDownW16; }
+
+template <int R, int MODE, int BNB>
+__device__ __forceinline__ void skinny_tile(
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int lda,
+    const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, long long strideB, int N, int K,
+    void* __restrict__ Out, int ldo, uint32_t* __restrict__ flags, const MTile t, int ni, int kst0,
+    int kstn, bool out_half) {
+  static_assert(BNB == 256, "eight waves of 32 columns");
+  constexpr bool DUAL = MODE == kGateUp;
+  constexpr int NB = DUAL ? 2 : 1;
+  constexpr int D = DUAL ? 4 : 6;
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int cw = ni * BNB + 32 * wave;
+  if (cw >= N || t.rows < 1 || kstn < 1) return;
+  const int j = lane >> 3, c = lane & 7;
+  // Buffer loads: one resource per weight matrix (the expert's, from the
+  // block's first K segment) and per token row, a lane offset per row group,
+  // and the segment's byte offset in a scalar register, so a load needs no
+  // address registers of its own.  Every offset fits 32 bits (an expert's
+  // matrix and a row hold fewer than 2^31 elements); reads past a resource's
+  // end return zeros.
+  const size_t k0 = (size_t)kst0 * kPingRowElems;
+  const uint32_t wbytes = (uint32_t)(((size_t)N * K - k0) * 2);
+  const __amdgpu_buffer_rsrc_t rw0 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(B0 + (size_t)t.expert * strideB + k0), 0, wbytes, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rw1 = DUAL ? __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(B1 + (size_t)t.expert * strideB + k0), 0, wbytes, kBufferRsrcWord3) : rw0;
+  const uint32_t xbytes = (uint32_t)(((size_t)K - k0) * 2);
+  __amdgpu_buffer_rsrc_t rx[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int rr = t.row0 + min(r, t.rows - 1);
+    const int row = __builtin_amdgcn_readfirstlane(a_rows ? a_rows[rr] : rr);
+    rx[r] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A + (size_t)row * lda + k0), 0, xbytes,
+                                              kBufferRsrcWord3);
+  }
+  int wo[4];  // byte offsets below 2^32, passed as their 32-bit pattern
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    wo[g] = __builtin_bit_cast(int, ((uint32_t)(cw + 8 * g + j) * (uint32_t)K + 8u * c) * 2u);
+  const int xo = 16 * c;
+  u32x4 wv[D][NB][4];
+  u32x4 xv[D][R];
+  float acc[NB][4][R];
+#pragma unroll
+  for (int m = 0; m < NB; ++m)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[m][g][r] = 0.f;
+  // weight lines are read once: non-temporal (aux bit 1)
+#define MOE_SK_ISSUE(d_, seg_)                                                          \
+  do {                                                                                  \
+    const int so_ = (seg_) * (kPingRowElems * 2);                                       \
+    _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                     \
+      wv[d_][0][g] = __builtin_amdgcn_raw_buffer_load_b128(rw0, wo[g], so_, 2);         \
+      if constexpr (DUAL) wv[d_][NB - 1][g] = __builtin_amdgcn_raw_buffer_load_b128(rw1, wo[g], so_, 2); \
+    }                                                                                   \
+    _Pragma("unroll") for (int r = 0; r < R; ++r)                                       \
+      xv[d_][r] = __builtin_amdgcn_raw_buffer_load_b128(rx[r], xo, so_, 0);             \
+  } while (0)
+#define MOE_SK_DOT(d_)                                                                  \
+  do {                                                                                  \
+    _Pragma("unroll") for (int m = 0; m < NB; ++m) {                                    \
+      _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                   \
+        const u32x4 w_ = MODE == kDown ? bf16x8_to_f16x8(wv[d_][m][g]) : wv[d_][m][g];   \
+        _Pragma("unroll") for (int r = 0; r < R; ++r) {                                 \
+          _Pragma("unroll") for (int q = 0; q < 4; ++q) {                               \
+            /* words copied out first: a bit_cast of a vector element reads */          \
+            /* element 0 with this compiler */                                          \
+            const uint32_t wq_ = w_[q], xq_ = xv[d_][r][q];                             \
+            if constexpr (DUAL)                                                         \
+              acc[m][g][r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wq_), \
+                  __builtin_bit_cast(bf16x2_t, xq_), acc[m][g][r], false);             \
+            else                                                                        \
+              acc[m][g][r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, wq_),    \
+                  __builtin_bit_cast(f16x2_t, xq_), acc[m][g][r], false);              \
+          }                                                                             \
+        }                                                                               \
+      }                                                                                 \
+    }                                                                                   \
+  } while (0)
+  // segments 0 .. D-1 in flight; each step multiplies one and issues the one D
+  // ahead (clamped to the last: re-read lines, never used)
+#pragma unroll
+  for (int d = 0; d < D; ++d) MOE_SK_ISSUE(d, min(d, kstn - 1));
+  const int full = kstn - kstn % D;
+  for (int s = 0; s < full; s += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      // fences keep the scheduler from hoisting the next loads above the
+      // products (longer live ranges, then waits for every load in flight)
+      MOE_SK_DOT(d);
+      __builtin_amdgcn_sched_barrier(0);
+      MOE_SK_ISSUE(d, min(s + d + D, kstn - 1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (d < kstn - full) MOE_SK_DOT(d);
+  __builtin_amdgcn_s_waitcnt(0);  // drain the clamped loads before the block ends
+#undef MOE_SK_DOT
+#undef MOE_SK_ISSUE
+  // The 8 lanes of a weight row add their partial sums, halving the values
+  // each lane holds at every exchange: lanes c and c ^ 4 split the row groups
+  // {0, 1} / {2, 3}, then c and c ^ 2 split those, then c and c ^ 1 add.  Lanes
+  // c and c ^ 1 end with the same sum (fp addition commutes), of row group
+  // g = c / 2 for even c.
+  float res[NB][R];
+  const bool hi4 = (c & 4) != 0, hi2 = (c & 2) != 0;
+#pragma unroll
+  for (int m = 0; m < NB; ++m)
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float k0 = hi4 ? acc[m][2][r] : acc[m][0][r], k1 = hi4 ? acc[m][3][r] : acc[m][1][r];
+      const float s0 = hi4 ? acc[m][0][r] : acc[m][2][r], s1 = hi4 ? acc[m][1][r] : acc[m][3][r];
+      k0 += __shfl_xor(s0, 4);
+      k1 += __shfl_xor(s1, 4);
+      float k = hi2 ? k1 : k0;
+      k += __shfl_xor(hi2 ? k0 : k1, 2);
+      k += __shfl_xor(k, 1);
+      res[m][r] = k;
+    }
+  if (c & 1) return;
+  const int col = cw + 4 * c + j;   // row group c / 2: column cw + 8 (c / 2) + j
+  bool overflow = false;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r >= t.rows) break;
+    const size_t o = (size_t)(t.row0 + r) * ldo + col;
+    if constexpr (DUAL) {
+      const float h = silu_mul(res[0][r], res[NB - 1][r]);
+      overflow |= !(fabsf(h) <= 65504.f);
+      static_cast<uint16_t*>(Out)[o] = (uint16_t)f32_to_f16_bits(h);
+    } else if (out_half) {
+      overflow |= !(fabsf(res[0][r]) <= 65504.f);
+      static_cast<uint16_t*>(Out)[o] = (uint16_t)f32_to_f16_bits(res[0][r]);
+    } else {
+      static_cast<float*>(Out)[o] = res[0][r];
+    }
+  }
+  if (overflow && flags) atomicOr(flags, DUAL ? (uint32_t)MOE_FLAG_H_RANGE : (uint32_t)MOE_FLAG_Y_RANGE);
+}
+
 // One row-tile class per launch: block -> (row tile, column tile) by block_tile.
 // ksplit > 1 splits K into that many ranges of whole 64-element stages; the
 // blocks of range p write their partial sums to Out + p * part_elems (fp32
@@ -935,6 +1116,21 @@ __global__ __launch_bounds__(512) void k_gemm_mfma2(
     gemm_tile<BM1, BNB1, MODE, 2, 8>(smem, A, a_rows, lda, B0, B1, strideB, N, K, Out, ldo, nullptr,
                                      sched1, 0, flags, mx, mi, ni, kst0, kst1 - kst0, 0, out_half != 0);
   } else {
+    if constexpr (skinny_mode(MODE)) {
+      const MTile t = sched2[mi];
+      if (t.rows <= kSkinnyRows) {
+        if (t.rows == 1)
+          skinny_tile<1, MODE, BNB2>(A, a_rows, lda, B0, B1, strideB, N, K, Out, ldo, flags, t, ni, kst0,
+                                     kst1 - kst0, out_half != 0);
+        else if (t.rows == 2)
+          skinny_tile<2, MODE, BNB2>(A, a_rows, lda, B0, B1, strideB, N, K, Out, ldo, flags, t, ni, kst0,
+                                     kst1 - kst0, out_half != 0);
+        else
+          skinny_tile<4, MODE, BNB2>(A, a_rows, lda, B0, B1, strideB, N, K, Out, ldo, flags, t, ni, kst0,
+                                     kst1 - kst0, out_half != 0);
+        return;
+      }
+    }
     gemm_tile<BM2, BNB2, MODE, 2, 8>(smem, A, a_rows, lda, B0, B1, strideB, N, K, Out, ldo, nullptr,
                                      sched2, 0, flags, mx, mi, ni, kst0, kst1 - kst0, 0, out_half != 0);
   }

@@ -88,6 +88,25 @@ def test_layer_big_tiles_k_split_three(fmt):
         compare_layer_mx(cfg, inp, sample=np.array([0, 255], np.int32), tiles=True)
 
 
+def test_layer_skinny_tiles_with_k_split():
+    """Experts and tails of at most four rows inside the interleaved launch,
+    with the down projection's K split in three: Mixtral-shaped, 512 tokens,
+    and a router bias that gives the experts about 443, 260, 24, 127, 164, 3,
+    2 and 1 rows (260 = one 256-row tile and a 4-row tail).  Rows of at most
+    four run on the vector-ALU tiles (1, 2 or 4 token rows), the rest on MFMA
+    tiles; every token is compared."""
+    cfg = W.CONFIGS["mixtral_prefill"].with_tokens(512)
+    say("skinny tiles, K split in three")
+    inp = W.make_layer_inputs(cfg, dev(), salt=17)
+    inp["bias"] = torch.tensor([3.019, 1.876, 0.246, 1.336, 1.412, -0.888, -0.835, -1.424], dtype=torch.float32,
+                               device=dev())
+    d = compare_layer(cfg, inp)
+    counts = d["counts"]
+    few = [int(c) for c in counts if 1 <= c <= 4] + [int(c) % 256 for c in counts if c >= 256 and 1 <= c % 256 <= 4]
+    say(f"  rows per expert {counts.tolist()}; groups of 1-4 rows: {few}")
+    assert len(few) >= 3 and counts.max() >= 256
+
+
 def test_layer_large_batch_every_tile():
     """32 times the Mixtral-shaped prefill batch: 131072 tokens, 262144 routed
     rows (h 7.5 GB and y 4.3 GB of workspace): the index arithmetic far past

@@ -34,6 +34,11 @@ FFN_CASES = [
     # a token or two: two one-row experts, so the gate/up K is split into
     # parts that a separate kernel adds before SwiGLU
     ("bf16_two_rows_split_gate_up", W.DT_BF16, 8, 1024, 512, [1, 0, 0, 0, 0, 0, 1, 0], 2),
+    # big and small experts in one interleaved launch, the small ones with
+    # 1, 2, 3 and 4 rows (vector-ALU tiles of 1, 2 and 4 token rows) and 5
+    # rows (MFMA); 17 and 10 K segments (pipeline remainders); the last
+    # column tile of each projection partly past N
+    ("bf16_skinny_small_experts", W.DT_BF16, 8, 1088, 640, [700, 1, 2, 3, 4, 5, 0, 300], 1015),
     ("f32_tiny", W.DT_F32, 3, 128, 96, [40, 0, 33], 73),
     ("f32_ragged", W.DT_F32, 5, 64, 36, [1, 31, 32, 33, 70], 167),
 ]

@@ -110,6 +110,7 @@ def compare_layer(cfg, inp, sample=None, tiles=False):
     got = g["out"].cpu().numpy()[tokens]
     tol = 2e-2 if cfg.dtype == W.DT_BF16 else 1e-4
     assert_close_rms(got, ref["out"], tol, f"{cfg.name} out[{len(tokens)} tokens]")
+    return d
 
 
 SMALL = [
