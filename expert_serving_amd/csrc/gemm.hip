@@ -838,6 +838,39 @@ __device__ __forceinline__ void gemm_tile(
         *reinterpret_cast<u32x4*>(dst + 8) = u32x4{x13[0], y13[0], x13[1], y13[1]};
       }
     }
+  } else if (!gemm_part(MODE) && out_half) {
+    // fp16 outputs (a layer's down projection), stored as the gate/up
+    // epilogue stores h: after the lane-half exchanges lane l holds columns
+    // 0..15 and lane l ^ 32 columns 16..31 of its row, two 16-byte stores
+    // each instead of four 8-byte ones (the stores had been the largest part
+    // of a short-K tile's epilogue)
+#pragma unroll
+    for (int b = 0; b < FM; ++b) {
+      const int m = wm * WM + b * 32 + fr;
+#pragma unroll
+      for (int a = 0; a < FN; ++a) {
+        const int nb = n0 + wn * WN + a * 32;
+        const f32x16 v = acc0[a][b];
+        uint32_t px[4], py[4];
+        bool ovf = false;
+#pragma unroll
+        for (int qi = 0; qi < 4; ++qi) {
+          ovf |= !(fabsf(v[4 * qi]) <= 65504.f && fabsf(v[4 * qi + 1]) <= 65504.f &&
+                   fabsf(v[4 * qi + 2]) <= 65504.f && fabsf(v[4 * qi + 3]) <= 65504.f);
+          px[qi] = f32_to_f16_bits(v[4 * qi]) | (f32_to_f16_bits(v[4 * qi + 1]) << 16);
+          py[qi] = f32_to_f16_bits(v[4 * qi + 2]) | (f32_to_f16_bits(v[4 * qi + 3]) << 16);
+        }
+        const auto x02 = __builtin_amdgcn_permlane32_swap(px[0], px[2], false, false);
+        const auto y02 = __builtin_amdgcn_permlane32_swap(py[0], py[2], false, false);
+        const auto x13 = __builtin_amdgcn_permlane32_swap(px[1], px[3], false, false);
+        const auto y13 = __builtin_amdgcn_permlane32_swap(py[1], py[3], false, false);
+        if (m >= rows || nb >= N) continue;
+        overflow |= ovf;
+        uint16_t* dst = static_cast<uint16_t*>(Out) + (size_t)(row0 + m) * ldo + nb + 16 * fk;
+        *reinterpret_cast<u32x4*>(dst) = u32x4{x02[0], y02[0], x02[1], y02[1]};
+        *reinterpret_cast<u32x4*>(dst + 8) = u32x4{x13[0], y13[0], x13[1], y13[1]};
+      }
+    }
   } else {
 #pragma unroll
   for (int b = 0; b < FM; ++b) {
@@ -853,17 +886,6 @@ __device__ __forceinline__ void gemm_tile(
         for (int ob = 0; ob < (gemm_part(MODE) ? 2 : 1); ++ob) {
           const f32x16 acc = ob ? acc1[DUAL ? a : 0][DUAL ? b : 0] : acc0[a][b];
           f32x4 v = {acc[4 * qi], acc[4 * qi + 1], acc[4 * qi + 2], acc[4 * qi + 3]};
-          if (out_half) {
-            // fp16 outputs (a layer's down projection; N is a multiple of 64
-            // and n of 4, so a run of four is all in or all out)
-            if (n >= N) continue;
-            overflow |= !(fabsf(v[0]) <= 65504.f && fabsf(v[1]) <= 65504.f && fabsf(v[2]) <= 65504.f &&
-                          fabsf(v[3]) <= 65504.f);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Out) + o) =
-                uint2{f32_to_f16_bits(v[0]) | (f32_to_f16_bits(v[1]) << 16),
-                      f32_to_f16_bits(v[2]) | (f32_to_f16_bits(v[3]) << 16)};
-            continue;
-          }
           float* dst = static_cast<float*>(Out) + o + (ob ? up_off : 0);
           if (n + 3 < N && (ldo & 3) == 0) {
             if (bias) {
