@@ -107,6 +107,54 @@ def test_layer_skinny_tiles_with_k_split():
     assert len(few) >= 3 and counts.max() >= 256
 
 
+def routed_layer_inputs(cfg, second, salt=23):
+    """Layer inputs whose routing is set by hand: the router reads hidden
+    dims 0..E-1 only (w_router = 10 * identity there) and x[t, :E] = +4 on the
+    token's experts and -4 elsewhere, so token t's top-2 is {0, second[t]}."""
+    inp = W.make_layer_inputs(cfg, dev(), salt=salt)
+    E = cfg.experts
+    code = torch.full((cfg.tokens, E), -4.0)
+    code[:, 0] = 4.0
+    code[torch.arange(cfg.tokens), torch.as_tensor(second)] = 4.0
+    inp["x"][:, :E] = code.to(inp["x"].dtype).to(dev())
+    wr = torch.zeros(E, cfg.hidden)
+    wr[:, :E] = 10.0 * torch.eye(E)
+    inp["w_router"] = wr.to(inp["w_router"].dtype).to(dev())
+    return inp
+
+
+def test_layer_fp16_range_flags():
+    """|h| or |y| past the fp16 range inside a bf16 layer call sets
+    MOE_FLAG_H_RANGE or MOE_FLAG_Y_RANGE, from every kind of tile: an expert
+    on one 256-row MFMA tile (256 rows, no tail), one on a 64-row MFMA tile
+    (20 rows) and one on vector-ALU tiles (2 rows), in one interleaved launch.
+    One expert's gate and up (or down) weights are scaled up per call (the
+    down weights far enough that their fp16 copies saturate); with the plain
+    weights no flag is set."""
+    cfg = W.CONFIGS["mixtral_prefill"].replace(hidden=1024, inter=2048, tokens=279)
+    second = np.full(cfg.tokens, 4)
+    second[:2] = 1
+    second[2:22] = 2
+    second[22] = 3
+    say("fp16 range flags")
+    inp = routed_layer_inputs(cfg, second)
+    g = gpu_layer(cfg, inp)
+    counts = g["expert_counts"]
+    assert counts.tolist() == [279, 2, 20, 1, 256, 0, 0, 0], counts
+    assert g["flags"] == 0
+    for e, kind in ((4, "256-row tile"), (2, "64-row tile"), (1, "vector-ALU tiles")):
+        for which, scale, flag in (("gate_up", 300.0, abi.MOE_FLAG_H_RANGE), ("down", 1e7, abi.MOE_FLAG_Y_RANGE)):
+            keys = ("w_gate", "w_up") if which == "gate_up" else ("w_down",)
+            saved = {key: inp[key][e].clone() for key in keys}
+            for key in keys:
+                inp[key][e] *= scale
+            flags = gpu_layer(cfg, inp)["flags"]
+            for key in keys:
+                inp[key][e] = saved[key]
+            say(f"  expert {e} ({kind}), {which} x {scale:g}: flags {flags}")
+            assert flags & flag, (e, which, flags)
+
+
 def test_layer_large_batch_every_tile():
     """32 times the Mixtral-shaped prefill batch: 131072 tokens, 262144 routed
     rows (h 7.5 GB and y 4.3 GB of workspace): the index arithmetic far past
