@@ -1153,6 +1153,17 @@ __global__ __launch_bounds__(512) void k_gemm_mfma2(
         return;
       }
     }
+    // small tiles of at most 32 rows run as 32-row tiles: the weight stream of
+    // a small tile is bound by the LDS traffic of its stages, which a 32-row
+    // tile cuts by about a quarter (one token fragment per wave instead of
+    // weight fragments read by two wave rows)
+    if constexpr (BM2 > 32) {
+      if (sched2[mi].rows <= 32) {
+        gemm_tile<32, BNB2, MODE, 2, 8>(smem, A, a_rows, lda, B0, B1, strideB, N, K, Out, ldo, nullptr,
+                                        sched2, 0, flags, mx, mi, ni, kst0, kst1 - kst0, 0, out_half != 0);
+        return;
+      }
+    }
     gemm_tile<BM2, BNB2, MODE, 2, 8>(smem, A, a_rows, lda, B0, B1, strideB, N, K, Out, ldo, nullptr,
                                      sched2, 0, flags, mx, mi, ni, kst0, kst1 - kst0, 0, out_half != 0);
   }
@@ -1386,7 +1397,8 @@ hipError_t launch_mfma2(const void* A, const int32_t* a_rows, int lda, const voi
                         hipStream_t st, const MxArgs mx = MxArgs{}, int ksplit = 1,
                         long long part_elems = 0, bool out_half = false, int group_m = kGroupM) {
   constexpr int l1 = gemm_lds_bytes(BM1, BNB1, MODE, 2, 8), l2 = gemm_lds_bytes(BM2, BNB2, MODE, 2, 8);
-  constexpr int lds = l1 > l2 ? l1 : l2;
+  constexpr int l3 = gemm_lds_bytes(32, BNB2, MODE, 2, 8);  // small tiles of at most 32 rows
+  constexpr int lds = (l1 > l2 ? l1 : l2) > l3 ? (l1 > l2 ? l1 : l2) : l3;
   static_assert(lds <= 160 * 1024, "LDS");
   static std::atomic<uint64_t> set_on{0};
   hipError_t e = raise_lds_limit<mfma2_kernel<BM1, BNB1, BM2, BNB2, MODE>>(lds, set_on);
