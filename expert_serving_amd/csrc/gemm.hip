@@ -910,11 +910,13 @@ __device__ __forceinline__ void gemm_tile(
 
 // Small-expert tiles of at most kSkinnyRows token rows in the interleaved
 // launches (bf16 gate/up and the down projection).  A 64-row MFMA tile runs
-// 16 to 64 times the needed MFMA work on such a tile (clamped duplicate rows)
-// while its weight stream is bound by the compute unit's memory path, not by
-// the MFMAs or the LDS (both tile kinds stream about 50 GB/s per compute unit
-// when few run, and about 7 TB/s together when every unit runs one).  Here the
-// weights go from memory straight into registers in whole 128-byte lines (8
+// 16 to 64 times the needed MFMA work on such a tile (clamped duplicate rows),
+// and inside a power-limited interleaved launch its ping-pong schedule streams
+// the weights at about 33 GB/s per compute unit; this tile streams about 55
+// GB/s there, the rate of the unit's memory path (alone, at a higher clock,
+// both reach about 50 GB/s, and about 7 TB/s together when every unit runs
+// one).  Here the weights go from memory straight into registers in whole
+// 128-byte lines (8
 // rows x 8 lanes per wavefront load) and the vector ALUs form the dot
 // products: v_dot2 (two products per lane and instruction, fp32 sums) on bf16
 // pairs for gate/up and on fp16 pairs for the down projection, whose bf16
